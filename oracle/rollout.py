@@ -1,0 +1,87 @@
+"""Synthetic FP4 exploration rollout -- oracle, test infrastructure only.
+
+Stage 1 of the two-stage pipeline (Sol-RL project page, "Two-Stage Pipeline";
+aitrends summary, Stage-1 paragraph): quantize the current weights to FP4,
+integrate N noises with a 6-step ODE solver whose linears run in FP4, score
+the candidates with a proxy reward and keep the top K/2 and bottom K/2 seeds.
+
+The pages' velocity network is a trained DiT; this stand-in keeps only the
+shape of its MLP linears. Readings (the pages give no network):
+  * velocity v(x) = h_4 with h_0 = x and
+        h_{b+1} = h_b + W2_b GELU(W1_b RMSNorm(h_b)),   b = 0..3
+    RMSNorm with unit gain and eps 1e-6, GELU in its exact erf form, no time
+    conditioning;
+  * every linear input is rounded to fp32 and then quantized (the quantizers
+    take fp32 or bf16 input); everything else is float64;
+  * proxy reward = <mean over tokens of x_final, u> for a fixed vector u;
+  * Euler steps on the uniform grid t_i = 1 - i/6.
+"""
+import numpy as np
+from scipy.special import erf
+
+from . import euler, gemm, mxfp4, nvfp4, reward
+
+EPS = 1e-6
+
+
+def rmsnorm(h):
+    h = np.asarray(h, dtype=np.float64)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + EPS)
+
+
+def gelu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+
+
+class QuantLinear:
+    """A weight [out, in] quantized once per iteration (the pages' per-iteration
+    re-quantization); __call__ quantizes its fp32 input and runs the exact GEMM."""
+
+    def __init__(self, w, fmt):
+        self.fmt = fmt
+        w = np.asarray(w, dtype=np.float32)
+        if fmt == "mx":
+            self.q = mxfp4.quantize(w)
+        elif fmt == "nv":
+            self.q = nvfp4.quantize(w)
+        elif fmt is None:
+            self.q = w.astype(np.float64)
+        else:
+            raise ValueError(fmt)
+
+    def __call__(self, x):
+        x32 = np.asarray(x, dtype=np.float32)
+        if self.fmt == "mx":
+            ac, as_ = mxfp4.quantize(x32)
+            return gemm.gemm_mx(ac, as_, *self.q)[0]
+        if self.fmt == "nv":
+            ac, as_, ag = nvfp4.quantize(x32)
+            return gemm.gemm_nv(ac, as_, ag, *self.q)[0]
+        return x32.astype(np.float64) @ self.q.T
+
+
+def velocity(x, w1, w2):
+    """x: [tokens_total, dim]; w1[b]: QuantLinear dim->hidden; w2[b]: hidden->dim."""
+    h = np.asarray(x, dtype=np.float64)
+    for l1, l2 in zip(w1, w2):
+        h = h + l2(gelu(l1(rmsnorm(h))))
+    return h
+
+
+def rollout(noise, w1, w2, u, n_steps=6, fmt="mx", k_top=12, k_bottom=12):
+    """noise: [n_cand, tokens, dim]; w1/w2: lists of float weights [out, in].
+
+    Returns (x_final [n_cand, tokens, dim], rewards [n_cand], top, bottom)."""
+    noise = np.asarray(noise, dtype=np.float32)
+    n_cand, tokens, dim = noise.shape
+    q1 = [QuantLinear(w, fmt) for w in w1]
+    q2 = [QuantLinear(w, fmt) for w in w2]
+    t = euler.schedule(n_steps)
+    x = noise.reshape(n_cand * tokens, dim).astype(np.float64)
+    for i in range(n_steps):
+        v = velocity(x, q1, q2)
+        x = euler.step(x, v, t[i], t[i + 1])
+    r = reward.proxy_reward(x, tokens, u)
+    top, bottom = reward.select(r, k_top, k_bottom)
+    return x.reshape(n_cand, tokens, dim), r, top, bottom
