@@ -1,0 +1,246 @@
+"""Benchmark: the full synthetic FP4 exploration rollout on one MI355X.
+
+One step = one Stage-1 pass over 96 candidates x 4096 tokens x 3072 dims:
+re-quantize the 8 weights (MXFP4), 6 Euler steps of a 4-block residual MLP
+velocity (RMSNorm->MXFP4 -> FP4 GEMM 3072->12288 -> GELU->MXFP4 -> FP4 GEMM
+12288->3072 + residual), proxy reward, top-12 / bottom-12 selection. All
+inputs are resident in HBM before timing starts.
+
+Prints one JSON line: candidates/s, the FP4 GEMM's achieved TFLOP/s against
+the MXFP4 peak (HIP events around every GEMM launch of the timed steps), the
+CPU oracle timed on a bounded sample, and rank agreement against the same
+rollout with bf16 linears (torch, outside the timed region).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--chunk C] [--no-cpu-baseline] [--no-rank-agreement]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 GEMM TFLOP/s (% of MI355X MXFP4 peak); FP4 rollout candidates/sec"
+PEAK_FP4 = 10.1e15      # MI355X dense MXFP4 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """Records a HIP event pair around each launch on the current stream."""
+
+    def __init__(self):
+        self.events = {}
+        self.enabled = True
+
+    def __call__(self, name, fn):
+        if not self.enabled:
+            return fn()
+        import torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.events.setdefault(name, []).append((s, e))
+        return out
+
+    def summary(self):
+        return {k: (len(v), sum(s.elapsed_time(e) for s, e in v) / len(v)) for k, v in self.events.items()}
+
+
+def make_inputs(cfg, device):
+    import torch
+    from fp4_quantized_diffusion_amd import inputs
+    t0 = time.time()
+    noise = inputs.rollout_noise_all(cfg["seed"], cfg["n_cand"], cfg["tokens"], cfg["dim"])
+    noise_d = torch.from_numpy(noise).to(device)
+    del noise
+    w1, w2 = [], []
+    for b in range(cfg["blocks"]):
+        a, bb = inputs.rollout_weights(cfg["seed"], b, cfg["dim"], cfg["hidden"])
+        w1.append(torch.from_numpy(a).to(device).bfloat16())
+        w2.append(torch.from_numpy(bb).to(device).bfloat16())
+    u = torch.from_numpy(inputs.reward_vector(cfg["seed"], cfg["dim"])).to(device)
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    return noise_d, w1, w2, u
+
+
+def bf16_rollout(noise, w1, w2, u, steps, tokens, chunk):
+    """Same rollout with bf16 linears (torch), for rank agreement only."""
+    import torch
+    import torch.nn.functional as F
+    n_cand, _, dim = noise.shape
+    x = noise.reshape(-1, dim).clone()
+    t = [1.0 - i / steps for i in range(steps + 1)]
+    for i in range(steps):
+        for c0 in range(0, n_cand, chunk):
+            xs = x[c0 * tokens:(c0 + chunk) * tokens]
+            h = xs.clone()
+            for a, b in zip(w1, w2):
+                y = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + 1e-6)
+                z = F.gelu(F.linear(y.bfloat16(), a).float())
+                h = h + F.linear(z.bfloat16(), b).float()
+            xs.add_(h, alpha=(t[i + 1] - t[i]))
+    r = (x.view(n_cand, tokens, dim).mean(1) @ u)
+    return r
+
+
+def rank_stats(a, b, k):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    ra, rb = np.argsort(np.argsort(a)), np.argsort(np.argsort(b))
+    rho = float(np.corrcoef(ra, rb)[0, 1])
+    n = len(a)
+    conc = 0
+    for i in range(n):
+        for j in range(i + 1, n):
+            conc += np.sign(a[i] - a[j]) * np.sign(b[i] - b[j])
+    tau = float(conc / (n * (n - 1) / 2))
+    ta, tb = set(np.argsort(-a)[:k]), set(np.argsort(-b)[:k])
+    ba, bb = set(np.argsort(a)[:k]), set(np.argsort(b)[:k])
+    return {"spearman": round(rho, 4), "kendall_tau": round(tau, 4), "top_overlap": len(ta & tb),
+            "bottom_overlap": len(ba & bb), "k": k}
+
+
+def cpu_baseline(cfg, tokens_sample=16, w_rows_sample=256):
+    """The CPU oracle on a bounded sample of the rollout, scaled to candidates/s:
+    (a) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one W1,
+        scaled by element count to all 8 weights (once per rollout);
+    (b) the oracle's rollout of 1 candidate x tokens_sample tokens through 6
+        steps of the 4-block network (weights in quantized form), scaled by
+        4096 / tokens_sample tokens per candidate."""
+    from fp4_quantized_diffusion_amd import inputs
+    from oracle import mxfp4, rollout as orollout
+    dim, hidden, blocks = cfg["dim"], cfg["hidden"], cfg["blocks"]
+    rng = np.random.default_rng(0)
+    w_slice = inputs.weights(rng, w_rows_sample, dim)
+    t0 = time.perf_counter()
+    mxfp4.quantize(w_slice)
+    t_wq = (time.perf_counter() - t0) * (2 * blocks * hidden * dim) / w_slice.size
+    # quantized weights for the timing sample: random codes / scales of the right shapes
+    q1 = [orollout.QuantLinear.from_quantized("mx", rng.integers(0, 256, (hidden, dim // 2), dtype=np.uint8),
+                                              rng.integers(118, 124, (hidden, dim // 32), dtype=np.uint8))
+          for _ in range(blocks)]
+    q2 = [orollout.QuantLinear.from_quantized("mx", rng.integers(0, 256, (dim, hidden // 2), dtype=np.uint8),
+                                              rng.integers(118, 124, (dim, hidden // 32), dtype=np.uint8))
+          for _ in range(blocks)]
+    noise = inputs.rollout_noise(cfg["seed"], 0, tokens_sample, dim)[None]
+    u = inputs.reward_vector(cfg["seed"], dim)
+    t0 = time.perf_counter()
+    orollout.rollout(noise, q1, q2, u, n_steps=cfg["steps"], k_top=1, k_bottom=0)
+    t_cand = (time.perf_counter() - t0) * cfg["tokens"] / tokens_sample
+    total = t_wq + cfg["n_cand"] * t_cand
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    return {"value": round(cfg["n_cand"] / total, 6), "unit": "candidates/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"oracle MXFP4 quantization of a {w_rows_sample}x{dim} weight slice (scaled by elements to "
+                       f"all {2 * blocks} weights: {t_wq:.1f}s) + oracle rollout of 1 candidate x {tokens_sample} "
+                       f"tokens, {cfg['steps']} steps x {blocks} blocks (scaled x{cfg['tokens'] // tokens_sample} "
+                       f"tokens, x{cfg['n_cand']} candidates: {cfg['n_cand'] * t_cand:.1f}s); numpy float64, "
+                       f"os.cpu_count()={os.cpu_count()}")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--chunk", type=int, default=0, help="candidates per network pass (0 = all 96)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rank-agreement", action="store_true")
+    ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the rollout shards over candidates "
+              "with no cross-GPU traffic besides a 384-byte reward exchange, which this build does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd.inputs import ROLLOUT
+    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
+
+    fq.load_library()
+    dev = "cuda:0"
+    cfg = dict(ROLLOUT)
+    cfg["tokens"] = args.tokens
+    chunk = args.chunk or cfg["n_cand"]
+    noise, w1, w2, u = make_inputs(cfg, dev)
+    work = torch.empty_like(noise)
+    timer = EventTimer()
+    ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
+                    timer=timer)
+
+    timer.enabled = False
+    for i in range(args.warmup):
+        ro.run(noise, work)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    timer.enabled = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rewards, top, bottom, rn = ro.run(noise, work)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = (t1 - t0) / args.steps
+    top_l, bottom_l = top.tolist(), bottom.tolist()
+    log(f"timed {args.steps} steps: {sec * 1e3:.1f} ms/step; top {top_l[:4]}... bottom {bottom_l[:4]}...")
+
+    ks = timer.summary()
+    m_rows = chunk * cfg["tokens"]
+    gemm_flop = 2.0 * m_rows * cfg["dim"] * cfg["hidden"]
+    n_gemm, gemm_ms = ks["gemm"]
+    achieved = gemm_flop / (gemm_ms * 1e-3)
+    kernels = {k: {"launches_per_step": n // args.steps, "avg_us": round(ms * 1e3, 2)} for k, (n, ms) in ks.items()}
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg["n_cand"] / sec, 4),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"fp4_rollout_{cfg['n_cand']}x{cfg['tokens']}x{cfg['dim']}_mlp{cfg['hidden']}"
+                               f"x{cfg['blocks']}blk_{cfg['steps']}step_top{cfg['k_top']}_bottom{cfg['k_bottom']}",
+                   "n_cand": cfg["n_cand"], "tokens": cfg["tokens"], "dim": cfg["dim"], "hidden": cfg["hidden"],
+                   "blocks": cfg["blocks"], "euler_steps": cfg["steps"], "chunk_candidates": chunk,
+                   "gemm_shapes": [[m_rows, cfg["dim"], cfg["hidden"]], [m_rows, cfg["hidden"], cfg["dim"]]]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_FP4 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4), "traffic": None,
+                     "kernel": "gemm_mx (MXFP4 x MXFP4, fp32 accumulate)",
+                     "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
+        "gemm_tflops": round(achieved / 1e12, 2),
+        "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),
+        "kernels": kernels,
+    }
+    if not args.no_rank_agreement:
+        try:
+            t0 = time.time()
+            r_bf16 = bf16_rollout(noise, w1, w2, u, cfg["steps"], cfg["tokens"], min(chunk, 8))
+            out["rank_agreement_vs_bf16"] = rank_stats(rewards.cpu().numpy(), r_bf16.cpu().numpy(), cfg["k_top"])
+            log(f"bf16 rollout for rank agreement: {time.time() - t0:.1f}s")
+        except Exception as e:  # reported, never fatal
+            out["rank_agreement_vs_bf16"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(cfg)
+        log(f"cpu baseline: {time.time() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+"""ctypes binding of libfp4rollout.so (the C ABI in include/fp4rollout.h).
+
+Two layers, argument marshalling only -- every step of the path runs in the
+library's HIP kernels:
+  * the raw entry points under their C names (fp4_quantize, fp4_gemm,
+    euler_step, fp4_proxy_reward, select_topk_bottomk), taking integers and
+    device addresses and returning the status code;
+  * torch-tensor helpers (quantize, gemm, euler, proxy_reward, select) that
+    allocate outputs with torch, pass data_ptr()s and the current HIP stream,
+    and raise Fp4Error on a non-zero status.
+Loading fails loudly when the library has not been built; there is no
+fallback path.
+"""
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp4rollout.so")
+
+FMT_MX, FMT_NV = 0, 1
+DT_F32, DT_BF16 = 0, 1
+PRO_RMSNORM, PRO_GELU, TENSOR_SCALE_GIVEN = 0x1, 0x2, 0x100
+OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR, INTERNAL = 0, 1, 2, 3, 4
+
+_LIB = None
+
+_i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_SIGS = {
+    "fp4_quantize": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
+    "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
+    "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
+    "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
+    "select_topk_bottomk": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+}
+EXPORTS = tuple(_SIGS) + ("fp4_status_str", "fp4_abi_version")
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+
+
+def load_library(path=LIB_PATH):
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m fp4_quantized_diffusion_amd.build` "
+                               "(the FP4 path has no fallback)")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int32
+        lib.fp4_status_str.argtypes = [ctypes.c_int32]
+        lib.fp4_status_str.restype = ctypes.c_char_p
+        lib.fp4_abi_version.argtypes = []
+        lib.fp4_abi_version.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def status_str(s):
+    return load_library().fp4_status_str(int(s)).decode()
+
+
+# ---------------------------------------------------------------- raw C names
+def fp4_quantize(fmt, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales, tensor_scale, flags, stream):
+    return load_library().fp4_quantize(fmt, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales,
+                                       tensor_scale, flags, stream)
+
+
+def fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts, m, n, k, c, c_dtype,
+             ldc, residual, stream):
+    return load_library().fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts,
+                                   m, n, k, c, c_dtype, ldc, residual, stream)
+
+
+def euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream):
+    return load_library().euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream)
+
+
+def fp4_proxy_reward(x, n_cand, rows_per_cand, dim, ldx, u, rewards, stream):
+    return load_library().fp4_proxy_reward(x, n_cand, rows_per_cand, dim, ldx, u, rewards, stream)
+
+
+def select_topk_bottomk(rewards, n, k_top, k_bottom, top_idx, bottom_idx, r_norm, stream):
+    return load_library().select_topk_bottomk(rewards, n, k_top, k_bottom, top_idx, bottom_idx, r_norm, stream)
+
+
+def fp4_abi_version():
+    return load_library().fp4_abi_version()
+
+
+# ------------------------------------------------------------- torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(status, what):
+    if status != OK:
+        raise Fp4Error(status, what)
+
+
+class QTensor(NamedTuple):
+    """A quantized [rows, k] matrix: packed codes [rows, >= k/2] (row stride a
+    multiple of 16 bytes), scale bytes [rows, k/block], and for the NV format
+    the fp32 tensor scale (a 1-element device tensor)."""
+    codes: object
+    scales: object
+    tensor_scale: Optional[object]
+    fmt: int
+    k: int
+
+
+def _row_view_ok(x):
+    return x.dim() == 2 and x.stride(1) == 1
+
+
+def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None):
+    """x: 2-D CUDA tensor (fp32 or bf16, unit inner stride). prologue: None,
+    "rmsnorm" or "gelu" (MX only). tensor_scale: a 1-element fp32 tensor whose
+    value is used as s_g (NV only). out: a QTensor to write into."""
+    torch = _torch()
+    if not _row_view_ok(x):
+        raise ValueError("x must be 2-D with unit inner stride")
+    f = {"mx": FMT_MX, "nv": FMT_NV}[fmt]
+    rows, k = x.shape
+    blk = 32 if f == FMT_MX else 16
+    flags = {None: 0, "rmsnorm": PRO_RMSNORM, "gelu": PRO_GELU}[prologue]
+    if out is None:
+        ldc = ((k // 2 + 15) // 16) * 16
+        codes = torch.empty((rows, ldc), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, max(k // blk, 1)), dtype=torch.uint8, device=x.device)
+        ts = None
+        if f == FMT_NV:
+            ts = torch.empty(1, dtype=torch.float32, device=x.device)
+        out = QTensor(codes, scales, ts, f, k)
+    ts = out.tensor_scale
+    if f == FMT_NV and tensor_scale is not None:
+        ts.copy_(tensor_scale.reshape(1))
+        flags |= TENSOR_SCALE_GIVEN
+    st = fp4_quantize(f, x.data_ptr(), _dtype_code(x), rows, k, x.stride(0), out.codes.data_ptr(),
+                      out.codes.stride(0), out.scales.data_ptr(), out.scales.stride(0), _ptr(ts), flags, _stream())
+    _check(st, "fp4_quantize")
+    return out
+
+
+def gemm(a, b, out_dtype="bf16", residual=None, out=None):
+    """C = A_hat B_hat^T (+ residual) for QTensors a [m, k] and b [n, k]."""
+    torch = _torch()
+    if a.fmt != b.fmt or a.k != b.k:
+        raise ValueError("operands differ in format or k")
+    m, n, k = a.codes.shape[0], b.codes.shape[0], a.k
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out is None:
+        ldc = ((n + 3) // 4) * 4
+        out = torch.empty((m, ldc), dtype=dt, device=a.codes.device)[:, :n]
+    st = fp4_gemm(a.fmt, a.codes.data_ptr(), a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(0),
+                  _ptr(a.tensor_scale), b.codes.data_ptr(), b.codes.stride(0), b.scales.data_ptr(),
+                  b.scales.stride(0), _ptr(b.tensor_scale), m, n, k, out.data_ptr(), _dtype_code(out),
+                  out.stride(0), _ptr(residual), _stream())
+    _check(st, "fp4_gemm")
+    return out
+
+
+def euler(x, v, t_cur, t_next, out=None):
+    """x_out = x + (t_next - t_cur) v over contiguous tensors (x fp32)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    st = euler_step(out.data_ptr(), x.data_ptr(), v.data_ptr(), _dtype_code(v), x.numel(), float(t_cur),
+                    float(t_next), _stream())
+    _check(st, "euler_step")
+    return out
+
+
+def proxy_reward(x, n_cand, rows_per_cand, u=None, out=None):
+    """x: [n_cand * rows_per_cand, dim] fp32 (unit inner stride)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(n_cand, dtype=torch.float32, device=x.device)
+    st = fp4_proxy_reward(x.data_ptr(), n_cand, rows_per_cand, x.shape[1], x.stride(0), _ptr(u), out.data_ptr(),
+                          _stream())
+    _check(st, "fp4_proxy_reward")
+    return out
+
+
+def select(rewards, k_top, k_bottom, normalize=True):
+    """Returns (top [k_top] int32, bottom [k_bottom] int32, r_norm or None)."""
+    torch = _torch()
+    n = rewards.numel()
+    top = torch.empty(max(k_top, 1), dtype=torch.int32, device=rewards.device)[:k_top]
+    bottom = torch.empty(max(k_bottom, 1), dtype=torch.int32, device=rewards.device)[:k_bottom]
+    rn = torch.empty(n, dtype=torch.float32, device=rewards.device) if normalize else None
+    st = select_topk_bottomk(rewards.data_ptr(), n, k_top, k_bottom, top.data_ptr(), bottom.data_ptr(), _ptr(rn),
+                             _stream())
+    _check(st, "select_topk_bottomk")
+    return top, bottom, rn

@@ -1,0 +1,32 @@
+// Host-side launch entry points of the fp4rollout kernels (no device code, so
+// the C ABI layer can be built with the host compiler).
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fp4r {
+
+// ---- launch entry points (host side, defined in the kernel sources) ----
+// Each returns the hipError_t of its launch(es); arguments are already validated.
+hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           int prologue, hipStream_t st);
+hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           float* tensor_scale, int scale_given, hipStream_t st);
+hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as,
+                          const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs,
+                          int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,
+                          const float* residual, hipStream_t st);
+hipError_t launch_gemm_nv(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
+                          const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
+                          int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,
+                          const float* residual, hipStream_t st);
+hipError_t launch_euler(float* x_out, const float* x, const void* v, int v_bf16, int64_t numel,
+                        float t_cur, float t_next, hipStream_t st);
+hipError_t launch_proxy_reward(const float* x, int64_t n_cand, int64_t rows_per_cand, int64_t dim,
+                               int64_t ldx, const float* u, float* rewards, hipStream_t st);
+hipError_t launch_select(const float* r, int64_t n, int64_t k_top, int64_t k_bottom,
+                         int32_t* top, int32_t* bottom, float* r_norm, hipStream_t st);
+
+}  // namespace fp4r

@@ -1,0 +1,292 @@
+// Block-scaled 4-bit quantization kernels (MXFP4 and NVFP4-style) for gfx950.
+//
+// The rollout re-quantizes its weights every iteration and quantizes the
+// activations entering every solver linear (Sol-RL project page, "Two-Stage
+// Pipeline"). Both are HBM-bound streams: the kernels read each input element
+// once (RMSNorm: the row's second read hits L2), write half a byte of code per
+// element and one scale byte per block, and keep every decision in integer
+// or exactly-rounded fp32 arithmetic so the codes are bit-identical to the
+// format's definition.
+//
+// Thread layout: every thread owns 8 consecutive elements of one row
+// ("octet"); the 4 (MX, block 32) or 2 (NV, block 16) threads of a block are
+// adjacent lanes and combine their block maximum with lane shuffles. Input
+// reads are 16-byte vector loads, code writes one 32-bit store per thread.
+// This file is compiled with -ffp-contract=off: every fp32 operation below
+// rounds on its own.
+#include "common.h"
+
+namespace fp4r {
+namespace {
+
+constexpr int kThreads = 256;
+
+enum { PRO_NONE = 0, PRO_RMSNORM = 1, PRO_GELU = 2 };
+
+template <int BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
+  if (BF16) {
+    uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+__device__ __forceinline__ uint32_t amax_bits8(const float v[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// MX: E8M0 scale byte and the packed codes of one octet, given the block amax bits.
+// S = max(biased_exponent(amax) - 2, 0) is floor(log2 amax) - 2 + 127 clamped at
+// E = -127 (zero and subnormal amax land on the clamp). The codes encode
+// x * 2^(127 - S); the multiplier is a normal power of two and the product is
+// exact wherever it can reach a non-zero code.
+__device__ __forceinline__ uint32_t mx_scale(uint32_t amax_bits) {
+  int s = (int)(amax_bits >> 23) - 2;
+  return (uint32_t)(s < 0 ? 0 : s);
+}
+
+__device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
+  const float mul = __uint_as_float((254u - S) << 23);
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= e2m1_nibble(v[j] * mul) << (4 * j);
+  return w;
+}
+
+// One octet per thread, grid-stride. Elementwise prologues only.
+template <int BF16, int PRO>
+__global__ __launch_bounds__(kThreads) void quant_mx_kernel(
+    const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t total_oct) {
+  const int64_t oct_per_row = k >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
+    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
+    float v[8];
+    load8<BF16>(x, row * ldx + oct * 8, v);
+    if (PRO == PRO_GELU) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
+    }
+    // the 4 octets of a 32-block are lanes 4q..4q+3 (oct_per_row and stride are multiples of 4)
+    uint32_t am = amax_bits8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+    const uint32_t S = mx_scale(am);
+    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = mx_pack8(v, S);
+    if ((oct & 3) == 0) scales[row * ld_scales + (oct >> 2)] = (uint8_t)S;
+  }
+}
+
+// Deterministic block-wide fp32 sum (fixed shuffle tree, then fixed LDS order).
+__device__ float block_sum(float v, float* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += sh[w];
+    sh[8] = t;
+  }
+  __syncthreads();
+  t = sh[8];
+  __syncthreads();
+  return t;
+}
+
+// RMSNorm prologue: one workgroup per row. Pass 1 sums squares, pass 2
+// normalizes (y = x * (1 / sqrt(mean + 1e-6)), unit gain) and quantizes.
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_kernel(
+    const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales) {
+  __shared__ float sh[16];
+  const int64_t row = blockIdx.x;
+  const int64_t oct_per_row = k >> 3;
+  float ss = 0.f;
+  for (int64_t oct = threadIdx.x; oct < oct_per_row; oct += kThreads) {
+    float v[8];
+    load8<BF16>(x, row * ldx + oct * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+  }
+  const float tot = block_sum(ss, sh);
+  const float inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+  for (int64_t oct = threadIdx.x; oct < oct_per_row; oct += kThreads) {
+    float v[8];
+    load8<BF16>(x, row * ldx + oct * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
+    uint32_t am = amax_bits8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+    const uint32_t S = mx_scale(am);
+    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = mx_pack8(v, S);
+    if ((oct & 3) == 0) scales[row * ld_scales + (oct >> 2)] = (uint8_t)S;
+  }
+}
+
+// ---------------------------- NVFP4-style ----------------------------------
+
+__global__ void nv_zero_kernel(float* ts) { *reinterpret_cast<uint32_t*>(ts) = 0u; }
+
+// Tensor amax: |x| bit patterns order like the values, so an integer max is
+// exact and order-independent (deterministic).
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restrict__ x, int64_t k, int64_t ldx,
+                                                           int64_t total_oct, float* ts) {
+  __shared__ uint32_t sh[kThreads / 64];
+  const int64_t oct_per_row = k >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
+    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
+    float v[8];
+    load8<BF16>(x, row * ldx + oct * 8, v);
+    m = max(m, amax_bits8(v));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t = max(t, sh[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(ts), t);
+  }
+}
+
+// s_g = fl(A_t / 2688); 1 where that quotient is 0 (all-zero tensor, or one
+// so small the quotient underflows: its codes are signed zeros either way).
+__global__ void nv_finalize_kernel(float* ts) {
+  const float at = __uint_as_float(*reinterpret_cast<const uint32_t*>(ts));
+  const float sg = at / 2688.0f;
+  *ts = (sg == 0.0f) ? 1.0f : sg;
+}
+
+// E4M3 (bias 7, max 448) code of a non-negative finite fp32 value, round to
+// nearest even, saturating at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float s) {
+  const uint32_t b = __float_as_uint(s);
+  const int e = (int)(b >> 23) - 127;
+  if (e < -6) {
+    // below the smallest normal 2^-6: steps of 2^-9; s * 512 is exact
+    return (uint32_t)rintf(s * 512.0f);  // 0..8 (8 is the smallest normal, code 0x08)
+  }
+  // round the 23-bit mantissa to 3 bits (nearest even), carry into the exponent
+  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+  const uint32_t code = r - (120u << 3);  // exponent bias 127 -> 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t S) {
+  const uint32_t e = S >> 3, m = S & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void quant_nv_kernel(
+    const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t total_oct, const float* __restrict__ ts) {
+  const int64_t oct_per_row = k >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const float sg = *ts;
+  const float tau = 6.0f * sg;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
+    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
+    float v[8];
+    load8<BF16>(x, row * ldx + oct * 8, v);
+    uint32_t am = amax_bits8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));  // the 2 octets of a 16-block
+    const float sf = __uint_as_float(am) / tau;
+    const uint32_t S = e4m3_rne(sf);
+    const float d = e4m3_value(S) * sg;
+    uint32_t w = 0;
+    if (d == 0.0f) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= ((__float_as_uint(v[j]) >> 28) & 8u) << (4 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= e2m1_nibble(v[j] / d) << (4 * j);
+    }
+    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = w;
+    if ((oct & 1) == 0) scales[row * ld_scales + (oct >> 1)] = (uint8_t)S;
+  }
+}
+
+inline unsigned grid_for(int64_t work_items) {
+  int64_t g = (work_items + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  if (g > (1 << 20)) g = 1 << 20;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           int prologue, hipStream_t st) {
+  const int64_t total = rows * (k >> 3);
+  if (prologue == PRO_RMSNORM) {
+    if (x_bf16)
+      quant_mx_rmsnorm_kernel<1><<<(unsigned)rows, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales);
+    else
+      quant_mx_rmsnorm_kernel<0><<<(unsigned)rows, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales);
+    return hipGetLastError();
+  }
+  const unsigned g = grid_for(total);
+  if (prologue == PRO_GELU) {
+    if (x_bf16)
+      quant_mx_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+    else
+      quant_mx_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+  } else {
+    if (x_bf16)
+      quant_mx_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+    else
+      quant_mx_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           float* tensor_scale, int scale_given, hipStream_t st) {
+  const int64_t total = rows * (k >> 3);
+  const unsigned g = grid_for(total);
+  if (!scale_given) {
+    nv_zero_kernel<<<1, 1, 0, st>>>(tensor_scale);
+    const unsigned ga = g < 4096 ? g : 4096;
+    if (x_bf16)
+      nv_amax_kernel<1><<<ga, kThreads, 0, st>>>(x, k, ldx, total, tensor_scale);
+    else
+      nv_amax_kernel<0><<<ga, kThreads, 0, st>>>(x, k, ldx, total, tensor_scale);
+    nv_finalize_kernel<<<1, 1, 0, st>>>(tensor_scale);
+  }
+  if (x_bf16)
+    quant_nv_kernel<1><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total, tensor_scale);
+  else
+    quant_nv_kernel<0><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total, tensor_scale);
+  return hipGetLastError();
+}
+
+}  // namespace fp4r

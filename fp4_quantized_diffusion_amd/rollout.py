@@ -1,0 +1,109 @@
+"""Stage-1 FP4 exploration rollout driven through the C ABI.
+
+Sol-RL's first stage (project page, "Two-Stage Pipeline"; aitrends summary,
+Stage-1 paragraph): re-quantize the current weights, integrate N noise seeds
+with a 6-step ODE solver whose linears run FP4 x FP4, score every candidate
+with a proxy reward and keep the K/2 best and K/2 worst seeds.
+
+The velocity network stands in for the pages' trained transformers with the
+shape of their MLP linears: 4 residual blocks
+    h <- h + W2 GELU(W1 RMSNorm(h)),    v = h_4,  h_0 = x
+(dim -> hidden -> dim, no time conditioning), then Euler steps on the
+uniform grid t_i = 1 - i/steps. Per block the device work is:
+    fp4_quantize(h, RMSNORM prologue)     -> A1 (MXFP4)
+    fp4_gemm(A1, W1q) -> z (bf16)
+    fp4_quantize(z, GELU prologue)        -> A2 (MXFP4)
+    fp4_gemm(A2, W2q, residual = h) -> h  (fp32, in place)
+and per step euler_step(x, v = h). The hidden activation z is stored as bf16
+between the two kernels (the float64 oracle keeps it unrounded).
+
+Every call enqueues on the current stream; the only host synchronization is
+the caller reading the selected indices.
+"""
+from . import binding as fb
+
+
+class Fp4Rollout:
+    def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None):
+        """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
+        chunk: candidates per pass through the network (None = all).
+        timer: optional callable(name, fn) wrapping each GEMM launch (for timing)."""
+        if fmt != "mx":
+            raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
+        self.w1, self.w2, self.u = list(w1), list(w2), u
+        self.steps, self.k_top, self.k_bottom = steps, k_top, k_bottom
+        self.fmt, self.chunk = fmt, chunk
+        self.timer = timer
+        self.q1 = self.q2 = None
+        self._bufs = {}
+
+    def requantize(self):
+        """Per-iteration weight re-quantization (all weights, on device)."""
+        self.q1 = [fb.quantize(w, self.fmt, out=None if self.q1 is None else self.q1[i])
+                   for i, w in enumerate(self.w1)]
+        self.q2 = [fb.quantize(w, self.fmt, out=None if self.q2 is None else self.q2[i])
+                   for i, w in enumerate(self.w2)]
+
+    def _buf(self, name, shape, dtype, device):
+        import torch
+        key = (name, tuple(shape), dtype)
+        t = self._bufs.get(key)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=device)
+            self._bufs[key] = t
+        return t
+
+    def _call(self, name, fn):
+        return fn() if self.timer is None else self.timer(name, fn)
+
+    def _gemm(self, a, b, out_dtype, residual=None, out=None):
+        return self._call("gemm", lambda: fb.gemm(a, b, out_dtype, residual=residual, out=out))
+
+    def velocity(self, x, h):
+        """h <- v(x) for x, h fp32 [rows, dim] (h_0 = x is never copied: the
+        first block's GEMM takes x as its residual)."""
+        import torch
+        rows, dim = x.shape
+        hidden = self.w1[0].shape[0]
+        z = self._buf("z", (rows, hidden), torch.bfloat16, x.device)
+        src = x
+        for b in range(len(self.w1)):
+            a1 = self._call("quant_rmsnorm", lambda: fb.quantize(
+                src, self.fmt, prologue="rmsnorm", out=self._qbuf("a1", rows, dim, x.device)))
+            self._gemm(a1, self.q1[b], "bf16", out=z)
+            a2 = self._call("quant_gelu", lambda: fb.quantize(
+                z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
+            self._gemm(a2, self.q2[b], "f32", residual=src, out=h)
+            src = h
+        return h
+
+    def _qbuf(self, name, rows, k, device):
+        import torch
+        ldc = ((k // 2 + 15) // 16) * 16
+        codes = self._buf(name + ".c", (rows, ldc), torch.uint8, device)
+        scales = self._buf(name + ".s", (rows, k // 32), torch.uint8, device)
+        return fb.QTensor(codes, scales, None, fb.FMT_MX, k)
+
+    def run(self, noise, work=None):
+        """noise: fp32 CUDA [n_cand, tokens, dim]. The trajectory is integrated
+        in `work` (same shape; the first Euler step reads `noise` and writes
+        `work`, so `noise` stays intact), or in place in `noise` if work is None.
+        Returns (rewards [n_cand], top [k_top], bottom [k_bottom], r_norm)."""
+        import torch
+        n_cand, tokens, dim = noise.shape
+        chunk = self.chunk or n_cand
+        self._call("requantize", self.requantize)
+        x0 = noise.view(n_cand * tokens, dim)
+        x = x0 if work is None else work.view(n_cand * tokens, dim)
+        h = self._buf("h", (chunk * tokens, dim), torch.float32, noise.device)
+        t = [1.0 - i / self.steps for i in range(self.steps + 1)]
+        for i in range(self.steps):
+            src = x0 if i == 0 else x
+            for c0 in range(0, n_cand, chunk):
+                r0, rows = c0 * tokens, min(chunk, n_cand - c0) * tokens
+                xs, xd = src[r0:r0 + rows], x[r0:r0 + rows]
+                hc = self.velocity(xs, h[:rows])
+                self._call("euler", lambda: fb.euler(xs, hc, t[i], t[i + 1], out=xd))
+        rewards = self._call("reward", lambda: fb.proxy_reward(x, n_cand, tokens, self.u))
+        top, bottom, rn = self._call("select", lambda: fb.select(rewards, self.k_top, self.k_bottom))
+        return rewards, top, bottom, rn

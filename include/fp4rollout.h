@@ -1,0 +1,183 @@
+/*
+ * fp4rollout -- C ABI of the FP4 exploration hot path on MI355X (gfx950).
+ *
+ * The method (Sol-RL, "FP4 Explore, BF16 Train", project page section
+ * "Two-Stage Pipeline"; aitrends summary, Stage-1 and Stage-2 paragraphs):
+ * every iteration re-quantizes the current weights to a 4-bit float format,
+ * integrates N = 96 noise seeds with a 6-step ODE solver whose linears run as
+ * FP4 x FP4 products, scores the candidates with a proxy reward and keeps the
+ * K/2 highest- and K/2 lowest-scoring seeds (K = 24) for BF16 regeneration.
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers (hipMalloc'ed or torch-owned);
+ *     the caller owns and frees every buffer. The library allocates nothing.
+ *   - Matrices are row-major; every leading dimension ("ld*") is the distance
+ *     between consecutive rows, in ELEMENTS for float/bf16 arrays and in
+ *     BYTES for packed codes and scale bytes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it; nothing synchronizes. A device
+ *     fault therefore surfaces at the caller's next synchronization.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK status no kernel was launched and no output was touched.
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bitwise-identical outputs (no floating-point atomics are used).
+ *   - Inputs must be finite; NaN/Inf give unspecified (but memory-safe) output.
+ *   - Output buffers must not overlap inputs unless a call says otherwise.
+ */
+#ifndef FP4ROLLOUT_H
+#define FP4ROLLOUT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef FP4_API
+#define FP4_API __attribute__((visibility("default")))
+#endif
+
+typedef int32_t fp4_status;
+#define FP4_OK               0
+#define FP4_INVALID_ARGUMENT 1  /* null pointer, bad size/stride/alignment, bad enum */
+#define FP4_UNSUPPORTED      2  /* valid but not implemented combination */
+#define FP4_DEVICE_ERROR     3  /* the HIP runtime reported an error at launch */
+#define FP4_INTERNAL         4  /* unexpected host-side failure */
+
+/* block formats */
+#define FP4_FMT_MX 0  /* MXFP4: E2M1 codes, one E8M0 scale byte per 32 elements along K */
+#define FP4_FMT_NV 1  /* NVFP4-style: E2M1 codes, one E4M3 scale byte per 16 elements
+                         along K, and one fp32 scale for the whole tensor */
+
+/* element types of float arrays */
+#define FP4_DT_F32  0
+#define FP4_DT_BF16 1
+
+/* fp4_quantize flags */
+#define FP4_PRO_RMSNORM        0x1   /* quantize x * (mean_k(x^2) + 1e-6)^(-1/2) (row-wise, unit gain) */
+#define FP4_PRO_GELU           0x2   /* quantize 0.5 x (1 + erf(x / sqrt 2)) */
+#define FP4_TENSOR_SCALE_GIVEN 0x100 /* NV: read s_g from *tensor_scale instead of computing it */
+
+/*
+ * fp4_quantize -- block-scaled 4-bit quantization of a [rows, k] matrix along k.
+ *
+ * Used for the per-iteration weight re-quantization (project page,
+ * "Two-Stage Pipeline", Stage 2: weights re-quantized for the next
+ * iteration; aitrends summary: real-time re-quantization with no compile
+ * step) and for the activations entering every FP4 linear of the solver
+ * (project page: the FP4 solver's TFLOP rate needs both operands in FP4).
+ *
+ *   fmt          FP4_FMT_MX or FP4_FMT_NV.
+ *   x            [rows, ldx] elements of type x_dtype (FP4_DT_F32 or FP4_DT_BF16);
+ *                16-byte aligned, ldx*sizeof(elem) a multiple of 16, ldx >= k.
+ *   rows, k      rows >= 1; k >= 32 and a multiple of 32 (MX) or 16 (NV).
+ *   codes        out, [rows, ld_codes] bytes; byte j of a row packs elements
+ *                2j (low nibble) and 2j+1 (high nibble). Nibble = sign<<3 | m,
+ *                magnitude G[m], G = {0, .5, 1, 1.5, 2, 3, 4, 6}; nearest value,
+ *                ties to even m, saturating at 6, sign always kept.
+ *                4-byte aligned, ld_codes a multiple of 4 and >= k/2.
+ *   scales       out, [rows, ld_scales] bytes, one per block; any alignment.
+ *                MX: S = max(floor(log2 amax) - 2, -127) + 127 (E8M0, value 2^(S-127)),
+ *                    codes of x * 2^(127-S).
+ *                NV: E4M3 code of fl(amax_block / fl(6 s_g)), round to nearest even,
+ *                    saturating at 448; codes of fl(x / fl(dec(S) s_g)); a block
+ *                    whose fl(dec(S) s_g) is 0 gets signed-zero codes.
+ *                ld_scales >= k/32 (MX) or k/16 (NV).
+ *   tensor_scale MX: must be NULL. NV: device float*, 4-byte aligned; receives
+ *                s_g = fl(max|x| / 2688) (1 where that quotient is 0), or
+ *                supplies it when flags has FP4_TENSOR_SCALE_GIVEN (it must then
+ *                be positive and finite). Without that flag its word is also
+ *                used as the amax accumulator while the call runs.
+ *   flags        MX: at most one of FP4_PRO_RMSNORM / FP4_PRO_GELU (applied in
+ *                fp32 before quantization). NV: only FP4_TENSOR_SCALE_GIVEN.
+ */
+FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                        uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                        float* tensor_scale, int flags, void* stream);
+
+/*
+ * fp4_gemm -- C[m, n] = sum_k A_hat[m, k] * B_hat[n, k]  (+ residual[m, n]),
+ * accumulated in fp32. A is the activation [m, k], B the weight in nn.Linear
+ * layout [n, k], both as fp4_quantize outputs of the same format. This is the
+ * FP4 x FP4 product of every solver linear (project page, "Two-Stage
+ * Pipeline": FP4 solver at up to 4x the BF16 TFLOP rate).
+ *
+ *   fmt               FP4_FMT_MX (E8M0 scale bytes, a_ts = b_ts = NULL) or
+ *                     FP4_FMT_NV (E4M3 scale bytes, a_ts/b_ts = device float*
+ *                     tensor scales; A_hat = G dec(S) s_g).
+ *   a_codes, lda      [m, lda] bytes, 16-byte aligned, lda multiple of 16, lda >= k/2.
+ *   a_scales, ld_as   [m, ld_as] bytes, any alignment, ld_as >= k/32 (MX) or k/16 (NV).
+ *   b_codes.. ld_bs   same for B with n rows.
+ *   m, n, k           >= 1; k a multiple of 32 (MX) or 16 (NV).
+ *   c, c_dtype, ldc   out [m, ldc] of FP4_DT_F32 or FP4_DT_BF16 (fp32 rounded to
+ *                     nearest even); 16-byte aligned (fp32) or 8-byte (bf16),
+ *                     ldc a multiple of 4 elements, ldc >= n.
+ *   residual          NULL, or fp32 [m, ldc] added to the fp32 sum before the
+ *                     store (fp32 C only). residual == c (in place) is allowed.
+ * Accuracy: |C - C_exact| <= 1e-4 * sum_k |A_hat B_hat| per element for fp32 C.
+ */
+FP4_API fp4_status fp4_gemm(int fmt,
+                    const uint8_t* a_codes, int64_t lda, const uint8_t* a_scales, int64_t ld_as,
+                    const float* a_ts,
+                    const uint8_t* b_codes, int64_t ldb, const uint8_t* b_scales, int64_t ld_bs,
+                    const float* b_ts,
+                    int64_t m, int64_t n, int64_t k,
+                    void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
+
+/*
+ * euler_step -- one explicit Euler step of the sampler's ODE,
+ *   x_out = x + (t_next - t_cur) * v,
+ * with dt = fl32(t_next - t_cur) and an fp32 multiply-add per element. The
+ * rollout takes 6 such steps from t = 1 to t = 0 (aitrends summary, Stage-1
+ * paragraph: 6 FP4 inference steps; project page, "Key Insight": the ODE
+ * sampler is deterministic).
+ *   x_out, x   fp32 [numel], 16-byte aligned; x_out == x (in place) is allowed.
+ *   v          [numel] of v_dtype (FP4_DT_F32 or FP4_DT_BF16), 16-byte aligned.
+ *   numel      >= 1.
+ */
+FP4_API fp4_status euler_step(float* x_out, const float* x, const void* v, int v_dtype, int64_t numel,
+                      float t_cur, float t_next, void* stream);
+
+/*
+ * fp4_proxy_reward -- per-candidate proxy reward (project page, "Two-Stage
+ * Pipeline", Stage 1: candidates are scored with proxy rewards):
+ *   u == NULL: reward[c] = mean over the rows_per_cand x dim block of candidate c;
+ *   u != NULL: reward[c] = sum_d u[d] * (mean over rows of x[c, :, d]).
+ *   x        fp32 [n_cand * rows_per_cand, ldx], 16-byte aligned, ldx multiple of
+ *            4, ldx >= dim; dim a multiple of 4.
+ *   u        NULL or fp32 [dim], 16-byte aligned.
+ *   rewards  out fp32 [n_cand].
+ * Summed in fp32 in a fixed order (one workgroup per candidate).
+ */
+FP4_API fp4_status fp4_proxy_reward(const float* x, int64_t n_cand, int64_t rows_per_cand, int64_t dim,
+                            int64_t ldx, const float* u, float* rewards, void* stream);
+
+/*
+ * select_topk_bottomk -- the seed filter of Stage 1 (project page, "Two-Stage
+ * Pipeline": keep the top/bottom-K most contrastive seeds; aitrends summary:
+ * top K/2 and bottom K/2 of the 96 candidates), plus the normalised reward
+ * r = 1/2 + 1/2 clip((x - mean)/std, -1, 1) (VeRL-Omni DiffusionNFT docs,
+ * "Algorithm", first equation; std over the whole batch, ddof 0; std 0 -> 1/2).
+ *
+ * One total order ranks the candidates: raw reward descending, equal rewards
+ * by ascending index. top_idx[i] is the i-th entry of that order (i < k_top);
+ * bottom_idx[i] is the i-th entry from its end (i < k_bottom), i.e. lowest
+ * reward first. With k_top + k_bottom <= n the two lists are disjoint.
+ *   rewards     fp32 [n], 1 <= n <= 65536.
+ *   top_idx     out int32 [k_top] (may be NULL when k_top == 0).
+ *   bottom_idx  out int32 [k_bottom] (may be NULL when k_bottom == 0).
+ *   r_norm      NULL or out fp32 [n].
+ */
+FP4_API fp4_status select_topk_bottomk(const float* rewards, int64_t n, int64_t k_top, int64_t k_bottom,
+                               int32_t* top_idx, int32_t* bottom_idx, float* r_norm, void* stream);
+
+/* Human-readable name of a status code (static string). */
+FP4_API const char* fp4_status_str(fp4_status s);
+
+/* Version of this ABI (major * 100 + minor). */
+FP4_API int fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4ROLLOUT_H */

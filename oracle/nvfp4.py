@@ -9,7 +9,9 @@ scale for the whole tensor, applied per block.
 Steps, all IEEE fp32 and correctly rounded, in this order (no fused
 multiply-add):
   1. A_t = max |x| over the whole [rows, K] argument; s_g = A_t / 2688
-     (2688 = 6 * 448), or 1 when A_t == 0; or s_g supplied by the caller.
+     (2688 = 6 * 448), or 1 when that quotient is 0 (an all-zero tensor, or
+     one so small that the quotient underflows -- every code is then a signed
+     zero either way); or s_g supplied by the caller.
   2. per block: a_b = block amax; tau = 6 * s_g; s_f = a_b / tau.
   3. S = E4M3 code of s_f, round to nearest even, saturating at 448.
   4. d = dec(S) * s_g. If d == 0 the block's codes are signed zeros; otherwise
@@ -56,11 +58,10 @@ def e4m3_encode(s):
 
 
 def tensor_scale(x):
-    """Step 1: s_g = fl32(A_t / 2688), 1 for an all-zero tensor."""
+    """Step 1: s_g = fl32(A_t / 2688); 1 where that is 0."""
     at = F32(np.abs(np.asarray(x, dtype=F32)).max()) if np.size(x) else F32(0)
-    if at == 0:
-        return F32(1.0)
-    return F32(at / F32(2688.0))
+    sg = F32(at / F32(2688.0))
+    return F32(1.0) if sg == 0 else sg
 
 
 def quantize(x, s_g=None):

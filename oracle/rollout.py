@@ -36,29 +36,40 @@ def gelu(z):
 
 class QuantLinear:
     """A weight [out, in] quantized once per iteration (the pages' per-iteration
-    re-quantization); __call__ quantizes its fp32 input and runs the exact GEMM."""
+    re-quantization) and held dequantized (exact float64); __call__ quantizes
+    its fp32 input and forms the exact product with that weight."""
 
     def __init__(self, w, fmt):
         self.fmt = fmt
         w = np.asarray(w, dtype=np.float32)
         if fmt == "mx":
-            self.q = mxfp4.quantize(w)
+            self.w_hat = mxfp4.dequant(*mxfp4.quantize(w))
         elif fmt == "nv":
-            self.q = nvfp4.quantize(w)
+            c, s, g = nvfp4.quantize(w)
+            self.w_hat = nvfp4.dequant(c, s, g)
         elif fmt is None:
-            self.q = w.astype(np.float64)
+            self.w_hat = w.astype(np.float64)
         else:
             raise ValueError(fmt)
+
+    @classmethod
+    def from_quantized(cls, fmt, codes, scales, s_g=None):
+        """A layer whose weight is already in quantized form."""
+        self = cls.__new__(cls)
+        self.fmt = fmt
+        self.w_hat = mxfp4.dequant(codes, scales) if fmt == "mx" else nvfp4.dequant(codes, scales, s_g)
+        return self
 
     def __call__(self, x):
         x32 = np.asarray(x, dtype=np.float32)
         if self.fmt == "mx":
-            ac, as_ = mxfp4.quantize(x32)
-            return gemm.gemm_mx(ac, as_, *self.q)[0]
-        if self.fmt == "nv":
-            ac, as_, ag = nvfp4.quantize(x32)
-            return gemm.gemm_nv(ac, as_, ag, *self.q)[0]
-        return x32.astype(np.float64) @ self.q.T
+            x_hat = mxfp4.dequant(*mxfp4.quantize(x32))
+        elif self.fmt == "nv":
+            c, s, g = nvfp4.quantize(x32)
+            x_hat = nvfp4.dequant(c, s, g)
+        else:
+            x_hat = x32.astype(np.float64)
+        return gemm.gemm_dense(x_hat, self.w_hat)[0]
 
 
 def velocity(x, w1, w2):
@@ -70,13 +81,14 @@ def velocity(x, w1, w2):
 
 
 def rollout(noise, w1, w2, u, n_steps=6, fmt="mx", k_top=12, k_bottom=12):
-    """noise: [n_cand, tokens, dim]; w1/w2: lists of float weights [out, in].
+    """noise: [n_cand, tokens, dim]; w1/w2: lists of float weights [out, in]
+    (or of ready QuantLinear layers).
 
     Returns (x_final [n_cand, tokens, dim], rewards [n_cand], top, bottom)."""
     noise = np.asarray(noise, dtype=np.float32)
     n_cand, tokens, dim = noise.shape
-    q1 = [QuantLinear(w, fmt) for w in w1]
-    q2 = [QuantLinear(w, fmt) for w in w2]
+    q1 = [w if isinstance(w, QuantLinear) else QuantLinear(w, fmt) for w in w1]
+    q2 = [w if isinstance(w, QuantLinear) else QuantLinear(w, fmt) for w in w2]
     t = euler.schedule(n_steps)
     x = noise.reshape(n_cand * tokens, dim).astype(np.float64)
     for i in range(n_steps):

@@ -1,0 +1,109 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and validates arguments on the host (returning a status before any
+device work). No compute call reaches a device here: every call below is
+rejected by validation, and the pointers are never dereferenced."""
+import os
+import re
+
+import pytest
+
+import fp4_quantized_diffusion_amd as fq
+from fp4_quantized_diffusion_amd import build as fbuild
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp4rollout.h")
+P = 0x10000       # a fake, 64 KiB-aligned "device address" (never dereferenced)
+P2 = 0x20000
+P3 = 0x30000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fq.LIB_PATH):
+        fbuild.build()
+    return fq.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"FP4_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert set(names) == set(fq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert fq.fp4_abi_version() == 100
+
+
+def test_status_strings(lib):
+    assert fq.status_str(0) == "ok"
+    assert fq.status_str(1) == "invalid argument"
+    assert fq.status_str(2) == "unsupported"
+    assert fq.status_str(99) == "unknown status"
+
+
+def q(**kw):
+    a = dict(fmt=0, x=P, x_dtype=0, rows=4, k=64, ldx=64, codes=P2, ld_codes=32, scales=P3, ld_scales=2,
+             tensor_scale=None, flags=0, stream=None)
+    a.update(kw)
+    return fq.fp4_quantize(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=2), dict(x=None), dict(codes=None), dict(scales=None), dict(x_dtype=5),
+    dict(rows=0), dict(k=48), dict(k=0), dict(ldx=32), dict(ldx=66), dict(x=P + 4),
+    dict(ld_codes=16), dict(ld_codes=34), dict(codes=P2 + 2), dict(ld_scales=1),
+    dict(tensor_scale=P3), dict(flags=3), dict(flags=0x100), dict(flags=0x40),
+    dict(fmt=1, tensor_scale=None), dict(fmt=1, k=24, ldx=64, tensor_scale=P3),
+    dict(fmt=1, tensor_scale=P3 + 1), dict(rows=1 << 31),
+])
+def test_quantize_rejects(lib, kw):
+    assert q(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_quantize_nv_prologue_unsupported(lib):
+    assert q(fmt=1, tensor_scale=P3, flags=1, ld_scales=4) == fq.binding.UNSUPPORTED
+
+
+def g(**kw):
+    a = dict(fmt=0, a=P, lda=32, a_s=P3, ld_as=2, a_ts=None, b=P2, ldb=32, b_s=P3, ld_bs=2, b_ts=None,
+             m=8, n=8, k=64, c=P, c_dtype=0, ldc=8, residual=None, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(b=None), dict(a_s=None), dict(c=None), dict(m=0), dict(n=0),
+    dict(k=48), dict(lda=16), dict(lda=40), dict(a=P + 8), dict(ldb=24), dict(ld_as=1), dict(ld_bs=1),
+    dict(c_dtype=7), dict(ldc=6), dict(ldc=10), dict(c=P + 4), dict(c_dtype=1, c=P + 2),
+    dict(c_dtype=1, residual=P2), dict(residual=P2 + 4), dict(a_ts=P3), dict(fmt=1),
+    dict(fmt=1, a_ts=P3, b_ts=None), dict(k=1 << 25, lda=1 << 24, ldb=1 << 24, ld_as=1 << 20, ld_bs=1 << 20),
+])
+def test_gemm_rejects(lib, kw):
+    assert g(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("args", [
+    (None, P, P2, 0, 16, 1.0, 0.5, None), (P, P, P2, 0, 0, 1.0, 0.5, None), (P, P, P2, 9, 16, 1.0, 0.5, None),
+    (P + 4, P, P2, 0, 16, 1.0, 0.5, None), (P, P, P2 + 8, 1, 16, 1.0, 0.5, None),
+])
+def test_euler_rejects(lib, args):
+    assert fq.euler_step(*args) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("args", [
+    (None, 2, 2, 8, 8, None, P2, None), (P, 0, 2, 8, 8, None, P2, None), (P, 2, 2, 6, 8, None, P2, None),
+    (P, 2, 2, 8, 4, None, P2, None), (P, 2, 2, 8, 8, P3 + 4, P2, None), (P, 2, 2, 8, 8, None, None, None),
+])
+def test_reward_rejects(lib, args):
+    assert fq.fp4_proxy_reward(*args) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("args", [
+    (None, 8, 2, 2, P, P2, None, None), (P, 0, 0, 0, P, P2, None, None), (P, 8, 5, 4, P, P2, None, None),
+    (P, 8, -1, 2, P, P2, None, None), (P, 8, 2, 2, None, P2, None, None), (P, 8, 2, 2, P, None, None, None),
+    (P, 65537, 2, 2, P, P2, None, None), (P + 2, 8, 2, 2, P, P2, None, None),
+])
+def test_select_rejects(lib, args):
+    assert fq.select_topk_bottomk(*args) == fq.binding.INVALID_ARGUMENT

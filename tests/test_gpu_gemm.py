@@ -1,0 +1,154 @@
+"""GPU parity: fp4_gemm against the oracle's exact dequantized product.
+|C_gpu - C| <= 1e-4 * sum_k |A_hat B_hat| per element (fp32 C), plus one bf16
+rounding of C for bf16 output; bit-exact in the exact-integer case."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_quantized_diffusion_amd import inputs
+from oracle import gemm as ogemm, mxfp4, nvfp4
+from tests._parity import gemm_within_tol, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def quantize_both(fq, a, b, fmt, dtype=torch.float32):
+    qa = fq.quantize(dev(a.astype(np.float32)).to(dtype), fmt)
+    qb = fq.quantize(dev(b.astype(np.float32)).to(dtype), fmt)
+    return qa, qb
+
+
+def oracle_c(qa, qb, fmt, rows=None, cols=None):
+    k = qa.k
+    ac, as_ = to_np(qa.codes)[:, : k // 2], to_np(qa.scales)
+    bc, bs = to_np(qb.codes)[:, : k // 2], to_np(qb.scales)
+    if rows is not None:
+        ac, as_ = ac[rows], as_[rows]
+    if cols is not None:
+        bc, bs = bc[cols], bs[cols]
+    if fmt == "mx":
+        return ogemm.gemm_mx(ac, as_, bc, bs)
+    return ogemm.gemm_nv(ac, as_, to_np(qa.tensor_scale)[0], bc, bs, to_np(qb.tensor_scale)[0])
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_tiny_config(gpu_lib, fmt, out):
+    x, b = inputs.tiny(0)
+    qa, qb = quantize_both(gpu_lib, x, b, fmt)
+    c = gpu_lib.gemm(qa, qb, out)
+    c_exact, s_abs = oracle_c(qa, qb, fmt)
+    ok, worst = gemm_within_tol(to_np(c.float()), c_exact, s_abs, bf16_out=(out == "bf16"))
+    assert ok, worst
+
+
+def test_exact_integer_case_bit_exact(gpu_lib):
+    """Scales 2^0 and grid codes: products are multiples of 1/4 and partial
+    sums stay below 2^22, so fp32 accumulation is exact and the GPU result
+    must equal the oracle bit for bit -- any operand-layout, K-order or
+    scale-plumbing slip shows up here."""
+    rng = np.random.default_rng(30)
+    for (m, n, k) in [(256, 256, 256), (300, 260, 512), (129, 515, 4096), (16, 16, 32)]:
+        ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+        bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        as_ = np.full((m, k // 32), 127, np.uint8)
+        bs = np.full((n, k // 32), 127, np.uint8)
+        from fp4_quantized_diffusion_amd.binding import QTensor, FMT_MX
+        lda = ((k // 2 + 15) // 16) * 16
+        acd = torch.zeros((m, lda), dtype=torch.uint8, device=DEV); acd[:, : k // 2] = dev(ac)
+        bcd = torch.zeros((n, lda), dtype=torch.uint8, device=DEV); bcd[:, : k // 2] = dev(bc)
+        qa = QTensor(acd, dev(as_), None, FMT_MX, k)
+        qb = QTensor(bcd, dev(bs), None, FMT_MX, k)
+        c = to_np(gpu_lib.gemm(qa, qb, "f32"))
+        c_exact, _ = ogemm.gemm_mx(ac, as_, bc, bs)
+        np.testing.assert_array_equal(c.astype(np.float64), c_exact)
+
+
+def test_varied_scales_exact_rational_small(gpu_lib):
+    """Random codes and random E8M0 scales (not from a quantizer) -- exercises
+    the per-lane scale selection of every K-block."""
+    rng = np.random.default_rng(31)
+    m, n, k = 64, 48, 512
+    ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(117, 138, size=(m, k // 32), dtype=np.uint8)
+    bs = rng.integers(117, 138, size=(n, k // 32), dtype=np.uint8)
+    from fp4_quantized_diffusion_amd.binding import QTensor, FMT_MX
+    qa = QTensor(dev(ac), dev(as_), None, FMT_MX, k)
+    qb = QTensor(dev(bc), dev(bs), None, FMT_MX, k)
+    c = to_np(gpu_lib.gemm(qa, qb, "f32"))
+    c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+    ok, worst = gemm_within_tol(c, c_exact, s_abs)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("shape", [(300, 260, 96), (257, 513, 2240), (100, 70, 5600), (33, 2432, 9728), (1, 1, 32)])
+def test_ragged_shapes(gpu_lib, fmt, shape):
+    m, n, k = shape
+    rng = np.random.default_rng(m * 7 + n)
+    a = rng.standard_t(4, size=(m, k)).astype(np.float32)
+    b = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    qa, qb = quantize_both(gpu_lib, a, b, fmt)
+    for out in ("f32", "bf16"):
+        c = gpu_lib.gemm(qa, qb, out)
+        c_exact, s_abs = oracle_c(qa, qb, fmt)
+        ok, worst = gemm_within_tol(to_np(c.float()), c_exact, s_abs, bf16_out=(out == "bf16"))
+        assert ok, (out, worst)
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_residual_and_in_place(gpu_lib, fmt):
+    rng = np.random.default_rng(32)
+    m, n, k = 200, 300, 640
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    b = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    r = rng.standard_normal((m, n)).astype(np.float32)
+    qa, qb = quantize_both(gpu_lib, a, b, fmt)
+    c_exact, s_abs = oracle_c(qa, qb, fmt)
+    rd = dev(r)
+    c = to_np(gpu_lib.gemm(qa, qb, "f32", residual=rd))
+    ok, worst = gemm_within_tol(c, c_exact + r, s_abs + np.abs(r) * 1e-3)
+    assert ok, worst
+    gpu_lib.gemm(qa, qb, "f32", residual=rd, out=rd)   # in place
+    ok, worst = gemm_within_tol(to_np(rd), c_exact + r, s_abs + np.abs(r) * 1e-3)
+    assert ok, worst
+
+
+def test_determinism(gpu_lib):
+    rng = np.random.default_rng(33)
+    a = rng.standard_normal((512, 1024)).astype(np.float32)
+    b = rng.standard_normal((768, 1024)).astype(np.float32)
+    qa, qb = quantize_both(gpu_lib, a, b, "mx")
+    c0 = to_np(gpu_lib.gemm(qa, qb, "f32"))
+    for _ in range(5):
+        np.testing.assert_array_equal(to_np(gpu_lib.gemm(qa, qb, "f32")), c0)
+
+
+@pytest.mark.parametrize("cls,which", [("flux", 1), ("flux", 2), ("sana", 2), ("sd35", 1)])
+def test_full_size_sampled(gpu_lib, cls, which):
+    """Workload-class GEMMs at full size, in the launch configuration the
+    benchmark uses (bf16 activations, bf16 output): quantized codes of sampled
+    rows are bit-exact and sampled outputs are within tolerance."""
+    a, w = inputs.class_linear(cls, which)
+    qa, qb = quantize_both(gpu_lib, a, w, "mx", torch.bfloat16)
+    c = gpu_lib.gemm(qa, qb, "bf16")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(34)
+    rows = np.sort(rng.choice(a.shape[0], 48, replace=False))
+    rows[-1] = a.shape[0] - 1
+    cols = np.sort(rng.choice(w.shape[0], 64, replace=False))
+    cols[-1] = w.shape[0] - 1
+    oc, os_ = mxfp4.quantize(a[rows])
+    k = a.shape[1]
+    np.testing.assert_array_equal(to_np(qa.codes[rows])[:, : k // 2], oc)
+    np.testing.assert_array_equal(to_np(qa.scales[rows]), os_)
+    c_exact, s_abs = oracle_c(qa, qb, "mx", rows, cols)
+    c_s = to_np(c.float())[np.ix_(rows, cols)]
+    ok, worst = gemm_within_tol(c_s, c_exact, s_abs, bf16_out=True)
+    assert ok, worst

@@ -1,0 +1,158 @@
+"""GPU parity: fp4_quantize (MXFP4 and NVFP4-style) against the oracle.
+Codes, scale bytes and the NV tensor scale must be bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_quantized_diffusion_amd import inputs
+from oracle import mxfp4, nvfp4, rollout as orollout
+from tests._parity import mx_codes_near_boundary_ok, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gpu_quant(fq, x_np, fmt, dtype=torch.float32, prologue=None):
+    x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).to(DEV).to(dtype)
+    q = fq.quantize(x, fmt, prologue=prologue)
+    torch.cuda.synchronize()
+    k = x_np.shape[1]
+    codes = to_np(q.codes)[:, : k // 2]
+    scales = to_np(q.scales)
+    ts = None if q.tensor_scale is None else np.float32(to_np(q.tensor_scale)[0])
+    return codes, scales, ts
+
+
+def special_values(rows, k, seed):
+    """Signed zeros, fp32 subnormals, E2M1 midpoints and grid points times
+    powers of two, huge values, and blocks of mixed binades."""
+    rng = np.random.default_rng(seed)
+    base = np.array([0.0, -0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.9, 0.5, 1e-40, -3e-41,
+                     3e38, -1.5, 4.0, 0.3], dtype=np.float32)
+    x = rng.choice(base, size=(rows, k)).astype(np.float64) * np.ldexp(1.0, rng.integers(-30, 30, size=(rows, 1)))
+    x = np.clip(x, -3.0e38, 3.0e38).astype(np.float32)   # finite inputs only
+    x[0] = 0.0
+    x[1] = -0.0
+    return x
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_tiny_config_bit_exact(gpu_lib, fmt):
+    x, b = inputs.tiny(0)
+    for mat in (x, b):
+        gc, gs, gt = gpu_quant(gpu_lib, mat, fmt)
+        if fmt == "mx":
+            oc, os_ = mxfp4.quantize(mat)
+        else:
+            oc, os_, ot = nvfp4.quantize(mat)
+            assert gt.tobytes() == np.float32(ot).tobytes()
+        np.testing.assert_array_equal(gc, oc)
+        np.testing.assert_array_equal(gs, os_)
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(1, 32), (37, 96), (300, 2240), (5, 5600)])
+def test_ragged_shapes_bit_exact(gpu_lib, fmt, dtype, shape):
+    rng = np.random.default_rng(hash((fmt, shape)) % 2**32)
+    x = (rng.standard_t(4, size=shape) * np.exp(rng.uniform(-4, 4, (shape[0], 1)))).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = inputs.to_bf16(x)
+    gc, gs, gt = gpu_quant(gpu_lib, x, fmt, dtype)
+    if fmt == "mx":
+        oc, os_ = mxfp4.quantize(x)
+    else:
+        oc, os_, ot = nvfp4.quantize(x)
+        assert gt == ot
+    np.testing.assert_array_equal(gc, oc)
+    np.testing.assert_array_equal(gs, os_)
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_special_values_bit_exact(gpu_lib, fmt):
+    x = special_values(64, 256, 3)
+    gc, gs, gt = gpu_quant(gpu_lib, x, fmt)
+    if fmt == "mx":
+        oc, os_ = mxfp4.quantize(x)
+    else:
+        oc, os_, ot = nvfp4.quantize(x)
+        assert gt == ot
+    np.testing.assert_array_equal(gc, oc)
+    np.testing.assert_array_equal(gs, os_)
+
+
+def test_zero_and_tiny_tensors_nv(gpu_lib):
+    for x in (np.zeros((3, 32), np.float32), np.full((2, 16), 1e-44, np.float32), -np.zeros((1, 16), np.float32)):
+        gc, gs, gt = gpu_quant(gpu_lib, x, "nv")
+        oc, os_, ot = nvfp4.quantize(x)
+        assert gt == ot
+        np.testing.assert_array_equal(gc, oc)
+        np.testing.assert_array_equal(gs, os_)
+
+
+def test_nv_given_tensor_scale(gpu_lib):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    sg = np.float32(0.0123)
+    xt = torch.from_numpy(x).to(DEV)
+    q = gpu_lib.quantize(xt, "nv", tensor_scale=torch.tensor([sg], device=DEV))
+    oc, os_, ot = nvfp4.quantize(x, s_g=sg)
+    np.testing.assert_array_equal(to_np(q.codes)[:, :32], oc)
+    np.testing.assert_array_equal(to_np(q.scales), os_)
+    assert to_np(q.tensor_scale)[0] == sg
+
+
+def test_element_rounding_sweep_mx(gpu_lib):
+    """fp32 values with exponent in [2^-3, 2^3): every 5th mantissa of each
+    binade plus every value within 256 ulps of each E2M1 decision point and
+    grid point, both signs, each in a block whose amax is pinned to [4, 8) so
+    the scale is 2^0. The GPU's element rounding must equal the oracle's."""
+    e_lo, e_hi = 124, 130
+    sweep = np.arange(e_lo << 23, e_hi << 23, 5, dtype=np.uint32)
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0],
+                   dtype=np.float32).view(np.uint32)
+    near = (pts[:, None].astype(np.int64) + np.arange(-256, 257)[None, :]).reshape(-1).astype(np.uint32)
+    mags = np.unique(np.concatenate([sweep, near])).view(np.float32)
+    mags = mags[mags < 8]
+    n = mags.size
+    per = 31
+    rows = -(-n // per)
+    flat = np.zeros(rows * per, dtype=np.float32)
+    flat[:n] = mags
+    x = np.zeros((rows, 32), dtype=np.float32)
+    x[:, 1:] = flat.reshape(rows, per)
+    x[:, 0] = 4.0
+    x[1::2] = -x[1::2]  # both signs
+    gc, gs, _ = gpu_quant(gpu_lib, x, "mx")
+    assert np.all(gs == 127)
+    step = 1 << 16
+    for r0 in range(0, rows, step):
+        oc, os_ = mxfp4.quantize(x[r0:r0 + step])
+        np.testing.assert_array_equal(gc[r0:r0 + step], oc)
+
+
+@pytest.mark.parametrize("prologue", ["gelu", "rmsnorm"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_mx_prologues(gpu_lib, prologue, dtype):
+    """Fused prologue then quantization: the prologue is fp32 on the GPU and
+    float64 in the oracle, so a code may differ only where the exact input
+    lies within 2e-6 (relative) of a decision point."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((256, 3072)) * 2).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = inputs.to_bf16(x)
+    gc, gs, _ = gpu_quant(gpu_lib, x, "mx", dtype, prologue=prologue)
+    ref = orollout.gelu(x) if prologue == "gelu" else orollout.rmsnorm(x)
+    bad, flips = mx_codes_near_boundary_ok(ref, gc, gs)
+    assert bad == 0, (bad, flips)
+    assert flips <= 50
+
+
+def test_weight_requantization_full_flux(gpu_lib):
+    """FLUX-class W1 [12288, 3072] bf16, full size: bit-exact on sampled rows."""
+    _, w = inputs.class_linear("flux", 1, rows=8)
+    gc, gs, _ = gpu_quant(gpu_lib, w, "mx", torch.bfloat16)
+    rows = np.random.default_rng(0).choice(w.shape[0], 64, replace=False)
+    oc, os_ = mxfp4.quantize(w[rows])
+    np.testing.assert_array_equal(gc[rows], oc)
+    np.testing.assert_array_equal(gs[rows], os_)
