@@ -70,21 +70,19 @@ __device__ __forceinline__ void make_operand(Operand& o, const uint8_t* codes, i
 // scale. SB = scale bytes per row per stage (8: MX, 16: NV); `bpb` = code
 // bytes per scale block (16: MX, 8: NV).
 template <int SB>
-__device__ __forceinline__ void load_operand(uint4 q[8], uint32_t sc[SB / 4], const Operand& o, int kb,
-                                             int kbytes, int bpb) {
+__device__ __forceinline__ void load_operand(uint4 q[8], uint32_t sc[SB], const Operand& o, int kb, int kbytes,
+                                             int bpb) {
   const int chunk = threadIdx.x & 7;
   const bool kin = kb + chunk * 16 < kbytes;
 #pragma unroll
   for (int it = 0; it < 8; ++it)
     q[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(o.codes, kin ? o.off[it] : kOob, kb, 0));
+  // scale bytes stay unpacked until the stage is stored to LDS, so no wait on
+  // them is needed before the MFMAs that overlap these loads
   const int kblk = kb / bpb, nblk = kbytes / bpb;
 #pragma unroll
-  for (int w = 0; w < SB / 4; ++w) sc[w] = 0;
-#pragma unroll
-  for (int j = 0; j < SB; ++j) {
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(o.scales, kblk + j < nblk ? o.soff + j : kOob, kblk, 0);
-    sc[j >> 2] |= v << (8 * (j & 3));
-  }
+  for (int j = 0; j < SB; ++j)
+    sc[j] = __builtin_amdgcn_raw_buffer_load_b8(o.scales, kblk + j < nblk ? o.soff + j : kOob, kblk, 0);
 }
 
 template <int SB>
@@ -98,7 +96,7 @@ struct Smem {
 template <int SB>
 struct Prefetch {
   uint4 a[8], b[8];
-  uint32_t as[SB / 4], bs[SB / 4];
+  uint32_t as[SB], bs[SB];  // one scale byte per register
 };
 
 template <int SB>
@@ -118,12 +116,18 @@ __device__ __forceinline__ void store_stage(Smem<SB>& s, int buf, const Prefetch
     *reinterpret_cast<uint4*>(&s.a[buf][r * ROWB + chunk * 16]) = p.a[it];
     *reinterpret_cast<uint4*>(&s.b[buf][r * ROWB + chunk * 16]) = p.b[it];
   }
+  uint32_t wa[SB / 4], wb[SB / 4];
+#pragma unroll
+  for (int w = 0; w < SB / 4; ++w) {
+    wa[w] = p.as[4 * w] | (p.as[4 * w + 1] << 8) | (p.as[4 * w + 2] << 16) | (p.as[4 * w + 3] << 24);
+    wb[w] = p.bs[4 * w] | (p.bs[4 * w + 1] << 8) | (p.bs[4 * w + 2] << 16) | (p.bs[4 * w + 3] << 24);
+  }
   if (SB == 8) {
-    *reinterpret_cast<uint2*>(&s.as[buf][t * SB]) = make_uint2(p.as[0], p.as[1]);
-    *reinterpret_cast<uint2*>(&s.bs[buf][t * SB]) = make_uint2(p.bs[0], p.bs[1]);
+    *reinterpret_cast<uint2*>(&s.as[buf][t * SB]) = make_uint2(wa[0], wa[1]);
+    *reinterpret_cast<uint2*>(&s.bs[buf][t * SB]) = make_uint2(wb[0], wb[1]);
   } else {
-    *reinterpret_cast<uint4*>(&s.as[buf][t * SB]) = make_uint4(p.as[0], p.as[1], p.as[2 % (SB / 4)], p.as[3 % (SB / 4)]);
-    *reinterpret_cast<uint4*>(&s.bs[buf][t * SB]) = make_uint4(p.bs[0], p.bs[1], p.bs[2 % (SB / 4)], p.bs[3 % (SB / 4)]);
+    *reinterpret_cast<uint4*>(&s.as[buf][t * SB]) = make_uint4(wa[0], wa[1], wa[2 % (SB / 4)], wa[3 % (SB / 4)]);
+    *reinterpret_cast<uint4*>(&s.bs[buf][t * SB]) = make_uint4(wb[0], wb[1], wb[2 % (SB / 4)], wb[3 % (SB / 4)]);
   }
 }
 
