@@ -108,7 +108,7 @@ def rank_stats(a, b, k):
             "bottom_overlap": len(ba & bb), "k": k}
 
 
-def cpu_baseline(cfg, tokens_sample=16, w_rows_sample=256):
+def cpu_baseline(cfg, tokens_sample=32, w_rows_sample=256):
     """The CPU oracle on a bounded sample of the rollout, scaled to candidates/s:
     (a) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one W1,
         scaled by element count to all 8 weights (once per rollout);
@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-agreement", action="store_true")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
+                         "profiler byte counters); not part of any step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the rollout shards over candidates "
@@ -178,6 +181,13 @@ def main():
     ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
                     timer=timer)
 
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: {args.copy_calibration} MiB read + {args.copy_calibration} MiB written")
     timer.enabled = False
     for i in range(args.warmup):
         ro.run(noise, work)

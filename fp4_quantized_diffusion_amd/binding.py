@@ -150,7 +150,10 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None):
     if out is None:
         ldc = ((k // 2 + 15) // 16) * 16
         codes = torch.empty((rows, ldc), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, max(k // blk, 1)), dtype=torch.uint8, device=x.device)
+        # scale rows padded to a multiple of 4 bytes: the GEMM then loads each
+        # stage's scale bytes as whole words
+        lds = ((max(k // blk, 1) + 3) // 4) * 4
+        scales = torch.empty((rows, lds), dtype=torch.uint8, device=x.device)[:, : max(k // blk, 1)]
         ts = None
         if f == FMT_NV:
             ts = torch.empty(1, dtype=torch.float32, device=x.device)

@@ -6,27 +6,34 @@
 // with A the activation [M, K] and B the weight [N, K], both MXFP4 (E2M1
 // codes, one E8M0 scale per 32 along K).
 //
-// Hardware mapping (gfx950, V_MFMA_SCALE_F32_16X16X128_F8F6F4 with FP4
-// operands): lane l of a wave supplies row (l % 16) of its operand and the 32
-// consecutive K-elements of K-block (l / 16) -- 16 packed bytes, exactly a
-// slice of the row-major code layout -- plus that block's E8M0 scale byte.
-// The accumulator holds D[4 (l / 16) + j][l % 16], j = 0..3.
-//
-// The WEIGHT rows feed the MFMA's first operand and the ACTIVATION rows its
-// second, so D's row index is n and its column index is m: each lane then
-// holds 4 consecutive n of one m row and stores them as one 16-byte (fp32)
-// or 8-byte (bf16) vector.
-//
-// K order: a stage covers 8 K-blocks (256 elements, 128 bytes per row). For
-// MFMA sub-step kk (0, 1) lane group g = l / 16 takes K-block 2g + kk, so a
-// lane's two scales are adjacent bytes (one 16-bit LDS read; the MFMA's
-// op_sel picks byte kk) and its codes are 32 contiguous bytes. Any
-// permutation of K applied to both operands leaves the sum unchanged.
-//
-// Tiling: 256 x 256 output tile per 256-thread workgroup (4 waves, 2 x 2,
-// 128 x 128 each: 8 x 8 MFMA tiles, 256 fp32 accumulators per lane).
-// Stages are double-buffered in LDS; the next stage's global loads are in
-// flight while the current stage's 128 MFMAs per wave run.
+// Design (gfx950):
+//  * MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands. Lane l
+//    supplies row l % 32 and the 32 K-elements of K-block l / 32 of a
+//    64-element K step (16 packed bytes -- a slice of the row-major code
+//    layout) plus that block's E8M0 byte; the accumulator holds
+//    D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15. Weight rows feed
+//    the MFMA's first operand, so D's row index is n and its column index m.
+//  * K order: a 128-element K stage is two K steps; in step ks lane half
+//    h = l / 32 takes K-block 2h + ks, so a lane's codes for the stage are 32
+//    contiguous bytes and its two scale bytes one 16-bit word (the MFMA's
+//    op_sel picks byte ks). Any K permutation applied to both operands leaves
+//    the sum unchanged.
+//  * Tiles: 256 x 256 outputs per 256-thread workgroup (4 waves of 128 x 128:
+//    4 x 4 MFMA tiles, 256 fp32 accumulators per lane in AGPRs).
+//  * Persistent: one workgroup per CU walks a sequence of tiles; its K
+//    stages form one stream across tiles. A ring of four LDS stage buffers
+//    keeps three stages in flight, filled by direct global->LDS buffer loads
+//    (no registers), so the next tile's first stages arrive while the
+//    current tile finishes and its epilogue runs.
+//  * Each pipeline step waits for the next stage, issues the stage four
+//    ahead, and runs the current stage's MFMAs from registers while the next
+//    stage's fragments are read from LDS.
+//  * Epilogue straight from registers: one lane-half swap (v_permlane32_swap)
+//    gives every lane 16 consecutive n of its m row, stored as 16-byte vectors.
+//  * Tile order: workgroups are dispatched round-robin over the 8 XCDs; the
+//    tile map gives each XCD a contiguous band of tiles, walked in groups of
+//    kGroupM tile-rows, so tiles that run together on an XCD share A and B
+//    panels in its L2.
 #include "gemm_common.h"
 
 namespace fp4r {
@@ -36,91 +43,109 @@ using namespace gemm;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// K stage = 128 elements: 64 code bytes and 4 scale bytes per row.
-constexpr int KSTAGE_B = 64;
-constexpr int SCB = 4;
-constexpr int NBUF = 4;      // LDS stage buffers: three stages in flight while one is consumed
+constexpr int KSTAGE_B = 64;  // code bytes per row per K stage (128 elements)
+constexpr int SCB = 4;        // scale bytes per row per K stage
+constexpr int NBUF = 4;       // LDS stage buffers
 
-// One K stage in LDS: codes of both operands and their scale bytes, all
-// written by direct global->LDS loads. The stage buffers are separate
-// objects, so the compiler can see that reading one never depends on the
-// loads in flight into another.
+// One K stage in LDS. The buffers are separate objects, so the compiler can
+// see that reading one never depends on the loads in flight into another.
 struct __attribute__((aligned(16))) StageMx {
   uint8_t a[BM * KSTAGE_B];
   uint8_t b[BN * KSTAGE_B];
   uint8_t as[BM * SCB];
   uint8_t bs[BN * SCB];
 };
-constexpr int kEpiRow = 272;  // epilogue staging row stride (bytes): 256 B of bf16 + 16 B against conflicts
 
 // 16-byte chunk c (0..3) of row r lives at position c ^ ((r >> 2) & 3): the
 // 16 rows of a fragment read then cover every (r % 4, position) pair, i.e.
 // all 64 LDS banks, without conflicts.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-struct OperandMx {
-  __amdgpu_buffer_rsrc_t codes, scales;
-  uint32_t off[4];   // this lane's chunk for each of the wave's 4 code loads of a stage
-  uint32_t soff;     // this lane's scale word / byte of a stage
+// Problem description shared by every step.
+struct Problem {
+  const uint8_t *a, *as, *b, *bs;
+  int64_t lda, ld_as, ldb, ld_bs;
+  int M, N, kbytes, nblk;
+  int tiles_m, tiles_n, total;
 };
 
-// Code loads: wave w's load `it` fills LDS rows 16 (4 w + it) .. +15 (1 KB);
-// lane L writes position L % 4 of row 16 (4 w + it) + L / 4, i.e. global
-// chunk (L % 4) ^ swizzle. Scales: thread t handles row t. With 4-byte
-// aligned scale rows (SDW) the stage's 4 scale bytes are one word, loaded
-// straight into LDS (a wave fills rows 64 w .. +63); otherwise the thread
-// loads the 4 bytes into registers and writes the word to LDS itself.
-template <bool SDW>
-__device__ __forceinline__ void make_operand_mx(OperandMx& o, const uint8_t* codes, int64_t ld, const uint8_t* scales,
-                                                int64_t ld_s, int row0, int rows) {
-  const int valid = min(rows - row0, 256);
-  o.codes = make_rsrc(codes + (int64_t)row0 * ld, (int64_t)valid * ld);
-  o.scales = make_rsrc(scales + (int64_t)row0 * ld_s, (int64_t)valid * ld_s);
+// This thread's share of a stage load, independent of the tile: code chunk
+// offsets for its 4 code loads per operand (wave w's load `it` fills LDS rows
+// 16 (4 w + it) .. +15; lane L writes position L % 4 of row
+// 16 (4 w + it) + L / 4) and its scale row (row t).
+struct LaneOffsets {
+  uint32_t ca[4], cb[4];
+  uint32_t sa, sb;
+};
+
+__device__ __forceinline__ void make_lane_offsets(LaneOffsets& o, const Problem& p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = (w * 4 + it) * 16 + (lane >> 2);
-    o.off[it] = (uint32_t)(r * ld + swz(r, lane & 3) * 16);
+    o.ca[it] = (uint32_t)(r * p.lda + swz(r, lane & 3) * 16);
+    o.cb[it] = (uint32_t)(r * p.ldb + swz(r, lane & 3) * 16);
   }
-  o.soff = (uint32_t)((w * 64 + lane) * ld_s);  // this thread's scale row (both paths)
+  o.sa = (uint32_t)(threadIdx.x * p.ld_as);
+  o.sb = (uint32_t)(threadIdx.x * p.ld_bs);
 }
 
-// Issue stage `st` into `dst`. Code chunks at or past the row's code length
-// read as zero (out-of-range offset): zero codes contribute nothing whatever
-// their scale. Without SDW the scale bytes come back in sc[] (issued first,
-// so they complete before this stage's code loads) and are written to LDS
-// by store_scale_regs().
+// Buffer resources of one tile's operands (uniform, in SGPRs). Loads past
+// the matrix (rows past M / N, a tile past the last) read as zero through
+// the buffer range check.
+struct TileDesc {
+  __amdgpu_buffer_rsrc_t a, b, as, bs;
+};
+
+__device__ __forceinline__ TileDesc make_desc(const Problem& p, int pid) {
+  int tm = 0, tn = 0;
+  const bool live = pid < p.total;
+  if (live) tile_coords(pid, p.tiles_m, p.tiles_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t va = live ? min(p.M - m0, BM) : 0, vb = live ? min(p.N - n0, BN) : 0;
+  TileDesc d;
+  d.a = make_rsrc(p.a + (int64_t)m0 * p.lda, va * p.lda);
+  d.b = make_rsrc(p.b + (int64_t)n0 * p.ldb, vb * p.ldb);
+  d.as = make_rsrc(p.as + (int64_t)m0 * p.ld_as, va * p.ld_as);
+  d.bs = make_rsrc(p.bs + (int64_t)n0 * p.ld_bs, vb * p.ld_bs);
+  return d;
+}
+
+// Issue K stage `st` of the tile described by `d` into `dst`. Code bytes
+// past K read as zero (out-of-range offset): zero codes contribute nothing
+// whatever their scale. Without SDW (scale rows not 4-byte aligned) the
+// scale bytes come back in sc[] -- issued first, so they complete before
+// this stage's code loads -- and are written to LDS by store_scale_regs().
 template <bool SDW>
-__device__ __forceinline__ void issue_stage(StageMx& dst, const OperandMx& oa, const OperandMx& ob, int st,
-                                            int kbytes, uint32_t sc[8]) {
+__device__ __forceinline__ void issue_stage(StageMx& dst, const Problem& p, const LaneOffsets& o, const TileDesc& d,
+                                            int st, uint32_t sc[8]) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kb = st * KSTAGE_B;
-  const int kblk = st * SCB, nblk = kbytes >> 4;
+  const int kb = st * KSTAGE_B, kblk = st * SCB;
   if (!SDW) {
 #pragma unroll
     for (int j = 0; j < SCB; ++j) {
-      const bool in = kblk + j < nblk;
-      sc[j] = __builtin_amdgcn_raw_buffer_load_b8(oa.scales, in ? oa.soff + j : kOob, kblk, 0);
-      sc[SCB + j] = __builtin_amdgcn_raw_buffer_load_b8(ob.scales, in ? ob.soff + j : kOob, kblk, 0);
+      const bool in = kblk + j < p.nblk;
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b8(d.as, in ? o.sa + j : kOob, kblk, 0);
+      sc[SCB + j] = __builtin_amdgcn_raw_buffer_load_b8(d.bs, in ? o.sb + j : kOob, kblk, 0);
     }
   }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = (w * 4 + it) * 16 + (lane >> 2);
-    const bool kin = kb + swz(r, lane & 3) * 16 < kbytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(oa.codes, (lds_ptr_t)(dst.a + (w * 4 + it) * 1024), 16,
-                                             kin ? oa.off[it] : kOob, kb, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ob.codes, (lds_ptr_t)(dst.b + (w * 4 + it) * 1024), 16,
-                                             kin ? ob.off[it] : kOob, kb, 0, 0);
+    const bool kin = kb + swz(r, lane & 3) * 16 < p.kbytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, (lds_ptr_t)(dst.a + (w * 4 + it) * 1024), 16,
+                                             kin ? o.ca[it] : kOob, kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, (lds_ptr_t)(dst.b + (w * 4 + it) * 1024), 16,
+                                             kin ? o.cb[it] : kOob, kb, 0, 0);
   }
   if (SDW) {
-    // whole words: bytes past the block count (inside the row's padding) are
-    // neutralised when the fragments are read
-    const bool in = kblk < nblk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(oa.scales, (lds_ptr_t)(dst.as + w * 256), 4, in ? oa.soff : kOob,
-                                             kblk, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ob.scales, (lds_ptr_t)(dst.bs + w * 256), 4, in ? ob.soff : kOob,
-                                             kblk, 0, 0);
+    // whole 4-byte words (a wave fills rows 64 w .. +63); bytes past the
+    // block count lie in the row and are neutralised when fragments are read
+    const bool in = kblk < p.nblk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.as, (lds_ptr_t)(dst.as + w * 256), 4, in ? o.sa : kOob, kblk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.bs, (lds_ptr_t)(dst.bs + w * 256), 4, in ? o.sb : kOob, kblk, 0, 0);
   }
 }
 
@@ -131,7 +156,7 @@ __device__ __forceinline__ void store_scale_regs(StageMx& dst, const uint32_t sc
 
 // The lane's two scale bytes (K-blocks 2h, 2h+1 of stage st) with blocks
 // past the end replaced by 127 (2^0): their codes are zero, but a stray
-// 0xFF (NaN) scale byte from row padding must not reach the MFMA.
+// 0xFF (NaN) byte from row padding must not reach the MFMA.
 __device__ __forceinline__ int clean_scales(int v, int st, int nblk, int h) {
   const int b0 = st * SCB + 2 * h;
   if (b0 + 1 < nblk) return v;
@@ -139,14 +164,31 @@ __device__ __forceinline__ int clean_scales(int v, int st, int nblk, int h) {
   return 0x7F7F;
 }
 
-template <int KS>
-__device__ __forceinline__ v16f mfma_ks(v8i w, v8i x, v16f acc, int sw, int sx) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, acc, 4, 4, KS, sw, KS, sx);
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all of its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// Fragments of K step ks: lane half h takes K-block 2h + ks of the stage.
+// A barrier without the release fence of __syncthreads(), which would also
+// wait for the younger stages still in flight. The asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// All of one stage's fragments for this lane: scales and both K steps' codes.
+struct Frags {
+  int sw[4], sx[4];
+  v8i w0[4], x0[4], w1[4], x1[4];
+};
+
 template <int KS>
-__device__ __forceinline__ void read_frags(const StageMx& cur, int rn0, int rm0, int h, v8i fw[4], v8i fx[4]) {
+__device__ __forceinline__ void read_codes(const StageMx& cur, int rn0, int rm0, int h, v8i fw[4], v8i fx[4]) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int rn = rn0 + f * 32, rm = rm0 + f * 32;
@@ -157,212 +199,247 @@ __device__ __forceinline__ void read_frags(const StageMx& cur, int rn0, int rm0,
   }
 }
 
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding (and all of its LDS operations are done).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N < 64, "vmcnt field is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+__device__ __forceinline__ void read_stage(const StageMx& cur, int st, int nblk, int rn0, int rm0, int h, Frags& f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f.sw[q] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.bs[(rn0 + q * 32) * SCB + 2 * h]), st, nblk, h);
+    f.sx[q] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.as[(rm0 + q * 32) * SCB + 2 * h]), st, nblk, h);
+  }
+  read_codes<0>(cur, rn0, rm0, h, f.w0, f.x0);
+  read_codes<1>(cur, rn0, rm0, h, f.w1, f.x1);
 }
 
-// Consume stage `st` from `cur` while stage st + 3 streams into `refill`.
-template <bool SDW>
-__device__ __forceinline__ void stage_step(v16f acc[4][4], StageMx& cur, StageMx& refill, int st, const OperandMx& oa,
-                                           const OperandMx& ob, int kbytes, int rn0, int rm0, int h) {
-  constexpr int PER = SDW ? 10 : 16;     // vector-memory instructions per wave per stage
-  wait_vm_lgkm0<2 * PER>();              // this wave's share of stage st has landed
-  // ... everyone's has, and nobody still reads `refill`. A bare barrier: the
-  // release fence of __syncthreads() would also wait for the two younger
-  // stages still in flight.
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+__device__ __forceinline__ void mfma_stage(v16f acc[4][4], const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w0[i], f.x0[j], acc[i][j], 4, 4, 0, f.sw[i], 0,
+                                                                  f.sx[j]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w1[i], f.x1[j], acc[i][j], 4, 4, 1, f.sw[i], 1,
+                                                                  f.sx[j]);
+}
+
+// One pipeline step. On entry `cur` holds stage st's fragments (registers),
+// buffer `nxt` holds or is receiving the stream's next stage, and `own` --
+// the buffer stage st was read from -- is free once every wave is past this
+// step's barrier. The step: wait for the next stage, barrier, start the
+// stage four ahead of st into `own`, then run stage st's MFMAs while reading
+// the next stage's fragments into `next`.
+// (d4, st4): tile and stage of the stream element four ahead;
+// st1: within-tile index of the next stage.
+template <bool SDW, bool READ_NEXT = true>
+__device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frags& next, StageMx& own,
+                                          const StageMx& nxt, const Problem& p, const LaneOffsets& o, const TileDesc& d4,
+                                          int st4, int st1, int rn0, int rm0, int h) {
+  constexpr int PER = SDW ? 10 : 16;  // vector-memory instructions per wave per stage
+  wait_vm_lgkm0<2 * PER>();           // this wave's share of the next stage has landed
+  bare_barrier();                     // ... everyone's has; nobody still reads `own`
   uint32_t sc[8];
-  issue_stage<SDW>(refill, oa, ob, st + 3, kbytes, sc);
-  const int nblk = kbytes >> 4;
-  int sw[4], sx[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    sw[f] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.bs[(rn0 + f * 32) * SCB + 2 * h]), st, nblk, h);
-    sx[f] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.as[(rm0 + f * 32) * SCB + 2 * h]), st, nblk, h);
+  issue_stage<SDW>(own, p, o, d4, st4, sc);
+  if (READ_NEXT) read_stage(nxt, st1, p.nblk, rn0, rm0, h, next);
+  mfma_stage(acc, cur);
+  // schedule: MFMAs back to back, with the next stage's fragment reads and
+  // the loads four stages ahead slotted between them
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+  for (int q = 0; q < 10; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
   }
-  v8i f0w[4], f0x[4], f1w[4], f1x[4];
-  read_frags<0>(cur, rn0, rm0, h, f0w, f0x);
-  read_frags<1>(cur, rn0, rm0, h, f1w, f1x);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_ks<0>(f0w[i], f0x[j], acc[i][j], sw[i], sx[j]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_ks<1>(f1w[i], f1x[j], acc[i][j], sw[i], sx[j]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 11, 0);
+  __builtin_amdgcn_sched_barrier(0);
   if (!SDW) {
     // the scale bytes were issued before this stage's code loads: once only
     // those 8 remain, the bytes are in registers
     asm volatile("" ::: "memory");
     wait_vm_lgkm0<8>();
-    store_scale_regs(refill, sc);
+    store_scale_regs(own, sc);
   }
 }
 
-// Main kernel. MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands --
-// lane l supplies row l % 32 and the 32 K-elements of K-block l / 32 of a
-// 64-element K step, plus that block's scale byte; the accumulator holds
-// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15. Weight rows feed the
-// MFMA's first operand, so D's row index is n and its column index m.
-// K order within a 128-element stage: K step ks (0, 1) gives lane half h
-// K-block 2h + ks, so a lane's code bytes are 32 contiguous bytes and its two
-// scale bytes one 16-bit word (the MFMA's op_sel picks byte ks).
-template <int BF16OUT, int RESID, bool SDW>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
-    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ as, int64_t ld_as,
-    const uint8_t* __restrict__ b, int64_t ldb, const uint8_t* __restrict__ bs, int64_t ld_bs, int M, int N,
-    int K, void* __restrict__ c, int64_t ldc, const float* residual, int tiles_m, int tiles_n) {
-  __shared__ StageMx s0, s1, s2, s3;
+// Epilogue of one tile straight from the accumulators. For MFMA tile (i, j)
+// a lane holds m = 32 j + l % 32 and n = 32 i + 8 q + 4 h + s (q, s = 0..3).
+// Swapping the q = 0/1 values of the upper lane half with the q = 2/3 values
+// of the lower half (v_permlane32_swap) leaves lane half h with the 16
+// consecutive n 32 i + 16 h .. +15, in register order q = 0, 2, 1, 3.
+__device__ __forceinline__ void gather16(v16f v, float o[16]) {
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[4 * qq + s]),
+                                                      __float_as_uint(v[4 * (qq + 2) + s]), false, false);
+      v[4 * qq + s] = __uint_as_float(r[0]);
+      v[4 * (qq + 2) + s] = __uint_as_float(r[1]);
+    }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o[s] = v[s];            // q = 0 slot
+    o[4 + s] = v[8 + s];    // q = 2 slot
+    o[8 + s] = v[4 + s];    // q = 1 slot
+    o[12 + s] = v[12 + s];  // q = 3 slot
+  }
+}
 
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+// 16-byte vector stores (element-wise at the N edge). They are issued after
+// the next tile's first stages, so the caller drains them before the
+// pipeline counts its loads again.
+template <int BF16OUT, int RESID>
+__device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
+                                           int64_t ldc, const float* residual) {
+  const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float o[16];
+      gather16(acc[i][j], o);
+      const int m = m_base + 32 * j + r32;
+      const int n = n_base + 32 * i + 16 * h;
+      if (m >= p.M || n >= p.N) continue;
+      const int64_t off = (int64_t)m * ldc + n;
+      if (n + 16 <= p.N) {
+        if (RESID) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 r4 = *reinterpret_cast<const float4*>(residual + off + 4 * g4);
+            o[4 * g4] += r4.x; o[4 * g4 + 1] += r4.y; o[4 * g4 + 2] += r4.z; o[4 * g4 + 3] += r4.w;
+          }
+        }
+        if (BF16OUT) {
+          uint32_t wv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            wv[e] = (uint32_t)f32_to_bf16(o[2 * e]) | ((uint32_t)f32_to_bf16(o[2 * e + 1]) << 16);
+          if ((ldc & 7) == 0) {  // 16-byte aligned rows
+            uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + off);
+            dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+          } else {               // rows only 8-byte aligned
+            uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = make_uint2(wv[2 * e], wv[2 * e + 1]);
+          }
+        } else {
+          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + off);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) dst[g4] = make_float4(o[4 * g4], o[4 * g4 + 1], o[4 * g4 + 2], o[4 * g4 + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (n + e >= p.N) continue;
+          float x = o[e];
+          if (RESID) x += residual[off + e];
+          if (BF16OUT)
+            reinterpret_cast<uint16_t*>(c)[off + e] = f32_to_bf16(x);
+          else
+            reinterpret_cast<float*>(c)[off + e] = x;
+        }
+      }
+    }
+  }
+}
+
+template <int BF16OUT, int RESID, bool SDW>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* __restrict__ c, int64_t ldc,
+                                                              const float* residual, int nst4) {
+  __shared__ StageMx s0, s1, s2, s3;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
   const int r32 = lane & 31, h = lane >> 5;
   const int rn0 = wn * 128 + r32, rm0 = wm * 128 + r32;
+  const int G = gridDim.x, g = blockIdx.x;
+  if (g >= p.total) return;
 
-  const int kbytes = K >> 1;
-  const int nstages = (kbytes + KSTAGE_B - 1) / KSTAGE_B;
+  LaneOffsets o;
+  make_lane_offsets(o, p);
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-  OperandMx oa, ob;
-  make_operand_mx<SDW>(oa, a, lda, as, ld_as, m0, M);
-  make_operand_mx<SDW>(ob, b, ldb, bs, ld_bs, n0, N);
-
-  // prologue: stages 0..2 in flight (stages past the end read zeros). The
-  // stage waits count this wave's loads in issue order, so no load may be
-  // moved across a stage boundary.
+  // Prologue: the stream's first four stages (tile g, stages 0..3; nst4 >= 4).
+  // The stage waits count this wave's loads in issue order, so no load may
+  // move across a stage boundary.
+  TileDesc dcur = make_desc(p, g);
   {
     uint32_t sc[8];
-    issue_stage<SDW>(s0, oa, ob, 0, kbytes, sc);
+    issue_stage<SDW>(s0, p, o, dcur, 0, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s0, sc); }
-    issue_stage<SDW>(s1, oa, ob, 1, kbytes, sc);
+    issue_stage<SDW>(s1, p, o, dcur, 1, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s1, sc); }
-    issue_stage<SDW>(s2, oa, ob, 2, kbytes, sc);
+    issue_stage<SDW>(s2, p, o, dcur, 2, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s2, sc); }
+    issue_stage<SDW>(s3, p, o, dcur, 3, sc);
+    asm volatile("" ::: "memory");
+    if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s3, sc); }
   }
-  // The stage count is rounded up to a multiple of 4 (the ring size); the
-  // extra stages hold only zero codes and add nothing. One exit keeps the
-  // accumulators in place.
-  for (int st = 0; st < nstages; st += NBUF) {
-    stage_step<SDW>(acc, s0, s3, st, oa, ob, kbytes, rn0, rm0, h);
-    stage_step<SDW>(acc, s1, s0, st + 1, oa, ob, kbytes, rn0, rm0, h);
-    stage_step<SDW>(acc, s2, s1, st + 2, oa, ob, kbytes, rn0, rm0, h);
-    stage_step<SDW>(acc, s3, s2, st + 3, oa, ob, kbytes, rn0, rm0, h);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing (past-the-end) loads before LDS is reused
-  __syncthreads();
+  constexpr int PER = SDW ? 10 : 16;
+  wait_vm_lgkm0<3 * PER>();  // stage 0 has landed (this wave's share) ...
+  bare_barrier();            // ... and everyone's
+  Frags fa, fb;
+  read_stage(s0, 0, p.nblk, rn0, rm0, h, fa);
 
-  // Epilogue: stage the wave's 128 x 128 tile through LDS so global stores
-  // are 16-byte vectors covering whole 256/512-byte row segments.
-  int me = m0 + wm * 128, ne = n0 + wn * 128;
-  float one = 1.0f;  // opaque to the compiler: keeps epilogue work out of the main loop
-  asm volatile("" : "+v"(me), "+v"(ne), "+v"(one));
-  uint8_t* stage = (wave == 0 ? s0.a : wave == 1 ? s1.a : wave == 2 ? s2.a : s3.a);
-  constexpr int ESZ = BF16OUT ? 2 : 4;
-  constexpr int ROWS_PER_PASS = BF16OUT ? 64 : 32;
-  constexpr int ROWBYTES = 128 * ESZ;
-  constexpr int PITCH = ROWBYTES + 16;
-  static_assert(ROWS_PER_PASS * PITCH <= (int)sizeof(StageMx), "epilogue pass must fit in one stage buffer");
+  for (int pid = g; pid < p.total; pid += G) {
+    int tm, tn;
+    tile_coords(pid, p.tiles_m, p.tiles_n, tm, tn);
+    const TileDesc dnext = make_desc(p, pid + G);
+    v16f acc[4][4];
 #pragma unroll
-  for (int pass = 0; pass < 128 / ROWS_PER_PASS; ++pass) {
-    // accumulators -> LDS: m-row = 32 j + r32 (within the pass), n = 32 i + 8 q + 4 h + 0..3
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 32 * j + r32 - pass * ROWS_PER_PASS;
-      if (32 * j < pass * ROWS_PER_PASS || 32 * j >= (pass + 1) * ROWS_PER_PASS) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = 32 * i + 8 * q + 4 * h;
-          const float v0 = acc[i][j][4 * q] * one, v1 = acc[i][j][4 * q + 1] * one;
-          const float v2 = acc[i][j][4 * q + 2] * one, v3 = acc[i][j][4 * q + 3] * one;
-          uint8_t* dst = stage + row * PITCH + n * ESZ;
-          if (BF16OUT) {
-            *reinterpret_cast<uint2*>(dst) =
-                make_uint2((uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
-                           (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16));
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-          }
-        }
+      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    // The per-tile stage count nst4 is a multiple of 4 (the ring size); the
+    // stages past K hold only zero codes and add nothing. In the last group
+    // the stages four ahead belong to the next tile.
+    for (int st = 0; st < nst4; st += NBUF) {
+      const bool last = st + NBUF == nst4;
+      const TileDesc& d4 = last ? dnext : dcur;
+      const int b4 = last ? 0 : st + NBUF;
+      pipe_step<SDW>(acc, fa, fb, s0, s1, p, o, d4, b4, st + 1, rn0, rm0, h);
+      pipe_step<SDW>(acc, fb, fa, s1, s2, p, o, d4, b4 + 1, st + 2, rn0, rm0, h);
+      pipe_step<SDW>(acc, fa, fb, s2, s3, p, o, d4, b4 + 2, st + 3, rn0, rm0, h);
+      pipe_step<SDW>(acc, fb, fa, s3, s0, p, o, d4, b4 + 3, last ? 0 : st + 4, rn0, rm0, h);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // LDS -> global: each lane moves 16 bytes; a wave instruction covers whole rows
-    constexpr int CH_PER_ROW = ROWBYTES / 16;
-    constexpr int ITERS = ROWS_PER_PASS * CH_PER_ROW / 64;
-#pragma unroll 4
-    for (int t = 0; t < ITERS; ++t) {
-      const int id = t * 64 + lane;
-      const int row = id / CH_PER_ROW, ch = id % CH_PER_ROW;
-      const int m = me + pass * ROWS_PER_PASS + row;
-      const int n = ne + ch * (16 / ESZ);
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * PITCH + ch * 16);
-      if (m >= M || n >= N) continue;
-      const int64_t off = (int64_t)m * ldc + n;
-      if (n + 16 / ESZ <= N) {
-        if (BF16OUT) {
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + off) = v;
-        } else {
-          float4 o = __builtin_bit_cast(float4, v);
-          if (RESID) {
-            const float4 r = *reinterpret_cast<const float4*>(residual + off);
-            o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
-          }
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + off) = o;
-        }
-      } else {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        for (int e = 0; e < 16 / ESZ && n + e < N; ++e) {
-          if (BF16OUT) {
-            reinterpret_cast<uint16_t*>(c)[off + e] = (uint16_t)(wv[e / 2] >> (16 * (e & 1)));
-          } else {
-            float o = __uint_as_float(wv[e]);
-            if (RESID) o += residual[off + e];
-            reinterpret_cast<float*>(c)[off + e] = o;
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
+    dcur = dnext;
+    int mb = tm * BM + wm * 128, nb = tn * BN + wn * 128;
+    asm volatile("" : "+v"(mb), "+v"(nb));  // keep epilogue address math out of the main loop
+    store_tile<BF16OUT, RESID>(acc, mb, nb, p, c, ldc, residual);
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are not counted by the stage waits: drain them here
   }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing (past-the-end) loads before the workgroup exits
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
 }
 
 template <int BF16OUT, int RESID>
-hipError_t launch(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const uint8_t* b, int64_t ldb,
-                  const uint8_t* bs, int64_t ld_bs, int64_t m, int64_t n, int64_t k, void* c, int64_t ldc,
-                  const float* residual, hipStream_t st) {
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  const unsigned grid = (unsigned)(tiles_m * tiles_n);
-  // scales as whole 4-byte words when every row's scale bytes start 4-byte aligned
-  const bool sdw = (ld_as % 4 == 0) && (ld_bs % 4 == 0) &&
-                   (reinterpret_cast<uintptr_t>(as) % 4 == 0) && (reinterpret_cast<uintptr_t>(bs) % 4 == 0);
+hipError_t launch(const Problem& p, void* c, int64_t ldc, const float* residual, hipStream_t st, bool sdw) {
+  const int nstages = (p.kbytes + KSTAGE_B - 1) / KSTAGE_B;
+  const int nst4 = (nstages + NBUF - 1) / NBUF * NBUF;
+  const unsigned grid = (unsigned)min(p.total, cu_count());
   if (sdw)
-    gemm_mx_kernel<BF16OUT, RESID, true><<<grid, kThreads, 0, st>>>(a, lda, as, ld_as, b, ldb, bs, ld_bs, (int)m,
-                                                                    (int)n, (int)k, c, ldc, residual, tiles_m, tiles_n);
+    gemm_mx_kernel<BF16OUT, RESID, true><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   else
-    gemm_mx_kernel<BF16OUT, RESID, false><<<grid, kThreads, 0, st>>>(a, lda, as, ld_as, b, ldb, bs, ld_bs, (int)m,
-                                                                     (int)n, (int)k, c, ldc, residual, tiles_m, tiles_n);
+    gemm_mx_kernel<BF16OUT, RESID, false><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   return hipGetLastError();
 }
 
@@ -371,9 +448,18 @@ hipError_t launch(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_a
 hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const uint8_t* b,
                           int64_t ldb, const uint8_t* bs, int64_t ld_bs, int64_t m, int64_t n, int64_t k, void* c,
                           int c_bf16, int64_t ldc, const float* residual, hipStream_t st) {
-  if (c_bf16) return launch<1, 0>(a, lda, as, ld_as, b, ldb, bs, ld_bs, m, n, k, c, ldc, nullptr, st);
-  if (residual) return launch<0, 1>(a, lda, as, ld_as, b, ldb, bs, ld_bs, m, n, k, c, ldc, residual, st);
-  return launch<0, 0>(a, lda, as, ld_as, b, ldb, bs, ld_bs, m, n, k, c, ldc, nullptr, st);
+  Problem p;
+  p.a = a; p.as = as; p.b = b; p.bs = bs;
+  p.lda = lda; p.ld_as = ld_as; p.ldb = ldb; p.ld_bs = ld_bs;
+  p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
+  p.tiles_m = (int)((m + BM - 1) / BM); p.tiles_n = (int)((n + BN - 1) / BN);
+  p.total = p.tiles_m * p.tiles_n;
+  // scales as whole 4-byte words when every row's scale bytes start 4-byte aligned
+  const bool sdw = (ld_as % 4 == 0) && (ld_bs % 4 == 0) && (reinterpret_cast<uintptr_t>(as) % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(bs) % 4 == 0);
+  if (c_bf16) return launch<1, 0>(p, c, ldc, nullptr, st, sdw);
+  if (residual) return launch<0, 1>(p, c, ldc, residual, st, sdw);
+  return launch<0, 0>(p, c, ldc, nullptr, st, sdw);
 }
 
 }  // namespace fp4r

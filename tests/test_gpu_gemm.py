@@ -69,6 +69,48 @@ def test_exact_integer_case_bit_exact(gpu_lib):
         np.testing.assert_array_equal(c.astype(np.float64), c_exact)
 
 
+@pytest.mark.parametrize("k", [5600, 2240, 96])
+def test_unaligned_scale_rows(gpu_lib, k):
+    """Scale rows of K/32 bytes with no padding (an odd stride for K = 5600):
+    the GEMM's byte-wise scale path."""
+    rng = np.random.default_rng(k)
+    m, n = 300, 272
+    ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(120, 134, size=(m, k // 32), dtype=np.uint8)
+    bs = rng.integers(120, 134, size=(n, k // 32), dtype=np.uint8)
+    from fp4_quantized_diffusion_amd.binding import QTensor, FMT_MX
+    lda = ((k // 2 + 15) // 16) * 16
+    acd = torch.zeros((m, lda), dtype=torch.uint8, device=DEV); acd[:, : k // 2] = dev(ac)
+    bcd = torch.zeros((n, lda), dtype=torch.uint8, device=DEV); bcd[:, : k // 2] = dev(bc)
+    qa = QTensor(acd, dev(as_), None, FMT_MX, k)
+    qb = QTensor(bcd, dev(bs), None, FMT_MX, k)
+    for out in ("f32", "bf16"):
+        c = to_np(gpu_lib.gemm(qa, qb, out).float())
+        c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+        ok, worst = gemm_within_tol(c, c_exact, s_abs, bf16_out=(out == "bf16"))
+        assert ok, (out, worst)
+
+
+def test_padded_scale_rows_with_garbage(gpu_lib):
+    """Scale rows padded past K/32 with 0xFF (an E8M0 NaN): the padding must
+    never reach the MFMA (K = 2240 ends mid-word)."""
+    rng = np.random.default_rng(35)
+    m, n, k = 260, 256, 2240
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    b = rng.standard_normal((n, k)).astype(np.float32)
+    qa, qb = quantize_both(gpu_lib, a, b, "mx")
+    from fp4_quantized_diffusion_amd.binding import QTensor
+    def pad(q):
+        s = torch.full((q.scales.shape[0], 72), 0xFF, dtype=torch.uint8, device=DEV)
+        s[:, :70] = q.scales
+        return QTensor(q.codes, s[:, :70], None, q.fmt, q.k)
+    c = to_np(gpu_lib.gemm(pad(qa), pad(qb), "f32"))
+    c_exact, s_abs = oracle_c(qa, qb, "mx")
+    ok, worst = gemm_within_tol(c, c_exact, s_abs)
+    assert ok, worst
+
+
 def test_varied_scales_exact_rational_small(gpu_lib):
     """Random codes and random E8M0 scales (not from a quantizer) -- exercises
     the per-lane scale selection of every K-block."""
