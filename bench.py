@@ -28,6 +28,23 @@ METRIC = "FP4 GEMM TFLOP/s (% of MI355X MXFP4 peak); FP4 rollout candidates/sec"
 PEAK_FP4 = 10.1e15      # MI355X dense MXFP4 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 
+# HBM bytes per GEMM launch from rocprofv3 FETCH_SIZE (x2, copy-calibrated)
+# and WRITE_SIZE (x1) runs of this workload, averaged over the two rollout
+# GEMMs; valid only for the kernel sources they were taken with (reported as
+# null once those change). See profiles/rollout_96x4096x3072_kernels.md.
+GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "9a0795501596d6af", "gemm_common.h": "d8952e405ad1a5b1"},
+                "bytes_per_launch": 26.1e9}
+
+
+def gemm_traffic():
+    import hashlib
+    csrc = os.path.join(ROOT, "fp4_quantized_diffusion_amd", "csrc")
+    for name, digest in GEMM_TRAFFIC["sources"].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    return GEMM_TRAFFIC["bytes_per_launch"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -230,7 +247,9 @@ def main():
                    "blocks": cfg["blocks"], "euler_steps": cfg["steps"], "chunk_candidates": chunk,
                    "gemm_shapes": [[m_rows, cfg["dim"], cfg["hidden"]], [m_rows, cfg["hidden"], cfg["dim"]]]},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_FP4 / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4),
+                     "traffic": (None if gemm_traffic() is None else round(gemm_traffic() / 1e9, 2)),
+                     "traffic_unit": "GB per launch (HBM reads + writes, rocprofv3 counters)",
                      "kernel": "gemm_mx (MXFP4 x MXFP4, fp32 accumulate)",
                      "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "gemm_tflops": round(achieved / 1e12, 2),
