@@ -232,12 +232,19 @@ __device__ __forceinline__ void mfma_stage(v16f acc[4][4], const Frags& f) {
 // the next stage's fragments into `next`.
 // (d4, st4): tile and stage of the stream element four ahead;
 // st1: within-tile index of the next stage.
-template <bool SDW, bool READ_NEXT = true>
+// after_epi: the previous tile's epilogue issued exactly EPI vector-memory
+// instructions after the stages now in flight (they count in vmcnt too).
+template <bool SDW, int EPI = 0, bool READ_NEXT = true>
 __device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frags& next, StageMx& own,
                                           const StageMx& nxt, const Problem& p, const LaneOffsets& o, const TileDesc& d4,
-                                          int st4, int st1, int rn0, int rm0, int h) {
+                                          int st4, int st1, int rn0, int rm0, int h, bool after_epi = false) {
   constexpr int PER = SDW ? 10 : 16;  // vector-memory instructions per wave per stage
-  wait_vm_lgkm0<2 * PER>();           // this wave's share of the next stage has landed
+  constexpr int ALLOW_EPI = 2 * PER + EPI < 63 ? 2 * PER + EPI : 63;
+  // this wave's share of the next stage has landed
+  if (EPI > 0 && after_epi)
+    wait_vm_lgkm0<ALLOW_EPI>();
+  else
+    wait_vm_lgkm0<2 * PER>();
   bare_barrier();                     // ... everyone's has; nobody still reads `own`
   uint32_t sc[8];
   issue_stage<SDW>(own, p, o, d4, st4, sc);
@@ -288,10 +295,18 @@ __device__ __forceinline__ void gather16(v16f v, float o[16]) {
   }
 }
 
-// 16-byte vector stores (element-wise at the N edge). They are issued after
-// the next tile's first stages, so the caller drains them before the
-// pipeline counts its loads again.
+// Vector-memory instructions store_tile<FULL = true> issues per wave: per
+// MFMA tile two 16-byte stores (bf16) or four (fp32), plus four residual loads.
 template <int BF16OUT, int RESID>
+constexpr int full_tile_vmem() { return 16 * (BF16OUT ? 2 : (RESID ? 8 : 4)); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// FULL: the tile lies wholly inside C and rows are 16-byte aligned, so every
+// wave issues exactly full_tile_vmem() instructions and the pipeline can
+// count them instead of draining them. Otherwise element-wise tails at the
+// N edge and the caller drains the stores.
+template <int BF16OUT, int RESID, bool FULL>
 __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
                                            int64_t ldc, const float* residual) {
   const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
@@ -303,9 +318,9 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
       gather16(acc[i][j], o);
       const int m = m_base + 32 * j + r32;
       const int n = n_base + 32 * i + 16 * h;
-      if (m >= p.M || n >= p.N) continue;
+      if (!FULL && (m >= p.M || n >= p.N)) continue;
       const int64_t off = (int64_t)m * ldc + n;
-      if (n + 16 <= p.N) {
+      if (FULL || n + 16 <= p.N) {
         if (RESID) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
@@ -316,13 +331,13 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
         if (BF16OUT) {
           uint32_t wv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            wv[e] = (uint32_t)f32_to_bf16(o[2 * e]) | ((uint32_t)f32_to_bf16(o[2 * e + 1]) << 16);
-          if ((ldc & 7) == 0) {  // 16-byte aligned rows
+          for (int e = 0; e < 8; ++e)  // hardware round-to-nearest-even conversion
+            wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
+          if (FULL || (ldc & 7) == 0) {  // 16-byte aligned rows
             uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + off);
             dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-          } else {               // rows only 8-byte aligned
+          } else {                        // rows only 8-byte aligned
             uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + off);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[e] = make_uint2(wv[2 * e], wv[2 * e + 1]);
@@ -339,7 +354,7 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
           float x = o[e];
           if (RESID) x += residual[off + e];
           if (BF16OUT)
-            reinterpret_cast<uint16_t*>(c)[off + e] = f32_to_bf16(x);
+            reinterpret_cast<__bf16*>(c)[off + e] = (__bf16)x;
           else
             reinterpret_cast<float*>(c)[off + e] = x;
         }
@@ -351,6 +366,8 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
 template <int BF16OUT, int RESID, bool SDW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* __restrict__ c, int64_t ldc,
                                                               const float* residual, int nst4) {
+  constexpr int EPI = full_tile_vmem<BF16OUT, RESID>();
+  const bool rows16 = BF16OUT ? (ldc % 8 == 0) : true;  // 16-byte aligned output rows
   __shared__ StageMx s0, s1, s2, s3;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -388,6 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
   Frags fa, fb;
   read_stage(s0, 0, p.nblk, rn0, rm0, h, fa);
 
+  bool counted = false;  // the previous tile's stores are counted, not drained
   for (int pid = g; pid < p.total; pid += G) {
     int tm, tn;
     tile_coords(pid, p.tiles_m, p.tiles_n, tm, tn);
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
       const bool last = st + NBUF == nst4;
       const TileDesc& d4 = last ? dnext : dcur;
       const int b4 = last ? 0 : st + NBUF;
-      pipe_step<SDW>(acc, fa, fb, s0, s1, p, o, d4, b4, st + 1, rn0, rm0, h);
+      pipe_step<SDW, EPI>(acc, fa, fb, s0, s1, p, o, d4, b4, st + 1, rn0, rm0, h, counted && st == 0);
       pipe_step<SDW>(acc, fb, fa, s1, s2, p, o, d4, b4 + 1, st + 2, rn0, rm0, h);
       pipe_step<SDW>(acc, fa, fb, s2, s3, p, o, d4, b4 + 2, st + 3, rn0, rm0, h);
       pipe_step<SDW>(acc, fb, fa, s3, s0, p, o, d4, b4 + 3, last ? 0 : st + 4, rn0, rm0, h);
@@ -412,8 +430,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
     dcur = dnext;
     int mb = tm * BM + wm * 128, nb = tn * BN + wn * 128;
     asm volatile("" : "+v"(mb), "+v"(nb));  // keep epilogue address math out of the main loop
-    store_tile<BF16OUT, RESID>(acc, mb, nb, p, c, ldc, residual);
-    __builtin_amdgcn_s_waitcnt(0);  // the stores are not counted by the stage waits: drain them here
+    counted = rows16 && (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
+    if (counted) {
+      store_tile<BF16OUT, RESID, true>(acc, mb, nb, p, c, ldc, residual);
+    } else {
+      store_tile<BF16OUT, RESID, false>(acc, mb, nb, p, c, ldc, residual);
+      __builtin_amdgcn_s_waitcnt(0);  // an edge tile's stores are not counted: drain them here
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing (past-the-end) loads before the workgroup exits
 }
