@@ -172,14 +172,25 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// A barrier without the release fence of __syncthreads(), which would also
-// wait for the younger stages still in flight. The asm statements keep the
-// compiler from moving memory operations across it.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// "Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS operations are done, then barrier" as ONE asm
+// block, so the wait cannot be scheduled after the barrier: a wave must not
+// signal the barrier before its own loads into the stage the others are
+// about to read have landed. No release fence (unlike __syncthreads(), whose
+// fence would also wait for the younger stages still in flight); the memory
+// clobber keeps the compiler from moving memory operations across it.
+#define FP4R_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  if constexpr (N == 20) FP4R_WAIT_BARRIER(20);
+  else if constexpr (N == 30) FP4R_WAIT_BARRIER(30);
+  else if constexpr (N == 32) FP4R_WAIT_BARRIER(32);
+  else if constexpr (N == 48) FP4R_WAIT_BARRIER(48);
+  else if constexpr (N == 52) FP4R_WAIT_BARRIER(52);
+  else if constexpr (N == 63) FP4R_WAIT_BARRIER(63);
+  else static_assert(N < 0, "add this vmcnt value");
 }
+#undef FP4R_WAIT_BARRIER
 
 // All of one stage's fragments for this lane: scales and both K steps' codes.
 struct Frags {
@@ -240,12 +251,12 @@ __device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frag
                                           int st4, int st1, int rn0, int rm0, int h, bool after_epi = false) {
   constexpr int PER = SDW ? 10 : 16;  // vector-memory instructions per wave per stage
   constexpr int ALLOW_EPI = 2 * PER + EPI < 63 ? 2 * PER + EPI : 63;
-  // this wave's share of the next stage has landed
+  // this wave's share of the next stage has landed; after the barrier,
+  // everyone's has and nobody still reads `own`
   if (EPI > 0 && after_epi)
-    wait_vm_lgkm0<ALLOW_EPI>();
+    wait_barrier<ALLOW_EPI>();
   else
-    wait_vm_lgkm0<2 * PER>();
-  bare_barrier();                     // ... everyone's has; nobody still reads `own`
+    wait_barrier<2 * PER>();
   uint32_t sc[8];
   issue_stage<SDW>(own, p, o, d4, st4, sc);
   if (READ_NEXT) read_stage(nxt, st1, p.nblk, rn0, rm0, h, next);
@@ -400,8 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s3, sc); }
   }
   constexpr int PER = SDW ? 10 : 16;
-  wait_vm_lgkm0<3 * PER>();  // stage 0 has landed (this wave's share) ...
-  bare_barrier();            // ... and everyone's
+  wait_barrier<3 * PER>();  // stage 0 has landed (this wave's share, then everyone's)
   Frags fa, fb;
   read_stage(s0, 0, p.nblk, rn0, rm0, h, fa);
 
