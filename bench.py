@@ -172,6 +172,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-agreement", action="store_true")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
+    ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
@@ -196,7 +197,7 @@ def main():
     work = torch.empty_like(noise)
     timer = EventTimer()
     ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
-                    timer=timer)
+                    timer=timer, layout=args.layout)
 
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
@@ -245,12 +246,13 @@ def main():
                                f"x{cfg['blocks']}blk_{cfg['steps']}step_top{cfg['k_top']}_bottom{cfg['k_bottom']}",
                    "n_cand": cfg["n_cand"], "tokens": cfg["tokens"], "dim": cfg["dim"], "hidden": cfg["hidden"],
                    "blocks": cfg["blocks"], "euler_steps": cfg["steps"], "chunk_candidates": chunk,
+                   "operand_layout": args.layout,
                    "gemm_shapes": [[m_rows, cfg["dim"], cfg["hidden"]], [m_rows, cfg["hidden"], cfg["dim"]]]},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_FP4 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4),
                      "traffic": (None if gemm_traffic() is None else round(gemm_traffic() / 1e9, 2)),
                      "traffic_unit": "GB per launch (HBM reads + writes, rocprofv3 counters)",
-                     "kernel": "gemm_mx (MXFP4 x MXFP4, fp32 accumulate)",
+                     "kernel": f"gemm_mx_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate)",
                      "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "gemm_tflops": round(achieved / 1e12, 2),
         "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),

@@ -2,9 +2,10 @@
 
 Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
-  * the raw entry points under their C names (fp4_quantize, fp4_gemm,
-    euler_step, fp4_proxy_reward, select_topk_bottomk), taking integers and
-    device addresses and returning the status code;
+  * the raw entry points under their C names (fp4_quantize, fp4_panel_bytes,
+    fp4_gemm, fp4_gemm_panel, euler_step, fp4_proxy_reward,
+    select_topk_bottomk), taking integers and device addresses and returning
+    the status code;
   * torch-tensor helpers (quantize, gemm, euler, proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
@@ -20,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libfp4rollout.so")
 
 FMT_MX, FMT_NV = 0, 1
 DT_F32, DT_BF16 = 0, 1
-PRO_RMSNORM, PRO_GELU, TENSOR_SCALE_GIVEN = 0x1, 0x2, 0x100
+PRO_RMSNORM, PRO_GELU, TENSOR_SCALE_GIVEN, LAYOUT_PANEL = 0x1, 0x2, 0x100, 0x200
 OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR, INTERNAL = 0, 1, 2, 3, 4
 
 _LIB = None
@@ -28,7 +29,9 @@ _LIB = None
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 _SIGS = {
     "fp4_quantize": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
+    "fp4_panel_bytes": [_i64, _i64, _p, _p],
     "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
+    "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
     "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
     "select_topk_bottomk": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
@@ -77,6 +80,16 @@ def fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, l
                                    m, n, k, c, c_dtype, ldc, residual, stream)
 
 
+def fp4_panel_bytes(rows, k, code_bytes, scale_bytes):
+    """code_bytes / scale_bytes: addresses of host int64s (ctypes.byref)."""
+    return load_library().fp4_panel_bytes(rows, k, code_bytes, scale_bytes)
+
+
+def fp4_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype, ldc, residual, stream):
+    return load_library().fp4_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype, ldc,
+                                         residual, stream)
+
+
 def euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream):
     return load_library().euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream)
 
@@ -122,24 +135,40 @@ def _check(status, what):
 
 
 class QTensor(NamedTuple):
-    """A quantized [rows, k] matrix: packed codes [rows, >= k/2] (row stride a
-    multiple of 16 bytes), scale bytes [rows, k/block], and for the NV format
-    the fp32 tensor scale (a 1-element device tensor)."""
+    """A quantized [rows, k] matrix. Row layout: packed codes [rows, >= k/2]
+    (row stride a multiple of 16 bytes), scale bytes [rows, k/block], and for
+    the NV format the fp32 tensor scale (a 1-element device tensor). Panel
+    layout (MX): codes and scales are flat byte tensors in the panel order of
+    include/fp4rollout.h, and `rows` gives the row count."""
     codes: object
     scales: object
     tensor_scale: Optional[object]
     fmt: int
     k: int
+    layout: str = "row"
+    rows: int = 0
+
+    @property
+    def n_rows(self):
+        return self.rows if self.layout == "panel" else self.codes.shape[0]
 
 
 def _row_view_ok(x):
     return x.dim() == 2 and x.stride(1) == 1
 
 
-def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None):
+def panel_bytes(rows, k):
+    """(code bytes, scale bytes) of the panel layout of a [rows, k] operand."""
+    cb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(fp4_panel_bytes(rows, k, ctypes.addressof(cb), ctypes.addressof(sb)), "fp4_panel_bytes")
+    return cb.value, sb.value
+
+
+def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None, layout="row"):
     """x: 2-D CUDA tensor (fp32 or bf16, unit inner stride). prologue: None,
     "rmsnorm" or "gelu" (MX only). tensor_scale: a 1-element fp32 tensor whose
-    value is used as s_g (NV only). out: a QTensor to write into."""
+    value is used as s_g (NV only). layout: "row" or "panel" (MX only).
+    out: a QTensor to write into (its layout wins)."""
     torch = _torch()
     if not _row_view_ok(x):
         raise ValueError("x must be 2-D with unit inner stride")
@@ -147,6 +176,17 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None):
     rows, k = x.shape
     blk = 32 if f == FMT_MX else 16
     flags = {None: 0, "rmsnorm": PRO_RMSNORM, "gelu": PRO_GELU}[prologue]
+    if out is None and layout == "panel":
+        cb, sb = panel_bytes(rows, k)
+        out = QTensor(torch.empty(cb, dtype=torch.uint8, device=x.device),
+                      torch.empty(sb, dtype=torch.uint8, device=x.device), None, f, k, "panel", rows)
+    if out is not None and out.layout == "panel":
+        if out.rows != rows or out.k != k:
+            raise ValueError("out was allocated for another shape")
+        st = fp4_quantize(f, x.data_ptr(), _dtype_code(x), rows, k, x.stride(0), out.codes.data_ptr(), 0,
+                          out.scales.data_ptr(), 0, None, flags | LAYOUT_PANEL, _stream())
+        _check(st, "fp4_quantize")
+        return out
     if out is None:
         ldc = ((k // 2 + 15) // 16) * 16
         codes = torch.empty((rows, ldc), dtype=torch.uint8, device=x.device)
@@ -169,15 +209,21 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None):
 
 
 def gemm(a, b, out_dtype="bf16", residual=None, out=None):
-    """C = A_hat B_hat^T (+ residual) for QTensors a [m, k] and b [n, k]."""
+    """C = A_hat B_hat^T (+ residual) for QTensors a [m, k] and b [n, k] of
+    one format and one layout."""
     torch = _torch()
-    if a.fmt != b.fmt or a.k != b.k:
-        raise ValueError("operands differ in format or k")
-    m, n, k = a.codes.shape[0], b.codes.shape[0], a.k
+    if a.fmt != b.fmt or a.k != b.k or a.layout != b.layout:
+        raise ValueError("operands differ in format, layout or k")
+    m, n, k = a.n_rows, b.n_rows, a.k
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     if out is None:
         ldc = ((n + 3) // 4) * 4
         out = torch.empty((m, ldc), dtype=dt, device=a.codes.device)[:, :n]
+    if a.layout == "panel":
+        st = fp4_gemm_panel(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                            m, n, k, out.data_ptr(), _dtype_code(out), out.stride(0), _ptr(residual), _stream())
+        _check(st, "fp4_gemm_panel")
+        return out
     st = fp4_gemm(a.fmt, a.codes.data_ptr(), a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(0),
                   _ptr(a.tensor_scale), b.codes.data_ptr(), b.codes.stride(0), b.scales.data_ptr(),
                   b.scales.stride(0), _ptr(b.tensor_scale), m, n, k, out.data_ptr(), _dtype_code(out),

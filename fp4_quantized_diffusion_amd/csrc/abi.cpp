@@ -32,11 +32,16 @@ fp4_status check_quantize(int fmt, const void* x, int x_dtype, int64_t rows, int
     return FP4_INVALID_ARGUMENT;
   const int64_t esize = x_dtype == FP4_DT_F32 ? 4 : 2;
   if (ldx < k || (ldx * esize) % 16 != 0 || !aligned(x, 16)) return FP4_INVALID_ARGUMENT;
-  if (ld_codes < k / 2 || ld_codes % 4 != 0 || !aligned(codes, 4)) return FP4_INVALID_ARGUMENT;
-  if (ld_scales < k / blk) return FP4_INVALID_ARGUMENT;
+  if (flags & FP4_LAYOUT_PANEL) {
+    if (fmt != FP4_FMT_MX) return FP4_UNSUPPORTED;
+    if (ld_codes != 0 || ld_scales != 0 || !aligned(codes, 16) || !aligned(scales, 4)) return FP4_INVALID_ARGUMENT;
+  } else {
+    if (ld_codes < k / 2 || ld_codes % 4 != 0 || !aligned(codes, 4)) return FP4_INVALID_ARGUMENT;
+    if (ld_scales < k / blk) return FP4_INVALID_ARGUMENT;
+  }
   if (fmt == FP4_FMT_MX) {
     if (tensor_scale) return FP4_INVALID_ARGUMENT;
-    if (flags & ~(FP4_PRO_RMSNORM | FP4_PRO_GELU)) return FP4_INVALID_ARGUMENT;
+    if (flags & ~(FP4_PRO_RMSNORM | FP4_PRO_GELU | FP4_LAYOUT_PANEL)) return FP4_INVALID_ARGUMENT;
     if ((flags & FP4_PRO_RMSNORM) && (flags & FP4_PRO_GELU)) return FP4_INVALID_ARGUMENT;
   } else {
     if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_INVALID_ARGUMENT;
@@ -73,6 +78,32 @@ fp4_status check_gemm(int fmt, const uint8_t* a, int64_t lda, const uint8_t* as,
   return FP4_OK;
 }
 
+fp4_status check_output(int64_t m, int64_t n, const void* c, int c_dtype, int64_t ldc, const float* residual) {
+  if (!c) return FP4_INVALID_ARGUMENT;
+  if (c_dtype != FP4_DT_F32 && c_dtype != FP4_DT_BF16) return FP4_INVALID_ARGUMENT;
+  if (ldc < n || ldc % 4 != 0 || ldc >= kMaxDim) return FP4_INVALID_ARGUMENT;
+  if (!aligned(c, c_dtype == FP4_DT_F32 ? 16 : 8)) return FP4_INVALID_ARGUMENT;
+  if (residual && (c_dtype != FP4_DT_F32 || !aligned(residual, 16))) return FP4_INVALID_ARGUMENT;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (tiles >= kMaxDim) return FP4_INVALID_ARGUMENT;
+  return FP4_OK;
+}
+
+fp4_status check_gemm_panel(int fmt, const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                            int64_t m, int64_t n, int64_t k, const void* c, int c_dtype, int64_t ldc,
+                            const float* residual) {
+  if (fmt != FP4_FMT_MX && fmt != FP4_FMT_NV) return FP4_INVALID_ARGUMENT;
+  if (!a || !as || !b || !bs) return FP4_INVALID_ARGUMENT;
+  if (m < 1 || n < 1 || k < 32 || k % 32 != 0) return FP4_INVALID_ARGUMENT;
+  // a panel's code bytes (k / 128 blocks of 16 KiB) stay below 2^31
+  if (m >= kMaxDim - 256 || n >= kMaxDim - 256 || k > ((int64_t)1 << 23)) return FP4_INVALID_ARGUMENT;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(as, 4) || !aligned(bs, 4)) return FP4_INVALID_ARGUMENT;
+  const fp4_status s = check_output(m, n, c, c_dtype, ldc, residual);
+  if (s != FP4_OK) return s;
+  if (fmt == FP4_FMT_NV) return FP4_UNSUPPORTED;
+  return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +119,8 @@ FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t row
     const int bf16 = x_dtype == FP4_DT_BF16;
     if (fmt == FP4_FMT_MX) {
       const int pro = (flags & FP4_PRO_RMSNORM) ? 1 : ((flags & FP4_PRO_GELU) ? 2 : 0);
+      if (flags & FP4_LAYOUT_PANEL)
+        return from_hip(fp4r::launch_quant_mx_panel(x, bf16, rows, k, ldx, codes, scales, pro, st));
       return from_hip(fp4r::launch_quant_mx(x, bf16, rows, k, ldx, codes, ld_codes, scales, ld_scales, pro, st));
     }
     return from_hip(fp4r::launch_quant_nv(x, bf16, rows, k, ldx, codes, ld_codes, scales, ld_scales, tensor_scale,
@@ -112,6 +145,28 @@ FP4_API fp4_status fp4_gemm(int fmt, const uint8_t* a_codes, int64_t lda, const 
                                            bf16, ldc, residual, st));
     return from_hip(fp4r::launch_gemm_nv(a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts, m,
                                          n, k, c, bf16, ldc, residual, st));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API fp4_status fp4_panel_bytes(int64_t rows, int64_t k, int64_t* code_bytes, int64_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes || rows < 1 || k < 32 || k % 32 != 0) return FP4_INVALID_ARGUMENT;
+  if (rows >= kMaxDim || k >= kMaxDim) return FP4_INVALID_ARGUMENT;
+  const int64_t blocks = ((rows + 255) / 256) * ((k + 127) / 128);
+  *code_bytes = blocks * 16384;
+  *scale_bytes = blocks * 1024;
+  return FP4_OK;
+}
+
+FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                                  const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, void* c, int c_dtype,
+                                  int64_t ldc, const float* residual, void* stream) {
+  try {
+    const fp4_status s = check_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype, ldc, residual);
+    if (s != FP4_OK) return s;
+    return from_hip(fp4r::launch_gemm_mx_panel(a_codes, a_scales, b_codes, b_scales, m, n, k, c,
+                                               c_dtype == FP4_DT_BF16, ldc, residual, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP4_INTERNAL;
   }
@@ -171,6 +226,6 @@ FP4_API const char* fp4_status_str(fp4_status s) {
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 100; }
+FP4_API int fp4_abi_version(void) { return 101; }
 
 }  // extern "C"

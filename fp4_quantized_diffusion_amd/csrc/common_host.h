@@ -11,6 +11,8 @@ namespace fp4r {
 hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            int prologue, hipStream_t st);
+hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx, uint8_t* codes,
+                                 uint8_t* scales, int prologue, hipStream_t st);
 hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            float* tensor_scale, int scale_given, hipStream_t st);
@@ -18,6 +20,9 @@ hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int6
                           const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs,
                           int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,
                           const float* residual, hipStream_t st);
+hipError_t launch_gemm_mx_panel(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,
+                                const float* residual, hipStream_t st);
 hipError_t launch_gemm_nv(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
                           const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,

@@ -30,6 +30,13 @@
 //    stage's fragments are read from LDS.
 //  * Epilogue straight from registers: one lane-half swap (v_permlane32_swap)
 //    gives every lane 16 consecutive n of its m row, stored as 16-byte vectors.
+//  * Operand layouts: row-major (any leading dimension) or the panel layout,
+//    where each 256-row x 128-element (panel, K chunk) pair is one contiguous
+//    16 KiB block of codes and a 1 KiB block of scales. Every stage load of
+//    the panel layout is a contiguous 1 KiB run per instruction; row-major
+//    rows give 64-byte pieces of 16 rows (codes) and single bytes or words of
+//    64 rows (scales), which costs the CU's load path about 2.5x the cycles
+//    per stage.
 //  * Tile order: workgroups are dispatched round-robin over the 8 XCDs; the
 //    tile map gives each XCD a contiguous band of tiles, walked in groups of
 //    kGroupM tile-rows, so tiles that run together on an XCD share A and B
@@ -61,13 +68,24 @@ struct __attribute__((aligned(16))) StageMx {
 // all 64 LDS banks, without conflicts.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
+// Operand layout (kernel template parameter).
+enum Layout {
+  LD_ROW_BYTE = 0,  // row-major, scale rows of any alignment (bytes through registers)
+  LD_ROW_WORD = 1,  // row-major, scale rows 4-byte aligned (direct word loads)
+  LD_PANEL = 2,     // panel layout
+};
+
 // Problem description shared by every step.
 struct Problem {
   const uint8_t *a, *as, *b, *bs;
-  int64_t lda, ld_as, ldb, ld_bs;
+  int64_t lda, ld_as, ldb, ld_bs;  // row-major layouts
   int M, N, kbytes, nblk;
+  int nkc;                         // K chunks of 128 elements (stages per tile)
   int tiles_m, tiles_n, total;
 };
+
+constexpr int kPanelCodeBlock = BM * KSTAGE_B;  // 16 KiB: one (panel, chunk) code block
+constexpr int kPanelScaleBlock = BM * SCB;      // 1 KiB: its scale block
 
 // This thread's share of a stage load, independent of the tile: code chunk
 // offsets for its 4 code loads per operand (wave w's load `it` fills LDS rows
@@ -78,34 +96,46 @@ struct LaneOffsets {
   uint32_t sa, sb;
 };
 
+template <int LD>
 __device__ __forceinline__ void make_lane_offsets(LaneOffsets& o, const Problem& p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t lda = LD == LD_PANEL ? KSTAGE_B : p.lda, ldb = LD == LD_PANEL ? KSTAGE_B : p.ldb;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = (w * 4 + it) * 16 + (lane >> 2);
-    o.ca[it] = (uint32_t)(r * p.lda + swz(r, lane & 3) * 16);
-    o.cb[it] = (uint32_t)(r * p.ldb + swz(r, lane & 3) * 16);
+    o.ca[it] = (uint32_t)(r * lda + swz(r, lane & 3) * 16);
+    o.cb[it] = (uint32_t)(r * ldb + swz(r, lane & 3) * 16);
   }
-  o.sa = (uint32_t)(threadIdx.x * p.ld_as);
-  o.sb = (uint32_t)(threadIdx.x * p.ld_bs);
+  o.sa = (uint32_t)(threadIdx.x * (LD == LD_PANEL ? SCB : p.ld_as));
+  o.sb = (uint32_t)(threadIdx.x * (LD == LD_PANEL ? SCB : p.ld_bs));
 }
 
 // Buffer resources of one tile's operands (uniform, in SGPRs). Loads past
 // the matrix (rows past M / N, a tile past the last) read as zero through
-// the buffer range check.
+// the buffer range check. A panel-layout resource spans the tile's whole
+// panel (every K chunk); its padding rows hold zero codes.
 struct TileDesc {
   __amdgpu_buffer_rsrc_t a, b, as, bs;
 };
 
+template <int LD>
 __device__ __forceinline__ TileDesc make_desc(const Problem& p, int pid) {
   int tm = 0, tn = 0;
   const bool live = pid < p.total;
   if (live) tile_coords(pid, p.tiles_m, p.tiles_n, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
+  TileDesc d;
+  if (LD == LD_PANEL) {
+    const int64_t cb = live ? (int64_t)p.nkc * kPanelCodeBlock : 0, sb = live ? (int64_t)p.nkc * kPanelScaleBlock : 0;
+    d.a = make_rsrc(p.a + tm * (int64_t)p.nkc * kPanelCodeBlock, cb);
+    d.b = make_rsrc(p.b + tn * (int64_t)p.nkc * kPanelCodeBlock, cb);
+    d.as = make_rsrc(p.as + tm * (int64_t)p.nkc * kPanelScaleBlock, sb);
+    d.bs = make_rsrc(p.bs + tn * (int64_t)p.nkc * kPanelScaleBlock, sb);
+    return d;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t va = live ? min(p.M - m0, BM) : 0, vb = live ? min(p.N - n0, BN) : 0;
-  TileDesc d;
   d.a = make_rsrc(p.a + (int64_t)m0 * p.lda, va * p.lda);
   d.b = make_rsrc(p.b + (int64_t)n0 * p.ldb, vb * p.ldb);
   d.as = make_rsrc(p.as + (int64_t)m0 * p.ld_as, va * p.ld_as);
@@ -115,13 +145,31 @@ __device__ __forceinline__ TileDesc make_desc(const Problem& p, int pid) {
 
 // Issue K stage `st` of the tile described by `d` into `dst`. Code bytes
 // past K read as zero (out-of-range offset): zero codes contribute nothing
-// whatever their scale. Without SDW (scale rows not 4-byte aligned) the
-// scale bytes come back in sc[] -- issued first, so they complete before
-// this stage's code loads -- and are written to LDS by store_scale_regs().
-template <bool SDW>
+// whatever their scale. With byte scales (row-major, rows not 4-byte
+// aligned) the scale bytes come back in sc[] -- issued first, so they
+// complete before this stage's code loads -- and are written to LDS by
+// store_scale_regs(). Panel layout: stage st is block st of the panel, and
+// stages past the last chunk read as zero codes with zero scale bytes.
+template <int LD>
 __device__ __forceinline__ void issue_stage(StageMx& dst, const Problem& p, const LaneOffsets& o, const TileDesc& d,
                                             int st, uint32_t sc[8]) {
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (LD == LD_PANEL) {
+    const bool in = st < p.nkc;  // uniform
+    const int cboff = st * kPanelCodeBlock, sboff = st * kPanelScaleBlock;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, (lds_ptr_t)(dst.a + (w * 4 + it) * 1024), 16,
+                                               in ? o.ca[it] : kOob, cboff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, (lds_ptr_t)(dst.b + (w * 4 + it) * 1024), 16,
+                                               in ? o.cb[it] : kOob, cboff, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.as, (lds_ptr_t)(dst.as + w * 256), 4, in ? o.sa : kOob, sboff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.bs, (lds_ptr_t)(dst.bs + w * 256), 4, in ? o.sb : kOob, sboff, 0, 0);
+    return;
+  }
+  constexpr bool SDW = LD == LD_ROW_WORD;
+  const int lane = threadIdx.x & 63;
   const int kb = st * KSTAGE_B, kblk = st * SCB;
   if (!SDW) {
 #pragma unroll
@@ -210,11 +258,16 @@ __device__ __forceinline__ void read_codes(const StageMx& cur, int rn0, int rm0,
   }
 }
 
+// Panel layout: the padding scale bytes are 127 and stages past the last
+// chunk read as zero, so no byte needs replacing.
+template <int LD>
 __device__ __forceinline__ void read_stage(const StageMx& cur, int st, int nblk, int rn0, int rm0, int h, Frags& f) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    f.sw[q] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.bs[(rn0 + q * 32) * SCB + 2 * h]), st, nblk, h);
-    f.sx[q] = clean_scales(*reinterpret_cast<const uint16_t*>(&cur.as[(rm0 + q * 32) * SCB + 2 * h]), st, nblk, h);
+    const int vw = *reinterpret_cast<const uint16_t*>(&cur.bs[(rn0 + q * 32) * SCB + 2 * h]);
+    const int vx = *reinterpret_cast<const uint16_t*>(&cur.as[(rm0 + q * 32) * SCB + 2 * h]);
+    f.sw[q] = LD == LD_PANEL ? vw : clean_scales(vw, st, nblk, h);
+    f.sx[q] = LD == LD_PANEL ? vx : clean_scales(vx, st, nblk, h);
   }
   read_codes<0>(cur, rn0, rm0, h, f.w0, f.x0);
   read_codes<1>(cur, rn0, rm0, h, f.w1, f.x1);
@@ -245,10 +298,11 @@ __device__ __forceinline__ void mfma_stage(v16f acc[4][4], const Frags& f) {
 // st1: within-tile index of the next stage.
 // after_epi: the previous tile's epilogue issued exactly EPI vector-memory
 // instructions after the stages now in flight (they count in vmcnt too).
-template <bool SDW, int EPI = 0, bool READ_NEXT = true>
+template <int LD, int EPI = 0, bool READ_NEXT = true>
 __device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frags& next, StageMx& own,
                                           const StageMx& nxt, const Problem& p, const LaneOffsets& o, const TileDesc& d4,
                                           int st4, int st1, int rn0, int rm0, int h, bool after_epi = false) {
+  constexpr bool SDW = LD != LD_ROW_BYTE;
   constexpr int PER = SDW ? 10 : 16;  // vector-memory instructions per wave per stage
   constexpr int ALLOW_EPI = 2 * PER + EPI < 63 ? 2 * PER + EPI : 63;
   // this wave's share of the next stage has landed; after the barrier,
@@ -258,8 +312,8 @@ __device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frag
   else
     wait_barrier<2 * PER>();
   uint32_t sc[8];
-  issue_stage<SDW>(own, p, o, d4, st4, sc);
-  if (READ_NEXT) read_stage(nxt, st1, p.nblk, rn0, rm0, h, next);
+  issue_stage<LD>(own, p, o, d4, st4, sc);
+  if (READ_NEXT) read_stage<LD>(nxt, st1, p.nblk, rn0, rm0, h, next);
   mfma_stage(acc, cur);
   // schedule: MFMAs back to back, with the next stage's fragment reads and
   // the loads four stages ahead slotted between them
@@ -374,7 +428,7 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
   }
 }
 
-template <int BF16OUT, int RESID, bool SDW>
+template <int BF16OUT, int RESID, int LD>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* __restrict__ c, int64_t ldc,
                                                               const float* residual, int nst4) {
   constexpr int EPI = full_tile_vmem<BF16OUT, RESID>();
@@ -388,38 +442,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
   const int G = gridDim.x, g = blockIdx.x;
   if (g >= p.total) return;
 
+  constexpr bool SDW = LD != LD_ROW_BYTE;
   LaneOffsets o;
-  make_lane_offsets(o, p);
+  make_lane_offsets<LD>(o, p);
 
   // Prologue: the stream's first four stages (tile g, stages 0..3; nst4 >= 4).
   // The stage waits count this wave's loads in issue order, so no load may
   // move across a stage boundary.
-  TileDesc dcur = make_desc(p, g);
+  TileDesc dcur = make_desc<LD>(p, g);
   {
     uint32_t sc[8];
-    issue_stage<SDW>(s0, p, o, dcur, 0, sc);
+    issue_stage<LD>(s0, p, o, dcur, 0, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s0, sc); }
-    issue_stage<SDW>(s1, p, o, dcur, 1, sc);
+    issue_stage<LD>(s1, p, o, dcur, 1, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s1, sc); }
-    issue_stage<SDW>(s2, p, o, dcur, 2, sc);
+    issue_stage<LD>(s2, p, o, dcur, 2, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s2, sc); }
-    issue_stage<SDW>(s3, p, o, dcur, 3, sc);
+    issue_stage<LD>(s3, p, o, dcur, 3, sc);
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s3, sc); }
   }
   constexpr int PER = SDW ? 10 : 16;
   wait_barrier<3 * PER>();  // stage 0 has landed (this wave's share, then everyone's)
   Frags fa, fb;
-  read_stage(s0, 0, p.nblk, rn0, rm0, h, fa);
+  read_stage<LD>(s0, 0, p.nblk, rn0, rm0, h, fa);
 
   bool counted = false;  // the previous tile's stores are counted, not drained
   for (int pid = g; pid < p.total; pid += G) {
     int tm, tn;
     tile_coords(pid, p.tiles_m, p.tiles_n, tm, tn);
-    const TileDesc dnext = make_desc(p, pid + G);
+    const TileDesc dnext = make_desc<LD>(p, pid + G);
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -432,10 +487,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
       const bool last = st + NBUF == nst4;
       const TileDesc& d4 = last ? dnext : dcur;
       const int b4 = last ? 0 : st + NBUF;
-      pipe_step<SDW, EPI>(acc, fa, fb, s0, s1, p, o, d4, b4, st + 1, rn0, rm0, h, counted && st == 0);
-      pipe_step<SDW>(acc, fb, fa, s1, s2, p, o, d4, b4 + 1, st + 2, rn0, rm0, h);
-      pipe_step<SDW>(acc, fa, fb, s2, s3, p, o, d4, b4 + 2, st + 3, rn0, rm0, h);
-      pipe_step<SDW>(acc, fb, fa, s3, s0, p, o, d4, b4 + 3, last ? 0 : st + 4, rn0, rm0, h);
+      pipe_step<LD, EPI>(acc, fa, fb, s0, s1, p, o, d4, b4, st + 1, rn0, rm0, h, counted && st == 0);
+      pipe_step<LD>(acc, fb, fa, s1, s2, p, o, d4, b4 + 1, st + 2, rn0, rm0, h);
+      pipe_step<LD>(acc, fa, fb, s2, s3, p, o, d4, b4 + 2, st + 3, rn0, rm0, h);
+      pipe_step<LD>(acc, fb, fa, s3, s0, p, o, d4, b4 + 3, last ? 0 : st + 4, rn0, rm0, h);
     }
     dcur = dnext;
     int mb = tm * BM + wm * 128, nb = tn * BN + wn * 128;
@@ -465,15 +520,34 @@ int cu_count() {
 }
 
 template <int BF16OUT, int RESID>
-hipError_t launch(const Problem& p, void* c, int64_t ldc, const float* residual, hipStream_t st, bool sdw) {
-  const int nstages = (p.kbytes + KSTAGE_B - 1) / KSTAGE_B;
-  const int nst4 = (nstages + NBUF - 1) / NBUF * NBUF;
+hipError_t launch(const Problem& p, void* c, int64_t ldc, const float* residual, hipStream_t st, int ld) {
+  const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
   const unsigned grid = (unsigned)min(p.total, cu_count());
-  if (sdw)
-    gemm_mx_kernel<BF16OUT, RESID, true><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+  if (ld == LD_PANEL)
+    gemm_mx_kernel<BF16OUT, RESID, LD_PANEL><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+  else if (ld == LD_ROW_WORD)
+    gemm_mx_kernel<BF16OUT, RESID, LD_ROW_WORD><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   else
-    gemm_mx_kernel<BF16OUT, RESID, false><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+    gemm_mx_kernel<BF16OUT, RESID, LD_ROW_BYTE><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   return hipGetLastError();
+}
+
+hipError_t dispatch(const Problem& p, void* c, int c_bf16, int64_t ldc, const float* residual, hipStream_t st, int ld) {
+  if (c_bf16) return launch<1, 0>(p, c, ldc, nullptr, st, ld);
+  if (residual) return launch<0, 1>(p, c, ldc, residual, st, ld);
+  return launch<0, 0>(p, c, ldc, nullptr, st, ld);
+}
+
+Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m, int64_t n,
+                     int64_t k) {
+  Problem p;
+  p.a = a; p.as = as; p.b = b; p.bs = bs;
+  p.lda = p.ld_as = p.ldb = p.ld_bs = 0;
+  p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
+  p.nkc = (int)((k + 127) >> 7);
+  p.tiles_m = (int)((m + BM - 1) / BM); p.tiles_n = (int)((n + BN - 1) / BN);
+  p.total = p.tiles_m * p.tiles_n;
+  return p;
 }
 
 }  // namespace
@@ -481,18 +555,18 @@ hipError_t launch(const Problem& p, void* c, int64_t ldc, const float* residual,
 hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const uint8_t* b,
                           int64_t ldb, const uint8_t* bs, int64_t ld_bs, int64_t m, int64_t n, int64_t k, void* c,
                           int c_bf16, int64_t ldc, const float* residual, hipStream_t st) {
-  Problem p;
-  p.a = a; p.as = as; p.b = b; p.bs = bs;
+  Problem p = make_problem(a, as, b, bs, m, n, k);
   p.lda = lda; p.ld_as = ld_as; p.ldb = ldb; p.ld_bs = ld_bs;
-  p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
-  p.tiles_m = (int)((m + BM - 1) / BM); p.tiles_n = (int)((n + BN - 1) / BN);
-  p.total = p.tiles_m * p.tiles_n;
   // scales as whole 4-byte words when every row's scale bytes start 4-byte aligned
   const bool sdw = (ld_as % 4 == 0) && (ld_bs % 4 == 0) && (reinterpret_cast<uintptr_t>(as) % 4 == 0) &&
                    (reinterpret_cast<uintptr_t>(bs) % 4 == 0);
-  if (c_bf16) return launch<1, 0>(p, c, ldc, nullptr, st, sdw);
-  if (residual) return launch<0, 1>(p, c, ldc, residual, st, sdw);
-  return launch<0, 0>(p, c, ldc, nullptr, st, sdw);
+  return dispatch(p, c, c_bf16, ldc, residual, st, sdw ? LD_ROW_WORD : LD_ROW_BYTE);
+}
+
+hipError_t launch_gemm_mx_panel(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m,
+                                int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc, const float* residual,
+                                hipStream_t st) {
+  return dispatch(make_problem(a, as, b, bs, m, n, k), c, c_bf16, ldc, residual, st, LD_PANEL);
 }
 
 }  // namespace fp4r

@@ -112,6 +112,42 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
   }
 }
 
+// Panel layout: (panel of 256 rows, chunk of 128 elements) blocks of 256 x 16
+// octets, thread i owns octet i % 16 of row i / 16 % 256 in block i / 4096,
+// so its code word lands at byte 4 i and its block's scale byte at i / 4 --
+// every wave writes 256 contiguous code bytes. Rows past `rows` and
+// elements past k are padding: code 0, scale byte 127.
+template <int BF16, int PRO>
+__global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t nc, int64_t total_oct) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
+    const int64_t blk = i >> 12;
+    const int64_t pnl = blk / nc, ch = blk - pnl * nc;
+    const int64_t row = pnl * 256 + ((i >> 4) & 255), e0 = ch * 128 + (i & 15) * 8;
+    // a 32-block's 4 octets share row and validity (k is a multiple of 32)
+    const bool valid = row < rows && e0 < k;
+    float v[8];
+    if (valid) {
+      load8<BF16>(x, row * ldx + e0, v);
+      if (PRO == PRO_GELU) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    uint32_t am = amax_bits8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+    const uint32_t S = mx_scale(am);
+    reinterpret_cast<uint32_t*>(codes)[i] = valid ? mx_pack8(v, S) : 0u;
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(valid ? S : 127u);
+  }
+}
+
 // Deterministic block-wide fp32 sum (fixed shuffle tree, then fixed LDS order).
 __device__ float block_sum(float v, float* sh) {
 #pragma unroll
@@ -159,6 +195,49 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_kernel(
     const uint32_t S = mx_scale(am);
     *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = mx_pack8(v, S);
     if ((oct & 3) == 0) scales[row * ld_scales + (oct >> 2)] = (uint8_t)S;
+  }
+}
+
+// RMSNorm prologue into the panel layout: one workgroup per row of the padded
+// row range (rows past `rows` write padding only); same arithmetic as above.
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_panel_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t nc) {
+  __shared__ float sh[16];
+  const int64_t row = blockIdx.x;
+  const bool row_valid = row < rows;  // uniform over the workgroup
+  const int64_t oct_per_row = k >> 3;
+  float ss = 0.f;
+  if (row_valid) {
+    for (int64_t oct = threadIdx.x; oct < oct_per_row; oct += kThreads) {
+      float v[8];
+      load8<BF16>(x, row * ldx + oct * 8, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+    }
+  }
+  const float tot = block_sum(ss, sh);
+  const float inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+  const int64_t pnl = row >> 8, rr = row & 255;
+  for (int64_t oct = threadIdx.x; oct < nc * 16; oct += kThreads) {
+    const bool valid = row_valid && oct < oct_per_row;  // shared by a 32-block's 4 octets
+    float v[8];
+    if (valid) {
+      load8<BF16>(x, row * ldx + oct * 8, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    uint32_t am = amax_bits8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+    const uint32_t S = mx_scale(am);
+    const int64_t blk = pnl * nc + (oct >> 4);
+    *reinterpret_cast<uint32_t*>(codes + (blk * 256 + rr) * 64 + (oct & 15) * 4) = valid ? mx_pack8(v, S) : 0u;
+    if ((oct & 3) == 0) scales[(blk * 256 + rr) * 4 + ((oct & 15) >> 2)] = (uint8_t)(valid ? S : 127u);
   }
 }
 
@@ -281,6 +360,33 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
       quant_mx_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
     else
       quant_mx_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx, uint8_t* codes,
+                                 uint8_t* scales, int prologue, hipStream_t st) {
+  const int64_t panels = (rows + 255) >> 8, nc = (k + 127) >> 7;
+  if (prologue == PRO_RMSNORM) {
+    const unsigned g = (unsigned)(panels * 256);
+    if (x_bf16)
+      quant_mx_rmsnorm_panel_kernel<1><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc);
+    else
+      quant_mx_rmsnorm_panel_kernel<0><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc);
+    return hipGetLastError();
+  }
+  const int64_t total = panels * nc * 4096;
+  const unsigned g = grid_for(total);
+  if (prologue == PRO_GELU) {
+    if (x_bf16)
+      quant_mx_panel_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+    else
+      quant_mx_panel_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+  } else {
+    if (x_bf16)
+      quant_mx_panel_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+    else
+      quant_mx_panel_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
   }
   return hipGetLastError();
 }

@@ -15,7 +15,10 @@ uniform grid t_i = 1 - i/steps. Per block the device work is:
     fp4_quantize(z, GELU prologue)        -> A2 (MXFP4)
     fp4_gemm(A2, W2q, residual = h) -> h  (fp32, in place)
 and per step euler_step(x, v = h). The hidden activation z is stored as bf16
-between the two kernels (the float64 oracle keeps it unrounded).
+between the two kernels (the float64 oracle keeps it unrounded). The FP4
+operands use the panel layout by default (fp4_quantize with FP4_LAYOUT_PANEL,
+fp4_gemm_panel): the same codes and scales, stored so that every GEMM stage
+load is contiguous; layout="row" runs the row-major entry points instead.
 
 Every call enqueues on the current stream; the only host synchronization is
 the caller reading the selected indices.
@@ -24,7 +27,8 @@ from . import binding as fb
 
 
 class Fp4Rollout:
-    def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None):
+    def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None,
+                 layout="panel"):
         """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
         chunk: candidates per pass through the network (None = all).
         timer: optional callable(name, fn) wrapping each GEMM launch (for timing)."""
@@ -32,16 +36,18 @@ class Fp4Rollout:
             raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
         self.w1, self.w2, self.u = list(w1), list(w2), u
         self.steps, self.k_top, self.k_bottom = steps, k_top, k_bottom
-        self.fmt, self.chunk = fmt, chunk
+        if layout not in ("panel", "row"):
+            raise ValueError(f"unknown layout {layout!r}")
+        self.fmt, self.chunk, self.layout = fmt, chunk, layout
         self.timer = timer
         self.q1 = self.q2 = None
         self._bufs = {}
 
     def requantize(self):
         """Per-iteration weight re-quantization (all weights, on device)."""
-        self.q1 = [fb.quantize(w, self.fmt, out=None if self.q1 is None else self.q1[i])
+        self.q1 = [fb.quantize(w, self.fmt, out=None if self.q1 is None else self.q1[i], layout=self.layout)
                    for i, w in enumerate(self.w1)]
-        self.q2 = [fb.quantize(w, self.fmt, out=None if self.q2 is None else self.q2[i])
+        self.q2 = [fb.quantize(w, self.fmt, out=None if self.q2 is None else self.q2[i], layout=self.layout)
                    for i, w in enumerate(self.w2)]
 
     def _buf(self, name, shape, dtype, device):
@@ -79,6 +85,11 @@ class Fp4Rollout:
 
     def _qbuf(self, name, rows, k, device):
         import torch
+        if self.layout == "panel":
+            cb, sb = fb.panel_bytes(rows, k)
+            codes = self._buf(name + ".c", (cb,), torch.uint8, device)
+            scales = self._buf(name + ".s", (sb,), torch.uint8, device)
+            return fb.QTensor(codes, scales, None, fb.FMT_MX, k, "panel", rows)
         ldc = ((k // 2 + 15) // 16) * 16
         codes = self._buf(name + ".c", (rows, ldc), torch.uint8, device)
         scales = self._buf(name + ".s", (rows, k // 32), torch.uint8, device)

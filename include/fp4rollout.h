@@ -13,7 +13,8 @@
  *     the caller owns and frees every buffer. The library allocates nothing.
  *   - Matrices are row-major; every leading dimension ("ld*") is the distance
  *     between consecutive rows, in ELEMENTS for float/bf16 arrays and in
- *     BYTES for packed codes and scale bytes.
+ *     BYTES for packed codes and scale bytes. The exception is the panel
+ *     layout of MXFP4 codes and scales (FP4_LAYOUT_PANEL, below).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it; nothing synchronizes. A device
  *     fault therefore surfaces at the caller's next synchronization.
@@ -57,6 +58,25 @@ typedef int32_t fp4_status;
 #define FP4_PRO_RMSNORM        0x1   /* quantize x * (mean_k(x^2) + 1e-6)^(-1/2) (row-wise, unit gain) */
 #define FP4_PRO_GELU           0x2   /* quantize 0.5 x (1 + erf(x / sqrt 2)) */
 #define FP4_TENSOR_SCALE_GIVEN 0x100 /* NV: read s_g from *tensor_scale instead of computing it */
+#define FP4_LAYOUT_PANEL       0x200 /* MX: write codes and scales in the panel layout (below) */
+
+/*
+ * Panel layout -- the GEMM-native arrangement of an MXFP4 [rows, k] operand
+ * (a storage order only: the codes and scale bytes are those of the
+ * row-major layout). Rows are grouped into panels of 256, k into chunks of
+ * 128 elements (nc = ceil(k / 128) chunks). The codes of one (panel, chunk)
+ * pair form one contiguous 16 KiB block of 256 rows x 64 bytes, row-major
+ * inside; the scale bytes one contiguous 1 KiB block of 256 rows x 4 bytes.
+ * Blocks are ordered panel-major, chunk-minor:
+ *   code byte j (elements 2j, 2j+1) of row r:
+ *     ((r / 256 * nc + j / 64) * 256 + r % 256) * 64 + j % 64
+ *   scale byte b (elements 32b .. 32b+31) of row r:
+ *     ((r / 256 * nc + b / 4) * 256 + r % 256) * 4 + b % 4
+ * Rows past `rows` in the last panel and elements past k in the last chunk
+ * are padding, written by fp4_quantize as code byte 0 and scale byte 127
+ * (2^0). Each load of a GEMM K stage is then one contiguous run, where
+ * row-major rows give short pieces of many rows.
+ */
 
 /*
  * fp4_quantize -- block-scaled 4-bit quantization of a [rows, k] matrix along k.
@@ -71,7 +91,8 @@ typedef int32_t fp4_status;
  *   x            [rows, ldx] elements of type x_dtype (FP4_DT_F32 or FP4_DT_BF16);
  *                16-byte aligned, ldx*sizeof(elem) a multiple of 16, ldx >= k.
  *   rows, k      rows >= 1; k >= 32 and a multiple of 32 (MX) or 16 (NV).
- *   codes        out, [rows, ld_codes] bytes; byte j of a row packs elements
+ *   codes        out, [rows, ld_codes] bytes (or the panel layout, see flags);
+ *                byte j of a row packs elements
  *                2j (low nibble) and 2j+1 (high nibble). Nibble = sign<<3 | m,
  *                magnitude G[m], G = {0, .5, 1, 1.5, 2, 3, 4, 6}; nearest value,
  *                ties to even m, saturating at 6, sign always kept.
@@ -89,11 +110,23 @@ typedef int32_t fp4_status;
  *                be positive and finite). Without that flag its word is also
  *                used as the amax accumulator while the call runs.
  *   flags        MX: at most one of FP4_PRO_RMSNORM / FP4_PRO_GELU (applied in
- *                fp32 before quantization). NV: only FP4_TENSOR_SCALE_GIVEN.
+ *                fp32 before quantization), optionally FP4_LAYOUT_PANEL: codes
+ *                and scales then use the panel layout (sizes from
+ *                fp4_panel_bytes; codes 16-byte, scales 4-byte aligned;
+ *                ld_codes and ld_scales must be 0).
+ *                NV: only FP4_TENSOR_SCALE_GIVEN.
  */
 FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                         float* tensor_scale, int flags, void* stream);
+
+/*
+ * fp4_panel_bytes -- sizes of the panel layout of a [rows, k] MXFP4 operand:
+ *   *code_bytes  = ceil(rows / 256) * ceil(k / 128) * 16384,
+ *   *scale_bytes = ceil(rows / 256) * ceil(k / 128) * 1024.
+ * rows >= 1, k >= 32 and a multiple of 32; both outputs are host pointers.
+ */
+FP4_API fp4_status fp4_panel_bytes(int64_t rows, int64_t k, int64_t* code_bytes, int64_t* scale_bytes);
 
 /*
  * fp4_gemm -- C[m, n] = sum_k A_hat[m, k] * B_hat[n, k]  (+ residual[m, n]),
@@ -123,6 +156,23 @@ FP4_API fp4_status fp4_gemm(int fmt,
                     const float* b_ts,
                     int64_t m, int64_t n, int64_t k,
                     void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
+
+/*
+ * fp4_gemm_panel -- fp4_gemm for MXFP4 operands in the panel layout (same
+ * product, accumulation, output and accuracy as fp4_gemm).
+ *   fmt               FP4_FMT_MX (FP4_FMT_NV: FP4_UNSUPPORTED).
+ *   a_codes, a_scales panel layout of A [m, k] as written by fp4_quantize with
+ *                     FP4_LAYOUT_PANEL (padding included); codes 16-byte and
+ *                     scales 4-byte aligned.
+ *   b_codes, b_scales the same for B [n, k].
+ *   m, n, k           >= 1; k a multiple of 32, k <= 2^23.
+ *   c, c_dtype, ldc,  as in fp4_gemm.
+ *   residual
+ */
+FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                          const uint8_t* b_codes, const uint8_t* b_scales,
+                          int64_t m, int64_t n, int64_t k,
+                          void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
 
 /*
  * euler_step -- one explicit Euler step of the sampler's ODE,

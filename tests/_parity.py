@@ -58,3 +58,18 @@ def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6):
         bad += int((dc & ~okay).sum())
         flips += int(okay.sum())
     return bad, flips
+
+
+def panel_to_rows(codes, scales, rows, k):
+    """Row-major (codes [rows, k/2], scales [rows, k/32]) of a panel-layout
+    MXFP4 operand, plus its padding (codes and scale bytes past rows / k) for
+    the padding checks. The layout is the storage order declared with
+    FP4_LAYOUT_PANEL in include/fp4rollout.h: (panel of 256 rows, chunk of 128
+    elements) blocks, 256 x 64 code bytes and 256 x 4 scale bytes each."""
+    codes, scales = np.asarray(codes), np.asarray(scales)
+    p, nc = (rows + 255) // 256, (k + 127) // 128
+    assert codes.size == p * nc * 16384 and scales.size == p * nc * 1024
+    c = codes.reshape(p, nc, 256, 64).transpose(0, 2, 1, 3).reshape(p * 256, nc * 64)
+    s = scales.reshape(p, nc, 256, 4).transpose(0, 2, 1, 3).reshape(p * 256, nc * 4)
+    pad = dict(code_rows=c[rows:], code_cols=c[:rows, k // 2:], scale_rows=s[rows:], scale_cols=s[:rows, k // 32:])
+    return c[:rows, : k // 2], s[:rows, : k // 32], pad

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 100
+    assert fq.fp4_abi_version() == 101
 
 
 def test_status_strings(lib):
@@ -107,3 +107,48 @@ def test_reward_rejects(lib, args):
 ])
 def test_select_rejects(lib, args):
     assert fq.select_topk_bottomk(*args) == fq.binding.INVALID_ARGUMENT
+
+
+def test_panel_bytes(lib):
+    import ctypes
+    cb, sb = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    for rows, k, blocks in [(1, 32, 1), (256, 128, 1), (257, 128, 2), (300, 160, 4), (393216, 3072, 1536 * 24)]:
+        assert fq.fp4_panel_bytes(rows, k, ctypes.addressof(cb), ctypes.addressof(sb)) == fq.binding.OK
+        assert (cb.value, sb.value) == (blocks * 16384, blocks * 1024)
+    assert fq.binding.panel_bytes(513, 4160) == (3 * 33 * 16384, 3 * 33 * 1024)
+    for rows, k in [(0, 32), (4, 48), (4, 0), (1 << 31, 32)]:
+        assert fq.fp4_panel_bytes(rows, k, ctypes.addressof(cb), ctypes.addressof(sb)) == fq.binding.INVALID_ARGUMENT
+    assert fq.fp4_panel_bytes(4, 32, None, ctypes.addressof(sb)) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [
+    dict(flags=0x200), dict(flags=0x200, ld_codes=0), dict(flags=0x200, ld_scales=0),
+    dict(flags=0x200, ld_codes=0, ld_scales=0, codes=P2 + 4), dict(flags=0x200, ld_codes=0, ld_scales=0, scales=P3 + 2),
+    dict(flags=0x203, ld_codes=0, ld_scales=0), dict(flags=0x400, ld_codes=0, ld_scales=0),
+])
+def test_quantize_panel_rejects(lib, kw):
+    assert q(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_quantize_panel_nv_unsupported(lib):
+    assert q(fmt=1, tensor_scale=P3, flags=0x200, ld_codes=0, ld_scales=0) == fq.binding.UNSUPPORTED
+
+
+def gp(**kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=8, n=8, k=64, c=P, c_dtype=0, ldc=8, residual=None, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_panel(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(b=None), dict(a_s=None), dict(b_s=None), dict(c=None), dict(m=0), dict(n=0),
+    dict(k=0), dict(k=48), dict(k=(1 << 23) + 32), dict(a=P + 8), dict(b=P2 + 4), dict(a_s=P3 + 2), dict(b_s=P3 + 1),
+    dict(c_dtype=7), dict(ldc=6), dict(ldc=10), dict(c=P + 4), dict(c_dtype=1, c=P + 2),
+    dict(c_dtype=1, residual=P2), dict(residual=P2 + 4), dict(m=1 << 31),
+])
+def test_gemm_panel_rejects(lib, kw):
+    assert gp(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_gemm_panel_nv_unsupported(lib):
+    assert gp(fmt=1) == fq.binding.UNSUPPORTED

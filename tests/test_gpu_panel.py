@@ -1,0 +1,170 @@
+"""GPU parity of the panel layout: fp4_quantize(FP4_LAYOUT_PANEL) writes the
+same codes and scale bytes as the row-major quantizer (and as the oracle),
+in the declared storage order, with the declared padding; fp4_gemm_panel
+matches the oracle's exact product within the fp32 bound, is bit-exact in
+the exact-integer case, and equals the row-major GEMM bit for bit (same K
+order, zero padding contributes exact zeros)."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_quantized_diffusion_amd import inputs
+from fp4_quantized_diffusion_amd.binding import FMT_MX, QTensor
+from oracle import gemm as ogemm, mxfp4, rollout as orollout
+from tests._parity import gemm_within_tol, mx_codes_near_boundary_ok, panel_to_rows, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# (rows, k): single row and block, ragged panels and chunks, several panels,
+# k below one chunk, k not a multiple of 128
+SHAPES = [(1, 32), (300, 160), (256, 3072), (513, 96), (77, 4160), (1024, 128)]
+
+
+def act(rows, cols, seed):
+    return inputs.activations(np.random.default_rng(seed), rows, cols)
+
+
+def wts(rows, cols, seed):
+    return inputs.weights(np.random.default_rng(seed), rows, cols)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check_padding(pad):
+    assert (pad["code_rows"] == 0).all() and (pad["code_cols"] == 0).all()
+    assert (pad["scale_rows"] == 127).all() and (pad["scale_cols"] == 127).all()
+
+
+@pytest.mark.parametrize("rows,k", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("prologue", [None, "gelu", "rmsnorm"])
+def test_quantize_panel_equals_row_major(gpu_lib, rows, k, dtype, prologue):
+    x = dev(act(rows, k, rows * 7 + k)).to(dtype)
+    qp = gpu_lib.quantize(x, "mx", prologue=prologue, layout="panel")
+    qr = gpu_lib.quantize(x, "mx", prologue=prologue)
+    c, s, pad = panel_to_rows(to_np(qp.codes), to_np(qp.scales), rows, k)
+    np.testing.assert_array_equal(c, to_np(qr.codes)[:, : k // 2])
+    np.testing.assert_array_equal(s, to_np(qr.scales)[:, : k // 32])
+    check_padding(pad)
+
+
+@pytest.mark.parametrize("rows,k", SHAPES)
+def test_quantize_panel_vs_oracle(gpu_lib, rows, k):
+    """Plain quantization is exact: the oracle's codes and scales bit for bit."""
+    x = act(rows, k, rows + 3 * k)
+    qp = gpu_lib.quantize(dev(x), "mx", layout="panel")
+    c, s, _ = panel_to_rows(to_np(qp.codes), to_np(qp.scales), rows, k)
+    oc, os_ = mxfp4.quantize(x)
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(s, os_)
+
+
+def test_quantize_panel_gelu_vs_oracle(gpu_lib):
+    """Fused GELU in fp32 against the fp64 oracle GELU: exact except within
+    2e-6 of a decision point."""
+    rows, k = 300, 4160
+    z = act(rows, k, 11) * 3.0
+    qp = gpu_lib.quantize(dev(z), "mx", prologue="gelu", layout="panel")
+    c, s, _ = panel_to_rows(to_np(qp.codes), to_np(qp.scales), rows, k)
+    bad, flips = mx_codes_near_boundary_ok(orollout.gelu(z.astype(np.float64)), c, s)
+    assert bad == 0, (bad, flips)
+
+
+def test_quantize_panel_reuses_out(gpu_lib):
+    rows, k = 300, 160
+    x1 = dev(act(rows, k, 1))
+    x2 = dev(act(rows, k, 2))
+    q = gpu_lib.quantize(x1, "mx", layout="panel")
+    q = gpu_lib.quantize(x2, "mx", out=q)
+    c, s, pad = panel_to_rows(to_np(q.codes), to_np(q.scales), rows, k)
+    oc, os_ = mxfp4.quantize(to_np(x2))
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(s, os_)
+    check_padding(pad)
+
+
+GEMM_SHAPES = [(1, 1, 32), (300, 520, 160), (256, 256, 128), (513, 260, 4160), (64, 1000, 96), (260, 300, 3072)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+@pytest.mark.parametrize("out", ["f32", "bf16", "f32+res"])
+def test_gemm_panel_vs_oracle_and_row_major(gpu_lib, m, n, k, out):
+    a = act(m, k, m + k)
+    b = wts(n, k, n + 2 * k)
+    qa_p = gpu_lib.quantize(dev(a), "mx", layout="panel")
+    qb_p = gpu_lib.quantize(dev(b), "mx", layout="panel")
+    qa_r = gpu_lib.quantize(dev(a), "mx")
+    qb_r = gpu_lib.quantize(dev(b), "mx")
+    res = None
+    if out == "f32+res":
+        ldc = ((n + 3) // 4) * 4
+        res = dev(act(m, ldc, 5))
+    dt = "bf16" if out == "bf16" else "f32"
+    cp = gpu_lib.gemm(qa_p, qb_p, dt, residual=res)
+    cr = gpu_lib.gemm(qa_r, qb_r, dt, residual=res)
+    np.testing.assert_array_equal(to_np(cp.float()), to_np(cr.float()))
+    ac, as_, _ = panel_to_rows(to_np(qa_p.codes), to_np(qa_p.scales), m, k)
+    bc, bs, _ = panel_to_rows(to_np(qb_p.codes), to_np(qb_p.scales), n, k)
+    c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+    if res is not None:
+        c_exact = c_exact + to_np(res)[:, :n].astype(np.float64)
+    ok, worst = gemm_within_tol(to_np(cp.float()), c_exact, s_abs, bf16_out=(out == "bf16"))
+    assert ok, worst
+
+
+def panel_operand(codes, scales, rows, k):
+    """Lay a row-major operand out in panel order on the device (test-side
+    placement of given bytes, padding included) -- used to feed hand-built
+    codes to fp4_gemm_panel."""
+    p, nc = (rows + 255) // 256, (k + 127) // 128
+    c = np.zeros((p * 256, nc * 64), np.uint8)
+    s = np.full((p * 256, nc * 4), 127, np.uint8)
+    c[:rows, : k // 2] = codes
+    s[:rows, : k // 32] = scales
+    c = c.reshape(p, 256, nc, 64).transpose(0, 2, 1, 3).reshape(-1)
+    s = s.reshape(p, 256, nc, 4).transpose(0, 2, 1, 3).reshape(-1)
+    return QTensor(dev(c), dev(s), None, FMT_MX, k, "panel", rows)
+
+
+def test_gemm_panel_exact_integer_case(gpu_lib):
+    """Scales 2^0 and grid codes: fp32 accumulation is exact, so the result
+    must equal the oracle bit for bit."""
+    rng = np.random.default_rng(31)
+    for (m, n, k) in [(256, 256, 256), (300, 260, 512), (129, 515, 4096), (16, 16, 32), (260, 33, 160)]:
+        ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+        bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        as_ = np.full((m, k // 32), 127, np.uint8)
+        bs = np.full((n, k // 32), 127, np.uint8)
+        c = to_np(gpu_lib.gemm(panel_operand(ac, as_, m, k), panel_operand(bc, bs, n, k), "f32"))
+        c_exact, _ = ogemm.gemm_mx(ac, as_, bc, bs)
+        np.testing.assert_array_equal(c.astype(np.float64), c_exact)
+
+
+def test_gemm_panel_rollout_shape_sampled(gpu_lib):
+    """The rollout's first solver linear at full size (96 candidates x 4096
+    tokens, 3072 -> 12288, bf16 out): sampled rows and columns against the
+    oracle's exact product."""
+    m, k, n = 96 * 4096, 3072, 12288
+    torch.manual_seed(0)
+    a = torch.randn(m, k, device=DEV, dtype=torch.bfloat16)
+    b = (torch.randn(n, k, device=DEV, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    qa = gpu_lib.quantize(a, "mx", layout="panel")
+    qb = gpu_lib.quantize(b, "mx", layout="panel")
+    c = gpu_lib.gemm(qa, qb, "bf16")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(m, 48, replace=False))
+    rows[-1] = m - 1
+    cols = np.sort(rng.choice(n, 64, replace=False))
+    cols[-1] = n - 1
+    a_rows = to_np(a[torch.from_numpy(rows).to(DEV)].float())
+    b_cols = to_np(b[torch.from_numpy(cols).to(DEV)].float())
+    ac, as_ = mxfp4.quantize(a_rows)
+    bc, bs = mxfp4.quantize(b_cols)
+    c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+    got = to_np(c[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float())
+    ok, worst = gemm_within_tol(got, c_exact, s_abs, bf16_out=True)
+    assert ok, worst

@@ -20,7 +20,8 @@ def ranks(v):
     return np.argsort(np.argsort(v))
 
 
-def test_reduced_rollout_against_oracle(gpu_lib):
+@pytest.mark.parametrize("layout", ["panel", "row"])
+def test_reduced_rollout_against_oracle(gpu_lib, layout):
     seed, n_cand, tokens, dim, hidden = 4, 8, 64, 256, 1024
     noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
     ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
@@ -31,7 +32,7 @@ def test_reduced_rollout_against_oracle(gpu_lib):
 
     ro = Fp4Rollout([torch.from_numpy(w).to(DEV).bfloat16() for w in w1],
                     [torch.from_numpy(w).to(DEV).bfloat16() for w in w2],
-                    torch.from_numpy(u).to(DEV), k_top=2, k_bottom=2, chunk=3)
+                    torch.from_numpy(u).to(DEV), k_top=2, k_bottom=2, chunk=3, layout=layout)
     xd = torch.from_numpy(noise).to(DEV)
     r, top, bottom, rn = ro.run(xd)
     torch.cuda.synchronize()
@@ -46,3 +47,24 @@ def test_reduced_rollout_against_oracle(gpu_lib):
     gt, gb = oreward.select(to_np(r), 2, 2)
     np.testing.assert_array_equal(to_np(top), gt)
     np.testing.assert_array_equal(to_np(bottom), gb)
+
+
+def test_panel_and_row_layouts_agree_bitwise(gpu_lib):
+    """The two operand layouts store the same codes and run the same K order,
+    so whole rollouts (ragged chunk, 300-token candidates: a ragged last
+    panel) agree bit for bit."""
+    seed, n_cand, tokens, dim, hidden = 5, 5, 300, 256, 1024
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
+    u = torch.from_numpy(inputs.reward_vector(seed, dim)).to(DEV)
+    w1 = [torch.from_numpy(w[0]).to(DEV).bfloat16() for w in ws]
+    w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
+    outs = []
+    for layout in ("panel", "row"):
+        ro = Fp4Rollout(w1, w2, u, k_top=2, k_bottom=1, chunk=2, layout=layout)
+        xd = torch.from_numpy(noise).to(DEV)
+        r, top, bottom, rn = ro.run(xd)
+        torch.cuda.synchronize()
+        outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
