@@ -34,6 +34,9 @@ Parity status per function:
   euler ....................... pinned (constant-field closed form, dt=0)
   reward / select ............. pinned (hand cases, brute-force sort,
                                 permutation equivariance)
+  rollout.gelu / rmsnorm ...... pinned (normal-CDF table values, the identity
+                                GELU(z) - GELU(-z) = z, Mills-ratio tail series;
+                                hand row, constant rows, mean-square identity)
   rollout (composite) ......... parity unpinned beyond the pinned pieces it
                                 composes (statistical comparison only)
 """

@@ -9,15 +9,15 @@ The pages' velocity network is a trained DiT; this stand-in keeps only the
 shape of its MLP linears. Readings (the pages give no network):
   * velocity v(x) = h_4 with h_0 = x and
         h_{b+1} = h_b + W2_b GELU(W1_b RMSNorm(h_b)),   b = 0..3
-    RMSNorm with unit gain and eps 1e-6, GELU in its exact erf form, no time
-    conditioning;
+    RMSNorm with unit gain and eps 1e-6, exact (not tanh-approximated) GELU,
+    GELU(z) = z Phi(z) with Phi the standard normal CDF, no time conditioning;
   * every linear input is rounded to fp32 and then quantized (the quantizers
     take fp32 or bf16 input); everything else is float64;
   * proxy reward = <mean over tokens of x_final, u> for a fixed vector u;
   * Euler steps on the uniform grid t_i = 1 - i/6.
 """
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 from . import euler, gemm, mxfp4, nvfp4, reward
 
@@ -30,8 +30,11 @@ def rmsnorm(h):
 
 
 def gelu(z):
+    """z Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2: the same function as
+    0.5 z (1 + erf(z / sqrt 2)), written so the negative tail keeps its
+    relative accuracy (1 + erf cancels there)."""
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+    return 0.5 * z * erfc(-z / np.sqrt(2.0))
 
 
 class QuantLinear:
