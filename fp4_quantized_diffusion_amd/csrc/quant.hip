@@ -41,9 +41,50 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8])
   }
 }
 
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+// GELU(z) = z Phi(z), Phi the standard normal CDF, through the complementary
+// error function: with Q = erfc(|z| / sqrt 2) / 2, Phi(z) = Q for z < 0 and
+// 1 - Q otherwise, so the negative side never forms 1 + erf (which cancels
+// to a few correct bits below z = -3). erfc uses the Chebyshev fit of Press
+// et al., Numerical Recipes in C (2nd ed.), section 6.2 ("erfcc", fractional
+// error below 1.2e-7 for x >= 0):
+//     erfc(x) ~ t exp(-x^2 + P(t)),  t = 1 / (1 + x / 2),  P of degree 9.
+// Here Q = t 2^(log2(e) P(t) - 1) 2^(-z^2 log2(e) / 2): the polynomial is
+// evaluated with its coefficients scaled by log2(e) (and 1 taken off the
+// constant term), and the large-argument factor takes the exact two-term
+// split of z^2 and of log2(e) / 2 plus a first-order correction for the low
+// parts, so it adds no rounding error of its own. v_rcp_f32 / v_exp_f32 are
+// 1-ulp operations. Relative error of the result: about 5e-7 for |z| <= 12
+// (fp32 emulation of this sequence against float64 erfc). |z| is clamped at
+// 16, where Q is below fp32's range (Phi is then 0 or 1).
+#define FP4R_L2E(c) ((float)((c) * 1.4426950408889634))
+__device__ __forceinline__ float gelu_erfc(float z) {
+  constexpr float kHalfLog2eHi = -0.7213475f;     // -log2(e) / 2, high part
+  constexpr float kHalfLog2eLo = -9.629815e-09f;  // and the rest
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float a = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 16.0f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(a, 0.353553390593273762f, 1.0f));  // 1 / (1 + a / (2 sqrt 2))
+  float p = FP4R_L2E(0.17087277);
+  p = fmaf(p, t, FP4R_L2E(-0.82215223));
+  p = fmaf(p, t, FP4R_L2E(1.48851587));
+  p = fmaf(p, t, FP4R_L2E(-1.13520398));
+  p = fmaf(p, t, FP4R_L2E(0.27886807));
+  p = fmaf(p, t, FP4R_L2E(-0.18628806));
+  p = fmaf(p, t, FP4R_L2E(0.09678418));
+  p = fmaf(p, t, FP4R_L2E(0.37409196));
+  p = fmaf(p, t, FP4R_L2E(1.00002368));
+  p = fmaf(p, t, (float)(-1.26551223 * 1.4426950408889634 - 1.0));
+  const float eph = __builtin_amdgcn_exp2f(p);    // exp(P(t)) / 2
+  const float s = a * a, s_lo = fmaf(a, a, -s);  // a^2 = s + s_lo exactly
+  const float y = s * kHalfLog2eHi;
+  float e = fmaf(s, kHalfLog2eHi, -y);            // -a^2 log2(e) / 2 = y + e (to ~2^-48 relative)
+  e = fmaf(s_lo, kHalfLog2eHi, e);
+  e = fmaf(s, kHalfLog2eLo, e);
+  float es = __builtin_amdgcn_exp2f(y);
+  es = fmaf(es * e, kLn2, es);                     // exp2(y + e) ~ exp2(y) (1 + e ln 2)
+  const float q = t * (eph * es);
+  return z * (z < 0.0f ? q : 1.0f - q);
 }
+#undef FP4R_L2E
 
 __device__ __forceinline__ uint32_t amax_bits8(const float v[8]) {
   uint32_t m = 0;
@@ -87,64 +128,76 @@ __device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
   return w;
 }
 
-// One octet per thread, grid-stride. Elementwise prologues only.
+// Elementwise prologue of one loaded octet.
+template <int PRO>
+__device__ __forceinline__ void prologue8(float v[8]) {
+  if (PRO == PRO_GELU) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = gelu_erfc(v[j]);
+  }
+}
+
+// Block scale of a 32-block held as 4 octets in lanes 4q..4q+3, and the
+// octet's code word.
+__device__ __forceinline__ uint32_t mx_block(const float v[8], uint32_t& S) {
+  uint32_t am = amax_bits8(v);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+  S = mx_scale(am);
+  return mx_pack8(v, S);
+}
+
+// Row-major layout, elementwise prologues. Work comes in steps of 256
+// consecutive octets of one row (segs steps per row); a step's row and
+// segment are workgroup-uniform, so the index arithmetic is scalar.
 template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
-    const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t total_oct) {
-  const int64_t oct_per_row = k >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
-    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
+    const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps) {
+  for (int64_t st = blockIdx.x; st < steps; st += gridDim.x) {
+    const int64_t row = st / segs;
+    const int64_t oct = (st - row * segs) * kThreads + threadIdx.x;
+    if (oct >= opr) continue;  // whole 32-blocks drop out: opr is a multiple of 4
     float v[8];
     load8<BF16>(x, row * ldx + oct * 8, v);
-    if (PRO == PRO_GELU) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
-    }
-    // the 4 octets of a 32-block are lanes 4q..4q+3 (oct_per_row and stride are multiples of 4)
-    uint32_t am = amax_bits8(v);
-    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
-    const uint32_t S = mx_scale(am);
-    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = mx_pack8(v, S);
+    prologue8<PRO>(v);
+    uint32_t S;
+    const uint32_t w = mx_block(v, S);
+    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = w;
     if ((oct & 3) == 0) scales[row * ld_scales + (oct >> 2)] = (uint8_t)S;
   }
 }
 
 // Panel layout: (panel of 256 rows, chunk of 128 elements) blocks of 256 x 16
-// octets, thread i owns octet i % 16 of row i / 16 % 256 in block i / 4096,
-// so its code word lands at byte 4 i and its block's scale byte at i / 4 --
-// every wave writes 256 contiguous code bytes. Rows past `rows` and
-// elements past k are padding: code 0, scale byte 127.
+// octets; octet i (= step * 256 + thread) is octet i % 16 of row i / 16 % 256
+// in block i / 4096, so its code word lands at byte 4 i and its block's scale
+// byte at i / 4 -- every wave writes 256 contiguous code bytes. A step lies
+// in one block, so panel and chunk are workgroup-uniform. Rows past `rows`
+// and elements past k are padding: code 0, scale byte 127.
 template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
     const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t nc, int64_t total_oct) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
-    const int64_t blk = i >> 12;
+    uint8_t* __restrict__ scales, int64_t nc, int64_t steps) {
+  for (int64_t st = blockIdx.x; st < steps; st += gridDim.x) {
+    const int64_t blk = st >> 4;
     const int64_t pnl = blk / nc, ch = blk - pnl * nc;
-    const int64_t row = pnl * 256 + ((i >> 4) & 255), e0 = ch * 128 + (i & 15) * 8;
+    const int64_t row = pnl * 256 + (int)((st & 15) << 4) + (int)(threadIdx.x >> 4);
+    const int64_t e0 = ch * 128 + (int)(threadIdx.x & 15) * 8;
+    const int64_t i = st * kThreads + threadIdx.x;
     // a 32-block's 4 octets share row and validity (k is a multiple of 32)
     const bool valid = row < rows && e0 < k;
     float v[8];
     if (valid) {
       load8<BF16>(x, row * ldx + e0, v);
-      if (PRO == PRO_GELU) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
-      }
+      prologue8<PRO>(v);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.f;
     }
-    uint32_t am = amax_bits8(v);
-    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
-    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
-    const uint32_t S = mx_scale(am);
-    reinterpret_cast<uint32_t*>(codes)[i] = valid ? mx_pack8(v, S) : 0u;
-    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(valid ? S : 127u);
+    uint32_t S;
+    const uint32_t w = mx_block(v, S);
+    reinterpret_cast<uint32_t*>(codes)[i] = valid ? w : 0u;
+    if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(valid ? S : 127u);
   }
 }
 
@@ -341,7 +394,6 @@ inline unsigned grid_for(int64_t work_items) {
 hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            int prologue, hipStream_t st) {
-  const int64_t total = rows * (k >> 3);
   if (prologue == PRO_RMSNORM) {
     if (x_bf16)
       quant_mx_rmsnorm_kernel<1><<<(unsigned)rows, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales);
@@ -349,17 +401,18 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
       quant_mx_rmsnorm_kernel<0><<<(unsigned)rows, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales);
     return hipGetLastError();
   }
-  const unsigned g = grid_for(total);
+  const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
+  const unsigned g = grid_for(steps * kThreads);
   if (prologue == PRO_GELU) {
     if (x_bf16)
-      quant_mx_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+      quant_mx_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
     else
-      quant_mx_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+      quant_mx_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
   } else {
     if (x_bf16)
-      quant_mx_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+      quant_mx_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
     else
-      quant_mx_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total);
+      quant_mx_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
   }
   return hipGetLastError();
 }
@@ -375,18 +428,18 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
       quant_mx_rmsnorm_panel_kernel<0><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc);
     return hipGetLastError();
   }
-  const int64_t total = panels * nc * 4096;
-  const unsigned g = grid_for(total);
+  const int64_t steps = panels * nc * 16;  // 256 octets per step, 16 steps per (panel, chunk) block
+  const unsigned g = grid_for(steps * kThreads);
   if (prologue == PRO_GELU) {
     if (x_bf16)
-      quant_mx_panel_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+      quant_mx_panel_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
     else
-      quant_mx_panel_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+      quant_mx_panel_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
   } else {
     if (x_bf16)
-      quant_mx_panel_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+      quant_mx_panel_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
     else
-      quant_mx_panel_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, total);
+      quant_mx_panel_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
   }
   return hipGetLastError();
 }

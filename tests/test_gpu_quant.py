@@ -6,7 +6,7 @@ import torch
 
 from fp4_quantized_diffusion_amd import inputs
 from oracle import mxfp4, nvfp4, rollout as orollout
-from tests._parity import mx_codes_near_boundary_ok, to_np
+from tests._parity import panel_to_rows, mx_codes_near_boundary_ok, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -146,6 +146,28 @@ def test_mx_prologues(gpu_lib, prologue, dtype):
     bad, flips = mx_codes_near_boundary_ok(ref, gc, gs)
     assert bad == 0, (bad, flips)
     assert flips <= 50
+
+
+@pytest.mark.parametrize("layout", ["row", "panel"])
+def test_mx_gelu_negative_tail(gpu_lib, layout):
+    """GELU blocks drawn from narrow bands of the negative tail ([-3.5, -2.5]
+    down to [-10, -7]): every block's scale and codes are then set by
+    z Phi(z) with Phi between 2e-4 and 1e-23, so they depend on Phi's
+    relative accuracy (1 + erf(z / sqrt 2) cancels there). Same 2e-6
+    decision band as the other fused-prologue tests."""
+    rng = np.random.default_rng(17)
+    rows, k = 512, 1024
+    bands = [(-3.5, -2.5), (-5.0, -3.5), (-7.0, -5.0), (-10.0, -7.0)]
+    x = np.empty((rows, k), np.float32)
+    for i, (lo, hi) in enumerate(bands):
+        x[i * rows // 4:(i + 1) * rows // 4] = rng.uniform(lo, hi, size=(rows // 4, k))
+    q = gpu_lib.quantize(torch.from_numpy(x).to(DEV), "mx", prologue="gelu", layout=layout)
+    if layout == "panel":
+        gc, gs, _ = panel_to_rows(to_np(q.codes), to_np(q.scales), rows, k)
+    else:
+        gc, gs = to_np(q.codes)[:, : k // 2], to_np(q.scales)[:, : k // 32]
+    bad, flips = mx_codes_near_boundary_ok(orollout.gelu(x.astype(np.float64)), gc, gs)
+    assert bad == 0, (bad, flips)
 
 
 def test_weight_requantization_full_flux(gpu_lib):
