@@ -367,62 +367,103 @@ constexpr int full_tile_vmem() { return 16 * (BF16OUT ? 2 : (RESID ? 8 : 4)); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// MFMA tiles are stored in the order t = 4 j + i (j: m block, i: n block),
+// so the two tiles i = 2k, 2k + 1 that share a 128-byte line of a bf16 row
+// are written back to back.
+__device__ __forceinline__ int64_t tile_offset(int t, int m_base, int n_base, int64_t ldc, int r32, int h) {
+  return (int64_t)(m_base + 32 * (t >> 2) + r32) * ldc + n_base + 32 * (t & 3) + 16 * h;
+}
+
+__device__ __forceinline__ void load_res16(float4 r[4], const float* src) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) r[g4] = reinterpret_cast<const float4*>(src)[g4];
+}
+
+template <int BF16OUT>
+__device__ __forceinline__ void store16(float o[16], void* c, int64_t off, bool rows16) {
+  if (BF16OUT) {
+    uint32_t wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)  // hardware round-to-nearest-even conversion
+      wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
+    if (rows16) {  // 16-byte aligned rows
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + off);
+      dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+    } else {       // rows only 8-byte aligned
+      uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = make_uint2(wv[2 * e], wv[2 * e + 1]);
+    }
+  } else {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + off);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) dst[g4] = make_float4(o[4 * g4], o[4 * g4 + 1], o[4 * g4 + 2], o[4 * g4 + 3]);
+  }
+}
+
 // FULL: the tile lies wholly inside C and rows are 16-byte aligned, so every
 // wave issues exactly full_tile_vmem() instructions and the pipeline can
-// count them instead of draining them. Otherwise element-wise tails at the
-// N edge and the caller drains the stores.
+// count them instead of draining them; the residual loads run two MFMA
+// tiles ahead of their use (three 16-register buffers in rotation), so one
+// memory round trip is exposed per tile, not one per MFMA tile. Otherwise
+// element-wise tails at the N edge and the caller drains the stores.
 template <int BF16OUT, int RESID, bool FULL>
 __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
                                            int64_t ldc, const float* residual) {
   const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+  if (FULL) {
+    float4 rq[3][4];
+    if (RESID) {
+      load_res16(rq[0], residual + tile_offset(0, m_base, n_base, ldc, r32, h));
+      load_res16(rq[1], residual + tile_offset(1, m_base, n_base, ldc, r32, h));
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int t = 0; t < 16; ++t) {
+      if (RESID && t + 2 < 16) load_res16(rq[(t + 2) % 3], residual + tile_offset(t + 2, m_base, n_base, ldc, r32, h));
       float o[16];
-      gather16(acc[i][j], o);
-      const int m = m_base + 32 * j + r32;
-      const int n = n_base + 32 * i + 16 * h;
-      if (!FULL && (m >= p.M || n >= p.N)) continue;
-      const int64_t off = (int64_t)m * ldc + n;
-      if (FULL || n + 16 <= p.N) {
-        if (RESID) {
+      gather16(acc[t & 3][t >> 2], o);
+      if (RESID) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 r4 = *reinterpret_cast<const float4*>(residual + off + 4 * g4);
-            o[4 * g4] += r4.x; o[4 * g4 + 1] += r4.y; o[4 * g4 + 2] += r4.z; o[4 * g4 + 3] += r4.w;
-          }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 r4 = rq[t % 3][g4];
+          o[4 * g4] += r4.x; o[4 * g4 + 1] += r4.y; o[4 * g4 + 2] += r4.z; o[4 * g4 + 3] += r4.w;
         }
-        if (BF16OUT) {
-          uint32_t wv[8];
+      }
+      store16<BF16OUT>(o, c, tile_offset(t, m_base, n_base, ldc, r32, h), true);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads' look-ahead at two tiles
+    }
+    return;
+  }
+  const bool rows16 = BF16OUT ? (ldc & 7) == 0 : true;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)  // hardware round-to-nearest-even conversion
-            wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
-          if (FULL || (ldc & 7) == 0) {  // 16-byte aligned rows
-            uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + off);
-            dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-            dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-          } else {                        // rows only 8-byte aligned
-            uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + off);
+  for (int t = 0; t < 16; ++t) {
+    float o[16];
+    gather16(acc[t & 3][t >> 2], o);
+    const int m = m_base + 32 * (t >> 2) + r32;
+    const int n = n_base + 32 * (t & 3) + 16 * h;
+    if (m >= p.M || n >= p.N) continue;
+    const int64_t off = (int64_t)m * ldc + n;
+    if (n + 16 <= p.N) {
+      if (RESID) {
+        float4 r[4];
+        load_res16(r, residual + off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = make_uint2(wv[2 * e], wv[2 * e + 1]);
-          }
-        } else {
-          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + off);
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) dst[g4] = make_float4(o[4 * g4], o[4 * g4 + 1], o[4 * g4 + 2], o[4 * g4 + 3]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          o[4 * g4] += r[g4].x; o[4 * g4 + 1] += r[g4].y; o[4 * g4 + 2] += r[g4].z; o[4 * g4 + 3] += r[g4].w;
         }
-      } else {
+      }
+      store16<BF16OUT>(o, c, off, rows16);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (n + e >= p.N) continue;
-          float x = o[e];
-          if (RESID) x += residual[off + e];
-          if (BF16OUT)
-            reinterpret_cast<__bf16*>(c)[off + e] = (__bf16)x;
-          else
-            reinterpret_cast<float*>(c)[off + e] = x;
-        }
+      for (int e = 0; e < 16; ++e) {
+        if (n + e >= p.N) continue;
+        float x = o[e];
+        if (RESID) x += residual[off + e];
+        if (BF16OUT)
+          reinterpret_cast<__bf16*>(c)[off + e] = (__bf16)x;
+        else
+          reinterpret_cast<float*>(c)[off + e] = x;
       }
     }
   }
