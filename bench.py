@@ -28,12 +28,14 @@ METRIC = "FP4 GEMM TFLOP/s (% of MI355X MXFP4 peak); FP4 rollout candidates/sec"
 PEAK_FP4 = 10.1e15      # MI355X dense MXFP4 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 
-# HBM bytes per GEMM launch from rocprofv3 FETCH_SIZE (x2, copy-calibrated)
-# and WRITE_SIZE (x1) runs of this workload, averaged over the two rollout
-# GEMMs; valid only for the kernel sources they were taken with (reported as
-# null once those change). See profiles/rollout_96x4096x3072_kernels.md.
-GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "9a0795501596d6af", "gemm_common.h": "d8952e405ad1a5b1"},
-                "bytes_per_launch": 26.1e9}
+# Bytes each GEMM launch moves between L2 and the memory fabric (Infinity
+# Cache or HBM), from rocprofv3 FETCH_SIZE (x2: every read request is
+# 128 bytes, which the counter's formula weighs as 64) and WRITE_SIZE (x1)
+# runs of this workload, averaged over the two rollout GEMMs; valid only for
+# the kernel sources they were taken with (reported as null once those
+# change). See profiles/rollout_96x4096x3072_kernels.md.
+GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "4915163ea7bfaaf7", "gemm_common.h": "d8952e405ad1a5b1"},
+                "bytes_per_launch": 22.84e9}
 
 
 def gemm_traffic():
@@ -173,6 +175,7 @@ def main():
     ap.add_argument("--no-rank-agreement", action="store_true")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
+    ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
@@ -197,7 +200,7 @@ def main():
     work = torch.empty_like(noise)
     timer = EventTimer()
     ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
-                    timer=timer, layout=args.layout)
+                    timer=timer, layout=args.layout, overlap=args.overlap)
 
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
@@ -223,9 +226,12 @@ def main():
     log(f"timed {args.steps} steps: {sec * 1e3:.1f} ms/step; top {top_l[:4]}... bottom {bottom_l[:4]}...")
 
     ks = timer.summary()
-    m_rows = chunk * cfg["tokens"]
-    gemm_flop = 2.0 * m_rows * cfg["dim"] * cfg["hidden"]
     n_gemm, gemm_ms = ks["gemm"]
+    # each step runs 2 GEMMs per block over all candidates; a launch covers
+    # the rows of one chunk, so price it by the step's FLOPs over its launches
+    step_flop = 2.0 * 2 * cfg["blocks"] * cfg["steps"] * cfg["n_cand"] * cfg["tokens"] * cfg["dim"] * cfg["hidden"]
+    gemm_flop = step_flop / (n_gemm / args.steps)
+    m_rows = int(round(gemm_flop / (2.0 * cfg["dim"] * cfg["hidden"])))
     achieved = gemm_flop / (gemm_ms * 1e-3)
     kernels = {k: {"launches_per_step": n // args.steps, "avg_us": round(ms * 1e3, 2)} for k, (n, ms) in ks.items()}
 
@@ -246,12 +252,12 @@ def main():
                                f"x{cfg['blocks']}blk_{cfg['steps']}step_top{cfg['k_top']}_bottom{cfg['k_bottom']}",
                    "n_cand": cfg["n_cand"], "tokens": cfg["tokens"], "dim": cfg["dim"], "hidden": cfg["hidden"],
                    "blocks": cfg["blocks"], "euler_steps": cfg["steps"], "chunk_candidates": chunk,
-                   "operand_layout": args.layout,
+                   "operand_layout": args.layout, "two_stream_overlap": args.overlap,
                    "gemm_shapes": [[m_rows, cfg["dim"], cfg["hidden"]], [m_rows, cfg["hidden"], cfg["dim"]]]},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_FP4 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4),
                      "traffic": (None if gemm_traffic() is None else round(gemm_traffic() / 1e9, 2)),
-                     "traffic_unit": "GB per launch (HBM reads + writes, rocprofv3 counters)",
+                     "traffic_unit": "GB per launch (L2 <-> fabric reads + writes, rocprofv3 counters)",
                      "kernel": f"gemm_mx_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate)",
                      "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "gemm_tflops": round(achieved / 1e12, 2),

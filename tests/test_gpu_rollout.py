@@ -68,3 +68,29 @@ def test_panel_and_row_layouts_agree_bitwise(gpu_lib):
         outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n_cand", [2, 5])
+def test_two_stream_schedule_matches_one_stream(gpu_lib, n_cand):
+    """The two-stream schedule (GEMMs and quantizers of the two halves
+    overlapped through device-side events) reproduces the one-stream
+    schedule bit for bit: every kernel's rows are independent of chunking.
+    Odd candidate counts give unequal halves; 300 tokens give ragged panels."""
+    seed, tokens, dim, hidden = 6, 300, 256, 1024
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
+    u = torch.from_numpy(inputs.reward_vector(seed, dim)).to(DEV)
+    w1 = [torch.from_numpy(w[0]).to(DEV).bfloat16() for w in ws]
+    w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
+    outs = []
+    for overlap in (True, False):
+        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, overlap=overlap)
+        nd = torch.from_numpy(noise).to(DEV)
+        work = torch.empty_like(nd)
+        for _ in range(2):  # a second run reuses every buffer
+            r, top, bottom, rn = ro.run(nd, work)
+        torch.cuda.synchronize()
+        outs.append((to_np(work), to_np(r), to_np(top), to_np(bottom), to_np(rn), to_np(nd)))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(outs[0][5], noise)  # noise left intact
