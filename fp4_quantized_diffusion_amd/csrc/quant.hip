@@ -57,7 +57,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8])
 // (fp32 emulation of this sequence against float64 erfc). |z| is clamped at
 // 16, where Q is below fp32's range (Phi is then 0 or 1).
 #define FP4R_L2E(c) ((float)((c) * 1.4426950408889634))
-__device__ __forceinline__ float gelu_erfc(float z) {
+__device__ __forceinline__ float phi_erfc(float z) {
   constexpr float kHalfLog2eHi = -0.7213475f;     // -log2(e) / 2, high part
   constexpr float kHalfLog2eLo = -9.629815e-09f;  // and the rest
   constexpr float kLn2 = 0.693147180559945309f;
@@ -82,9 +82,38 @@ __device__ __forceinline__ float gelu_erfc(float z) {
   float es = __builtin_amdgcn_exp2f(y);
   es = fmaf(es * e, kLn2, es);                     // exp2(y + e) ~ exp2(y) (1 + e ln 2)
   const float q = t * (eph * es);
-  return z * (z < 0.0f ? q : 1.0f - q);
+  return z < 0.0f ? q : 1.0f - q;
 }
 #undef FP4R_L2E
+
+__device__ __forceinline__ float gelu_erfc(float z) { return z * phi_erfc(z); }
+
+// GELU of a bf16 input through a table of Phi. A bf16 value has 8
+// significant bits, so the magnitudes 2^-22 .. 16 are 26 binades of 128
+// values plus 16 itself: 3329 entries per sign (26 KiB in LDS), holding
+// phi_erfc of exactly those values. z * tab[z] is then bit-identical to
+// gelu_erfc(z) for 2^-22 <= |z| <= 16, and beyond 16 too, because phi_erfc
+// clamps |z| at 16. Below 2^-22 the index clamps to the 2^-22 entry: Phi
+// there differs from Phi(z) by less than 0.4 * 2^-22 (2e-7 relative).
+constexpr uint32_t kGeluLo = (127u - 22u) << 7;  // bf16 magnitude bits of 2^-22
+constexpr uint32_t kGeluHi = (127u + 4u) << 7;   // and of 16
+constexpr uint32_t kGeluSpan = kGeluHi - kGeluLo + 1;
+constexpr int kGeluTab = 2 * (int)kGeluSpan;
+
+__device__ __forceinline__ void gelu_table_fill(float* tab) {
+  for (int e = threadIdx.x; e < kGeluTab; e += blockDim.x) {
+    const uint32_t sgn = (uint32_t)e >= kGeluSpan ? 1u : 0u;
+    const uint32_t mag = kGeluLo + (uint32_t)e - sgn * kGeluSpan;
+    tab[e] = phi_erfc(__uint_as_float(((sgn << 15) | mag) << 16));
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float gelu_bf16(float z, const float* tab) {
+  const uint32_t b = __float_as_uint(z) >> 16;  // z is a bf16 value: no bits are lost
+  const uint32_t m = min(max(b & 0x7FFFu, kGeluLo), kGeluHi);
+  return z * tab[m - kGeluLo + (b >> 15) * kGeluSpan];
+}
 
 __device__ __forceinline__ uint32_t amax_bits8(const float v[8]) {
   uint32_t m = 0;
@@ -128,14 +157,28 @@ __device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
   return w;
 }
 
-// Elementwise prologue of one loaded octet.
-template <int PRO>
-__device__ __forceinline__ void prologue8(float v[8]) {
+// Elementwise prologue of one loaded octet (tab: the GELU table, bf16 input).
+template <int BF16, int PRO>
+__device__ __forceinline__ void prologue8(float v[8], const float* tab) {
   if (PRO == PRO_GELU) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = gelu_erfc(v[j]);
+    for (int j = 0; j < 8; ++j) v[j] = BF16 ? gelu_bf16(v[j], tab) : gelu_erfc(v[j]);
   }
 }
+
+// LDS for the GELU table when the kernel needs it (bf16 input, GELU).
+template <int BF16, int PRO>
+struct GeluLds {
+  __device__ __forceinline__ float* get() { return nullptr; }
+};
+template <>
+struct GeluLds<1, PRO_GELU> {
+  __device__ __forceinline__ float* get() {
+    __shared__ float tab[kGeluTab];
+    gelu_table_fill(tab);
+    return tab;
+  }
+};
 
 // Block scale of a 32-block held as 4 octets in lanes 4q..4q+3, and the
 // octet's code word.
@@ -147,6 +190,11 @@ __device__ __forceinline__ uint32_t mx_block(const float v[8], uint32_t& S) {
   return mx_pack8(v, S);
 }
 
+// Steps a thread works on at once in the elementwise kernels: their loads
+// are all issued before the first is used, so each wave keeps four 16-byte
+// loads per lane in flight.
+constexpr int kUnroll = 4;
+
 // Row-major layout, elementwise prologues. Work comes in steps of 256
 // consecutive octets of one row (segs steps per row); a step's row and
 // segment are workgroup-uniform, so the index arithmetic is scalar.
@@ -154,17 +202,31 @@ template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
     const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps) {
-  for (int64_t st = blockIdx.x; st < steps; st += gridDim.x) {
-    const int64_t row = st / segs;
-    const int64_t oct = (st - row * segs) * kThreads + threadIdx.x;
-    if (oct >= opr) continue;  // whole 32-blocks drop out: opr is a multiple of 4
-    float v[8];
-    load8<BF16>(x, row * ldx + oct * 8, v);
-    prologue8<PRO>(v);
-    uint32_t S;
-    const uint32_t w = mx_block(v, S);
-    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = w;
-    if ((oct & 3) == 0) scales[row * ld_scales + (oct >> 2)] = (uint8_t)S;
+  const float* tab = GeluLds<BF16, PRO>().get();
+  const int64_t G = gridDim.x;
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
+    float v[kUnroll][8];
+    int64_t row[kUnroll], oct[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t st = st0 + u * G;
+      row[u] = st / segs;
+      oct[u] = (st - row[u] * segs) * kThreads + threadIdx.x;
+      // unconditional loads (an idle lane reads the first octet), so that
+      // all of them are in flight before the first is waited for
+      const bool ok = st < steps && oct[u] < opr;
+      load8<BF16>(x, ok ? row[u] * ldx + oct[u] * 8 : 0, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      // whole 32-blocks drop out: opr is a multiple of 4
+      if (st0 + u * G >= steps || oct[u] >= opr) continue;
+      prologue8<BF16, PRO>(v[u], tab);
+      uint32_t S;
+      const uint32_t w = mx_block(v[u], S);
+      *reinterpret_cast<uint32_t*>(codes + row[u] * ld_codes + oct[u] * 4) = w;
+      if ((oct[u] & 3) == 0) scales[row[u] * ld_scales + (oct[u] >> 2)] = (uint8_t)S;
+    }
   }
 }
 
@@ -178,26 +240,37 @@ template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
     const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t nc, int64_t steps) {
-  for (int64_t st = blockIdx.x; st < steps; st += gridDim.x) {
-    const int64_t blk = st >> 4;
-    const int64_t pnl = blk / nc, ch = blk - pnl * nc;
-    const int64_t row = pnl * 256 + (int)((st & 15) << 4) + (int)(threadIdx.x >> 4);
-    const int64_t e0 = ch * 128 + (int)(threadIdx.x & 15) * 8;
-    const int64_t i = st * kThreads + threadIdx.x;
-    // a 32-block's 4 octets share row and validity (k is a multiple of 32)
-    const bool valid = row < rows && e0 < k;
-    float v[8];
-    if (valid) {
-      load8<BF16>(x, row * ldx + e0, v);
-      prologue8<PRO>(v);
-    } else {
+  const float* tab = GeluLds<BF16, PRO>().get();
+  const int64_t G = gridDim.x;
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
+    float v[kUnroll][8];
+    bool valid[kUnroll];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t st = st0 + u * G;
+      const int64_t blk = st >> 4;
+      const int64_t pnl = blk / nc, ch = blk - pnl * nc;
+      const int64_t row = pnl * 256 + (int)((st & 15) << 4) + (int)(threadIdx.x >> 4);
+      const int64_t e0 = ch * 128 + (int)(threadIdx.x & 15) * 8;
+      // a 32-block's 4 octets share row and validity (k is a multiple of 32)
+      valid[u] = st < steps && row < rows && e0 < k;
+      // unconditional loads (an idle lane reads the first octet), so that
+      // all of them are in flight before the first is waited for
+      load8<BF16>(x, valid[u] ? row * ldx + e0 : 0, v[u]);
     }
-    uint32_t S;
-    const uint32_t w = mx_block(v, S);
-    reinterpret_cast<uint32_t*>(codes)[i] = valid ? w : 0u;
-    if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(valid ? S : 127u);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t st = st0 + u * G;
+      if (st >= steps) continue;  // workgroup-uniform
+      prologue8<BF16, PRO>(v[u], tab);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[u][j] = valid[u] ? v[u][j] : 0.f;
+      uint32_t S;
+      const uint32_t w = mx_block(v[u], S);
+      const int64_t i = st * kThreads + threadIdx.x;
+      reinterpret_cast<uint32_t*>(codes)[i] = valid[u] ? w : 0u;
+      if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(valid[u] ? S : 127u);
+    }
   }
 }
 
@@ -389,6 +462,28 @@ inline unsigned grid_for(int64_t work_items) {
   return (unsigned)g;
 }
 
+// Grid of an elementwise kernel over `steps` workgroup steps, kUnroll per
+// workgroup pass. A kernel that first fills an LDS table is instead given
+// exactly as many workgroups as fit on the GPU at once (each then walks its
+// share of the steps), so the table is filled once per resident workgroup.
+template <class Kernel>
+unsigned elementwise_grid(Kernel kernel, int64_t steps, bool table) {
+  unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
+  if (!table) return g;
+  static int resident = 0;  // per kernel instantiation
+  if (resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || cus <= 0 ||
+        per_cu <= 0)
+      resident = 1024;
+    else
+      resident = cus * per_cu;
+  }
+  return g < (unsigned)resident ? g : (unsigned)resident;
+}
+
 }  // namespace
 
 hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
@@ -402,18 +497,17 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
     return hipGetLastError();
   }
   const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
-  const unsigned g = grid_for(steps * kThreads);
+#define FP4R_LAUNCH(B, P, TAB)                                                                             \
+  quant_mx_kernel<B, P><<<elementwise_grid(quant_mx_kernel<B, P>, steps, TAB), kThreads, 0, st>>>(         \
+      x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps)
   if (prologue == PRO_GELU) {
-    if (x_bf16)
-      quant_mx_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
-    else
-      quant_mx_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
+    if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
+    else FP4R_LAUNCH(0, PRO_GELU, false);
   } else {
-    if (x_bf16)
-      quant_mx_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
-    else
-      quant_mx_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps);
+    if (x_bf16) FP4R_LAUNCH(1, PRO_NONE, false);
+    else FP4R_LAUNCH(0, PRO_NONE, false);
   }
+#undef FP4R_LAUNCH
   return hipGetLastError();
 }
 
@@ -429,18 +523,17 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
     return hipGetLastError();
   }
   const int64_t steps = panels * nc * 16;  // 256 octets per step, 16 steps per (panel, chunk) block
-  const unsigned g = grid_for(steps * kThreads);
+#define FP4R_LAUNCH(B, P, TAB)                                                                             \
+  quant_mx_panel_kernel<B, P><<<elementwise_grid(quant_mx_panel_kernel<B, P>, steps, TAB), kThreads, 0, st>>>( \
+      x, rows, k, ldx, codes, scales, nc, steps)
   if (prologue == PRO_GELU) {
-    if (x_bf16)
-      quant_mx_panel_kernel<1, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
-    else
-      quant_mx_panel_kernel<0, PRO_GELU><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
+    if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
+    else FP4R_LAUNCH(0, PRO_GELU, false);
   } else {
-    if (x_bf16)
-      quant_mx_panel_kernel<1, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
-    else
-      quant_mx_panel_kernel<0, PRO_NONE><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc, steps);
+    if (x_bf16) FP4R_LAUNCH(1, PRO_NONE, false);
+    else FP4R_LAUNCH(0, PRO_NONE, false);
   }
+#undef FP4R_LAUNCH
   return hipGetLastError();
 }
 

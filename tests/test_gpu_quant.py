@@ -170,6 +170,27 @@ def test_mx_gelu_negative_tail(gpu_lib, layout):
     assert bad == 0, (bad, flips)
 
 
+@pytest.mark.parametrize("layout", ["row", "panel"])
+def test_mx_gelu_every_bf16_value(gpu_lib, layout):
+    """Fused GELU on bf16 input over every finite bf16 value: 32-blocks of
+    consecutive bit patterns (one binade and sign per block) cover both
+    signs from the smallest subnormal to the largest finite value, i.e. the
+    small-argument, tabulated and large-argument branches of the bf16 GELU.
+    Same 2e-6 decision band as the other fused-prologue tests."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    vals = (bits << 16).view(np.float32).copy()
+    vals[~finite] = 0.0
+    x = vals.reshape(512, 128)
+    q = gpu_lib.quantize(torch.from_numpy(x).to(DEV).to(torch.bfloat16), "mx", prologue="gelu", layout=layout)
+    if layout == "panel":
+        gc, gs, _ = panel_to_rows(to_np(q.codes), to_np(q.scales), 512, 128)
+    else:
+        gc, gs = to_np(q.codes)[:, :64], to_np(q.scales)[:, :4]
+    bad, flips = mx_codes_near_boundary_ok(orollout.gelu(x.astype(np.float64)), gc, gs)
+    assert bad == 0, (bad, flips)
+
+
 def test_weight_requantization_full_flux(gpu_lib):
     """FLUX-class W1 [12288, 3072] bf16, full size: bit-exact on sampled rows."""
     _, w = inputs.class_linear("flux", 1, rows=8)
