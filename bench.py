@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP4 GEMM TFLOP/s (% of MI355X MXFP4 peak); FP4 rollout candidates/sec"
 PEAK_FP4 = 10.1e15      # MI355X dense MXFP4 MFMA, FLOP/s
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 
 # Bytes each GEMM launch moves between L2 and the memory fabric (Infinity
@@ -165,6 +166,96 @@ def cpu_baseline(cfg, tokens_sample=32, w_rows_sample=256):
                        f"os.cpu_count()={os.cpu_count()}")}
 
 
+def time_launches(fns, reps=50, warm_ms=100.0):
+    """Median / p10 / p90 (microseconds) of one launch, from a HIP event pair
+    around each call on the current stream. fns: one callable per rotating
+    input set (called round-robin). Warm-up runs for about warm_ms first, so
+    the timed launches see the clock the card settles at under this load."""
+    import torch
+    fns[0]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < warm_ms or i < 2 * len(fns):
+        fns[i % len(fns)]()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fns[i % len(fns)]()
+        e.record()
+        ev.append((s, e))
+    torch.cuda.synchronize()
+    us = np.sort(np.array([s.elapsed_time(e) * 1e3 for s, e in ev]))
+    return float(np.median(us)), float(np.percentile(us, 10)), float(np.percentile(us, 90))
+
+
+def class_benchmarks(dev, n_sets=4):
+    """The FLUX.1-, SANA- and SD3.5-L-class linears at full size: MXFP4 GEMM
+    (panel operands, bf16 C, operands pre-quantized) against torch's bf16
+    GEMM (F.linear) on the same shapes, plus the quantizers' bandwidth and
+    the NVFP4-style GEMM on the FLUX shapes. n_sets input sets rotate so that
+    the Infinity Cache cannot hold the operands between launches."""
+    import torch
+    import torch.nn.functional as F
+    import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd import inputs
+
+    def rate(flop, us, peak):
+        return {"tflops": round(flop / us / 1e6, 1), "frac_of_peak": round(flop / us / 1e-6 / peak, 4)}
+
+    gemms, mem = {}, {}
+    for name in ("flux", "sana", "sd35"):
+        for which in (1, 2):
+            t0 = time.time()
+            draws = [inputs.class_linear_device(name, which, dev, draw=d) for d in range(n_sets)]
+            m, k = draws[0][0].shape
+            n = draws[0][1].shape[0]
+            qa = [fq.quantize(a, "mx", layout="panel") for a, _ in draws]
+            qb = [fq.quantize(w, "mx", layout="panel") for _, w in draws]
+            c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            flop = 2.0 * m * n * k
+            key = f"{name}_{'qkv_or_up' if which == 1 else 'down'}_{m}x{k}x{n}"
+            f_us = time_launches([lambda i=i: fq.gemm(qa[i], qb[i], "bf16", out=c) for i in range(n_sets)])
+            b_us = time_launches([lambda i=i: F.linear(draws[i][0], draws[i][1]) for i in range(n_sets)])
+            g = {"m": m, "k": k, "n": n,
+                 "mxfp4_us": [round(v, 1) for v in f_us], **{"mxfp4_" + a: b for a, b in
+                                                            rate(flop, f_us[0], PEAK_FP4).items()},
+                 "bf16_us": [round(v, 1) for v in b_us], **{"bf16_" + a: b for a, b in
+                                                           rate(flop, b_us[0], PEAK_BF16).items()},
+                 "mxfp4_speedup_vs_bf16": round(b_us[0] / f_us[0], 3)}
+            # activation re-quantization (panel layout, bf16 in): 2 + 0.5 + 1/32 bytes per element
+            q_us = time_launches([lambda i=i: fq.quantize(draws[i][0], "mx", out=qa[i]) for i in range(n_sets)])
+            mem[f"mx_quantize_act_{name}_{m}x{k}"] = {"us": [round(v, 1) for v in q_us],
+                                                      "tbps": round(m * k * 2.53125 / q_us[0] / 1e6, 3),
+                                                      "frac_of_hbm": round(m * k * 2.53125 / q_us[0] / 1e-6 / PEAK_HBM, 4)}
+            if name == "flux":
+                qn_a = [fq.quantize(a, "nv") for a, _ in draws]
+                qn_b = [fq.quantize(w, "nv") for _, w in draws]
+                nv_us = time_launches([lambda i=i: fq.gemm(qn_a[i], qn_b[i], "bf16", out=c) for i in range(n_sets)])
+                g.update({"nvfp4_us": [round(v, 1) for v in nv_us],
+                          **{"nvfp4_" + a + "_bf16_peak": b for a, b in rate(flop, nv_us[0], PEAK_BF16).items()}})
+                # two passes: tensor amax (2 B/elem), then codes + E4M3 scales (2 + 0.5 + 1/16)
+                nq_us = time_launches([lambda i=i: fq.quantize(draws[i][0], "nv", out=qn_a[i]) for i in range(n_sets)])
+                mem[f"nv_quantize_act_{name}_{m}x{k}"] = {"us": [round(v, 1) for v in nq_us],
+                                                          "tbps": round(m * k * 4.5625 / nq_us[0] / 1e6, 3),
+                                                          "frac_of_hbm": round(m * k * 4.5625 / nq_us[0] / 1e-6 / PEAK_HBM, 4)}
+                wq_us = time_launches([lambda i=i: fq.quantize(draws[i][1], "mx", out=qb[i]) for i in range(n_sets)])
+                mem[f"mx_quantize_weight_{name}_{n}x{k}"] = {"us": [round(v, 1) for v in wq_us],
+                                                             "tbps": round(n * k * 2.53125 / wq_us[0] / 1e6, 3)}
+                del qn_a, qn_b
+            gemms[key] = g
+            log(f"class {key}: mxfp4 {f_us[0]:.0f} us ({g['mxfp4_tflops']} TF/s), bf16 {b_us[0]:.0f} us "
+                f"({g['bf16_tflops']} TF/s) [{time.time() - t0:.1f}s]")
+            del draws, qa, qb, c
+            torch.cuda.empty_cache()
+    return gemms, mem
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +264,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="candidates per network pass (0 = all 96)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-agreement", action="store_true")
+    ap.add_argument("--no-class-gemms", action="store_true",
+                    help="skip the FLUX/SANA/SD3.5-class GEMM, bf16 baseline and quantizer timings")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
@@ -264,6 +357,10 @@ def main():
         "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),
         "kernels": kernels,
     }
+    if not args.no_class_gemms:
+        t0 = time.time()
+        out["class_gemms"], out["memory_kernels"] = class_benchmarks(dev)
+        log(f"class benchmarks: {time.time() - t0:.1f}s")
     if not args.no_rank_agreement:
         try:
             t0 = time.time()

@@ -51,17 +51,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int KSTAGE_B = 64;  // code bytes per row per K stage (128 elements)
-constexpr int SCB = 4;        // scale bytes per row per K stage
+constexpr int SCB = 4;        // MX scale bytes per row per K stage
+constexpr int SCB_NV = 8;     // NVFP4-style scale bytes per row per K stage
 constexpr int NBUF = 4;       // LDS stage buffers
 
 // One K stage in LDS. The buffers are separate objects, so the compiler can
 // see that reading one never depends on the loads in flight into another.
-struct __attribute__((aligned(16))) StageMx {
+template <int SCBY>
+struct __attribute__((aligned(16))) StageT {
   uint8_t a[BM * KSTAGE_B];
   uint8_t b[BN * KSTAGE_B];
-  uint8_t as[BM * SCB];
-  uint8_t bs[BN * SCB];
+  uint8_t as[BM * SCBY];
+  uint8_t bs[BN * SCBY];
 };
+typedef StageT<SCB> StageMx;
 
 // 16-byte chunk c (0..3) of row r lives at position c ^ ((r >> 2) & 3): the
 // 16 rows of a fragment read then cover every (r % 4, position) pair, i.e.
@@ -73,11 +76,16 @@ enum Layout {
   LD_ROW_BYTE = 0,  // row-major, scale rows of any alignment (bytes through registers)
   LD_ROW_WORD = 1,  // row-major, scale rows 4-byte aligned (direct word loads)
   LD_PANEL = 2,     // panel layout
+  LD_NV = 3,        // NVFP4-style, row-major, scale rows 4-byte aligned (direct word loads)
 };
+
+template <int LD>
+using Stage = StageT<LD == LD_NV ? SCB_NV : SCB>;
 
 // Problem description shared by every step.
 struct Problem {
   const uint8_t *a, *as, *b, *bs;
+  const float *a_ts, *b_ts;        // NVFP4-style tensor scales
   int64_t lda, ld_as, ldb, ld_bs;  // row-major layouts
   int M, N, kbytes, nblk;
   int nkc;                         // K chunks of 128 elements (stages per tile)
@@ -90,10 +98,15 @@ constexpr int kPanelScaleBlock = BM * SCB;      // 1 KiB: its scale block
 // This thread's share of a stage load, independent of the tile: code chunk
 // offsets for its 4 code loads per operand (wave w's load `it` fills LDS rows
 // 16 (4 w + it) .. +15; lane L writes position L % 4 of row
-// 16 (4 w + it) + L / 4) and its scale row (row t).
+// 16 (4 w + it) + L / 4) and its scale row (row t). NVFP4-style stages have
+// 8 scale bytes per row, loaded as two 4-byte words per thread: word j of
+// wave w's lane L is word L % 2 of row 128 j + 32 w + L / 2, so each load of
+// a wave fills 256 contiguous LDS bytes in row order (sa2 / sb2: the second
+// load's offsets).
 struct LaneOffsets {
   uint32_t ca[4], cb[4];
   uint32_t sa, sb;
+  uint32_t sa2, sb2;
 };
 
 template <int LD>
@@ -108,6 +121,14 @@ __device__ __forceinline__ void make_lane_offsets(LaneOffsets& o, const Problem&
   }
   o.sa = (uint32_t)(threadIdx.x * (LD == LD_PANEL ? SCB : p.ld_as));
   o.sb = (uint32_t)(threadIdx.x * (LD == LD_PANEL ? SCB : p.ld_bs));
+  o.sa2 = o.sb2 = 0;
+  if (LD == LD_NV) {
+    const int r = w * 32 + (lane >> 1), wo = (lane & 1) * 4;
+    o.sa = (uint32_t)(r * p.ld_as + wo);
+    o.sb = (uint32_t)(r * p.ld_bs + wo);
+    o.sa2 = (uint32_t)((r + 128) * p.ld_as + wo);
+    o.sb2 = (uint32_t)((r + 128) * p.ld_bs + wo);
+  }
 }
 
 // Buffer resources of one tile's operands (uniform, in SGPRs). Loads past
@@ -151,9 +172,33 @@ __device__ __forceinline__ TileDesc make_desc(const Problem& p, int pid) {
 // store_scale_regs(). Panel layout: stage st is block st of the panel, and
 // stages past the last chunk read as zero codes with zero scale bytes.
 template <int LD>
-__device__ __forceinline__ void issue_stage(StageMx& dst, const Problem& p, const LaneOffsets& o, const TileDesc& d,
+__device__ __forceinline__ void issue_stage(Stage<LD>& dst, const Problem& p, const LaneOffsets& o, const TileDesc& d,
                                             int st, uint32_t sc[8]) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (LD == LD_NV) {
+    // codes as in the row-major MX layout; scale bytes st*8 .. st*8+7 of
+    // each row as two words (bytes past the row's blocks are masked when
+    // the fragments are read)
+    const int lane = threadIdx.x & 63;
+    const int kb = st * KSTAGE_B, kblk = st * SCB_NV;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = (w * 4 + it) * 16 + (lane >> 2);
+      const bool kin = kb + swz(r, lane & 3) * 16 < p.kbytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, (lds_ptr_t)(dst.a + (w * 4 + it) * 1024), 16,
+                                               kin ? o.ca[it] : kOob, kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, (lds_ptr_t)(dst.b + (w * 4 + it) * 1024), 16,
+                                               kin ? o.cb[it] : kOob, kb, 0, 0);
+    }
+    const bool in = kblk + (lane & 1) * 4 < p.nblk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.as, (lds_ptr_t)(dst.as + w * 256), 4, in ? o.sa : kOob, kblk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.as, (lds_ptr_t)(dst.as + 1024 + w * 256), 4, in ? o.sa2 : kOob, kblk,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.bs, (lds_ptr_t)(dst.bs + w * 256), 4, in ? o.sb : kOob, kblk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.bs, (lds_ptr_t)(dst.bs + 1024 + w * 256), 4, in ? o.sb2 : kOob, kblk,
+                                             0, 0);
+    return;
+  }
   if (LD == LD_PANEL) {
     const bool in = st < p.nkc;  // uniform
     const int cboff = st * kPanelCodeBlock, sboff = st * kPanelScaleBlock;
@@ -197,7 +242,8 @@ __device__ __forceinline__ void issue_stage(StageMx& dst, const Problem& p, cons
   }
 }
 
-__device__ __forceinline__ void store_scale_regs(StageMx& dst, const uint32_t sc[8]) {
+template <class St>
+__device__ __forceinline__ void store_scale_regs(St& dst, const uint32_t sc[8]) {
   *reinterpret_cast<uint32_t*>(&dst.as[threadIdx.x * SCB]) = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
   *reinterpret_cast<uint32_t*>(&dst.bs[threadIdx.x * SCB]) = sc[4] | (sc[5] << 8) | (sc[6] << 16) | (sc[7] << 24);
 }
@@ -232,9 +278,12 @@ template <int N>
 __device__ __forceinline__ void wait_barrier() {
   if constexpr (N == 20) FP4R_WAIT_BARRIER(20);
   else if constexpr (N == 30) FP4R_WAIT_BARRIER(30);
+  else if constexpr (N == 24) FP4R_WAIT_BARRIER(24);
   else if constexpr (N == 32) FP4R_WAIT_BARRIER(32);
+  else if constexpr (N == 36) FP4R_WAIT_BARRIER(36);
   else if constexpr (N == 48) FP4R_WAIT_BARRIER(48);
   else if constexpr (N == 52) FP4R_WAIT_BARRIER(52);
+  else if constexpr (N == 56) FP4R_WAIT_BARRIER(56);
   else if constexpr (N == 63) FP4R_WAIT_BARRIER(63);
   else static_assert(N < 0, "add this vmcnt value");
 }
@@ -246,8 +295,8 @@ struct Frags {
   v8i w0[4], x0[4], w1[4], x1[4];
 };
 
-template <int KS>
-__device__ __forceinline__ void read_codes(const StageMx& cur, int rn0, int rm0, int h, v8i fw[4], v8i fx[4]) {
+template <int KS, class St>
+__device__ __forceinline__ void read_codes(const St& cur, int rn0, int rm0, int h, v8i fw[4], v8i fx[4]) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int rn = rn0 + f * 32, rm = rm0 + f * 32;
@@ -258,10 +307,32 @@ __device__ __forceinline__ void read_codes(const StageMx& cur, int rn0, int rm0,
   }
 }
 
+// NVFP4-style: the lane's four scale bytes (blocks 4h .. 4h+3 of stage st,
+// i.e. those of its chunks 2h and 2h+1) with blocks past the end set to 0.
+// The GEMM multiplies every code by its block's scale, so a zero scale
+// makes the (zero) codes past K and whatever lies in the row padding
+// contribute exactly nothing.
+__device__ __forceinline__ int clean_scales_nv(int v, int st, int nblk, int h) {
+  const int b0 = st * SCB_NV + 4 * h;
+  if (b0 + 4 <= nblk) return v;
+  if (b0 >= nblk) return 0;
+  return (int)((uint32_t)v & ((1u << (8 * (nblk - b0))) - 1u));
+}
+
 // Panel layout: the padding scale bytes are 127 and stages past the last
 // chunk read as zero, so no byte needs replacing.
 template <int LD>
-__device__ __forceinline__ void read_stage(const StageMx& cur, int st, int nblk, int rn0, int rm0, int h, Frags& f) {
+__device__ __forceinline__ void read_stage(const Stage<LD>& cur, int st, int nblk, int rn0, int rm0, int h, Frags& f) {
+  if (LD == LD_NV) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f.sw[q] = clean_scales_nv(*reinterpret_cast<const int*>(&cur.bs[(rn0 + q * 32) * SCB_NV + 4 * h]), st, nblk, h);
+      f.sx[q] = clean_scales_nv(*reinterpret_cast<const int*>(&cur.as[(rm0 + q * 32) * SCB_NV + 4 * h]), st, nblk, h);
+    }
+    read_codes<0>(cur, rn0, rm0, h, f.w0, f.x0);
+    read_codes<1>(cur, rn0, rm0, h, f.w1, f.x1);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int vw = *reinterpret_cast<const uint16_t*>(&cur.bs[(rn0 + q * 32) * SCB + 2 * h]);
@@ -288,6 +359,71 @@ __device__ __forceinline__ void mfma_stage(v16f acc[4][4], const Frags& f) {
                                                                   f.sx[j]);
 }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+// Block scale byte `B` (an E4M3 value; gfx950's FP8 is OCP E4M3FN) of a
+// lane's four, as an f16 pair (s, s). The conversion is exact (E4M3 values
+// are f16 values).
+template <int B>
+__device__ __forceinline__ h2v scale_pair(int sw) {
+  constexpr uint32_t sel = (B << 24) | (B << 16) | (B << 8) | B;  // byte B into all four bytes
+  const uint32_t dup = __builtin_amdgcn_perm((uint32_t)sw, (uint32_t)sw, sel);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dup, 1.0f, false);
+}
+
+// 8 E2M1 codes (one word, element 2p in the low nibble of byte p) times
+// their block scale, as f16: the scaled convert gives the codes' values
+// exactly (its scale operand is 1), and each product code x E4M3 has at
+// most 6 significant bits between 2^-10 and 2688, so the f16 multiply is
+// exact too.
+__device__ __forceinline__ h8v dequant_nv(uint32_t w, h2v s) {
+  const h2v q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const h2v q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const h2v q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const h2v q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return h8v{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
+// NVFP4-style stage on V_MFMA_F32_32X32X16_F16. Chunk 2h + KS of lane half
+// h (32 elements, 16 bytes) feeds four K steps: step ks takes its word ks
+// (elements 8 ks .. 8 ks + 7, block 2 KS + ks / 2 of the lane's four), so a
+// 16-element MFMA K step pairs word ks of chunk KS (lanes 0..31) with word ks
+// of chunk 2 + KS (lanes 32..63) -- one K permutation, the same for both
+// operands. The accumulator layout is that of the FP4 MFMA.
+template <int KS>
+__device__ __forceinline__ void mfma_half_nv(v16f acc[4][4], const v8i fw[4], const v8i fx[4], const int sw[4],
+                                             const int sx[4]) {
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {  // the chunk's two scale blocks
+    h2v swp[4], sxp[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      swp[q] = hb ? scale_pair<2 * KS + 1>(sw[q]) : scale_pair<2 * KS>(sw[q]);
+      sxp[q] = hb ? scale_pair<2 * KS + 1>(sx[q]) : scale_pair<2 * KS>(sx[q]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ks = 2 * hb + kk;
+      h8v a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = dequant_nv((uint32_t)fw[q][ks], swp[q]);
+        b[q] = dequant_nv((uint32_t)fx[q][ks], sxp[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_stage_nv(v16f acc[4][4], const Frags& f) {
+  mfma_half_nv<0>(acc, f.w0, f.x0, f.sw, f.sx);
+  mfma_half_nv<1>(acc, f.w1, f.x1, f.sw, f.sx);
+}
+
 // One pipeline step. On entry `cur` holds stage st's fragments (registers),
 // buffer `nxt` holds or is receiving the stream's next stage, and `own` --
 // the buffer stage st was read from -- is free once every wave is past this
@@ -298,12 +434,17 @@ __device__ __forceinline__ void mfma_stage(v16f acc[4][4], const Frags& f) {
 // st1: within-tile index of the next stage.
 // after_epi: the previous tile's epilogue issued exactly EPI vector-memory
 // instructions after the stages now in flight (they count in vmcnt too).
+// Vector-memory instructions per wave per stage: 8 code loads plus the
+// scale loads (2 words; 4 for NVFP4-style; 8 bytes through registers).
+template <int LD>
+constexpr int stage_vmem() { return LD == LD_NV ? 12 : (LD == LD_ROW_BYTE ? 16 : 10); }
+
 template <int LD, int EPI = 0, bool READ_NEXT = true>
-__device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frags& next, StageMx& own,
-                                          const StageMx& nxt, const Problem& p, const LaneOffsets& o, const TileDesc& d4,
+__device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frags& next, Stage<LD>& own,
+                                          const Stage<LD>& nxt, const Problem& p, const LaneOffsets& o, const TileDesc& d4,
                                           int st4, int st1, int rn0, int rm0, int h, bool after_epi = false) {
   constexpr bool SDW = LD != LD_ROW_BYTE;
-  constexpr int PER = SDW ? 10 : 16;  // vector-memory instructions per wave per stage
+  constexpr int PER = stage_vmem<LD>();
   constexpr int ALLOW_EPI = 2 * PER + EPI < 63 ? 2 * PER + EPI : 63;
   // this wave's share of the next stage has landed; after the barrier,
   // everyone's has and nobody still reads `own`
@@ -314,6 +455,13 @@ __device__ __forceinline__ void pipe_step(v16f acc[4][4], const Frags& cur, Frag
   uint32_t sc[8];
   issue_stage<LD>(own, p, o, d4, st4, sc);
   if (READ_NEXT) read_stage<LD>(nxt, st1, p.nblk, rn0, rm0, h, next);
+  if (LD == LD_NV) {
+    // 128 MFMAs with the dequantization of their operands; the compiler
+    // interleaves the conversions of one K step with the MFMAs of the last
+    mfma_stage_nv(acc, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    return;
+  }
   mfma_stage(acc, cur);
   // schedule: MFMAs back to back, with the next stage's fragment reads and
   // the loads four stages ahead slotted between them
@@ -408,9 +556,11 @@ __device__ __forceinline__ void store16(float o[16], void* c, int64_t off, bool 
 // tiles ahead of their use (three 16-register buffers in rotation), so one
 // memory round trip is exposed per tile, not one per MFMA tile. Otherwise
 // element-wise tails at the N edge and the caller drains the stores.
-template <int BF16OUT, int RESID, bool FULL>
+// SCALE: multiply the sums by `mul` (the NVFP4-style tensor scales) before
+// the residual is added.
+template <int BF16OUT, int RESID, bool FULL, bool SCALE>
 __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
-                                           int64_t ldc, const float* residual) {
+                                           int64_t ldc, const float* residual, float mul) {
   const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
   if (FULL) {
     float4 rq[3][4];
@@ -423,6 +573,10 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
       if (RESID && t + 2 < 16) load_res16(rq[(t + 2) % 3], residual + tile_offset(t + 2, m_base, n_base, ldc, r32, h));
       float o[16];
       gather16(acc[t & 3][t >> 2], o);
+      if (SCALE) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] *= mul;
+      }
       if (RESID) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -440,6 +594,10 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
   for (int t = 0; t < 16; ++t) {
     float o[16];
     gather16(acc[t & 3][t >> 2], o);
+    if (SCALE) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] *= mul;
+    }
     const int m = m_base + 32 * (t >> 2) + r32;
     const int n = n_base + 32 * (t & 3) + 16 * h;
     if (m >= p.M || n >= p.N) continue;
@@ -469,12 +627,16 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
   }
 }
 
+// The persistent GEMM of either format: LD_ROW_BYTE, LD_ROW_WORD and
+// LD_PANEL take MXFP4 operands, LD_NV NVFP4-style ones. (One kernel body
+// for all: wrapping it in a device function made the compiler spill.)
 template <int BF16OUT, int RESID, int LD>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* __restrict__ c, int64_t ldc,
-                                                              const float* residual, int nst4) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* __restrict__ c, int64_t ldc,
+                                                               const float* residual, int nst4) {
   constexpr int EPI = full_tile_vmem<BF16OUT, RESID>();
+  constexpr bool NV = LD == LD_NV;
   const bool rows16 = BF16OUT ? (ldc % 8 == 0) : true;  // 16-byte aligned output rows
-  __shared__ StageMx s0, s1, s2, s3;
+  __shared__ Stage<LD> s0, s1, s2, s3;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
@@ -506,8 +668,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
     asm volatile("" ::: "memory");
     if (!SDW) { wait_vm_lgkm0<8>(); store_scale_regs(s3, sc); }
   }
-  constexpr int PER = SDW ? 10 : 16;
+  constexpr int PER = stage_vmem<LD>();
   wait_barrier<3 * PER>();  // stage 0 has landed (this wave's share, then everyone's)
+  const float mul = NV ? (*p.a_ts) * (*p.b_ts) : 1.0f;
   Frags fa, fb;
   read_stage<LD>(s0, 0, p.nblk, rn0, rm0, h, fa);
 
@@ -538,14 +701,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(Problem p, void* _
     asm volatile("" : "+v"(mb), "+v"(nb));  // keep epilogue address math out of the main loop
     counted = rows16 && (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
     if (counted) {
-      store_tile<BF16OUT, RESID, true>(acc, mb, nb, p, c, ldc, residual);
+      store_tile<BF16OUT, RESID, true, NV>(acc, mb, nb, p, c, ldc, residual, mul);
     } else {
-      store_tile<BF16OUT, RESID, false>(acc, mb, nb, p, c, ldc, residual);
+      store_tile<BF16OUT, RESID, false, NV>(acc, mb, nb, p, c, ldc, residual, mul);
       __builtin_amdgcn_s_waitcnt(0);  // an edge tile's stores are not counted: drain them here
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing (past-the-end) loads before the workgroup exits
 }
+
 
 int cu_count() {
   static int n = 0;
@@ -564,12 +728,14 @@ template <int BF16OUT, int RESID>
 hipError_t launch(const Problem& p, void* c, int64_t ldc, const float* residual, hipStream_t st, int ld) {
   const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
   const unsigned grid = (unsigned)min(p.total, cu_count());
-  if (ld == LD_PANEL)
-    gemm_mx_kernel<BF16OUT, RESID, LD_PANEL><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+  if (ld == LD_NV)
+    gemm_fp4_kernel<BF16OUT, RESID, LD_NV><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+  else if (ld == LD_PANEL)
+    gemm_fp4_kernel<BF16OUT, RESID, LD_PANEL><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   else if (ld == LD_ROW_WORD)
-    gemm_mx_kernel<BF16OUT, RESID, LD_ROW_WORD><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+    gemm_fp4_kernel<BF16OUT, RESID, LD_ROW_WORD><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   else
-    gemm_mx_kernel<BF16OUT, RESID, LD_ROW_BYTE><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
+    gemm_fp4_kernel<BF16OUT, RESID, LD_ROW_BYTE><<<grid, kThreads, 0, st>>>(p, c, ldc, residual, nst4);
   return hipGetLastError();
 }
 
@@ -583,6 +749,7 @@ Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, cons
                      int64_t k) {
   Problem p;
   p.a = a; p.as = as; p.b = b; p.bs = bs;
+  p.a_ts = p.b_ts = nullptr;
   p.lda = p.ld_as = p.ldb = p.ld_bs = 0;
   p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
   p.nkc = (int)((k + 127) >> 7);
@@ -602,6 +769,19 @@ hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int6
   const bool sdw = (ld_as % 4 == 0) && (ld_bs % 4 == 0) && (reinterpret_cast<uintptr_t>(as) % 4 == 0) &&
                    (reinterpret_cast<uintptr_t>(bs) % 4 == 0);
   return dispatch(p, c, c_bf16, ldc, residual, st, sdw ? LD_ROW_WORD : LD_ROW_BYTE);
+}
+
+// NVFP4-style operands with 4-byte aligned scale rows (16 scale bytes per
+// 256 K-elements, 8 per stage).
+hipError_t launch_gemm_nv_f16(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
+                              const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
+                              int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc, const float* residual,
+                              hipStream_t st) {
+  Problem p = make_problem(a, as, b, bs, m, n, k);
+  p.lda = lda; p.ld_as = ld_as; p.ldb = ldb; p.ld_bs = ld_bs;
+  p.nblk = (int)(k >> 4);
+  p.a_ts = a_ts; p.b_ts = b_ts;
+  return dispatch(p, c, c_bf16, ldc, residual, st, LD_NV);
 }
 
 hipError_t launch_gemm_mx_panel(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m,

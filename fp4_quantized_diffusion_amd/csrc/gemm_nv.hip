@@ -1,5 +1,8 @@
 // NVFP4-style x NVFP4-style GEMM (E2M1 codes, E4M3 scale per 16 along K,
-// fp32 tensor scale per operand) with fp32 accumulation, for gfx950.
+// fp32 tensor scale per operand) with fp32 accumulation, for gfx950:
+// the kernel for scale rows that are not 4-byte aligned. Aligned scale rows
+// (the library's own quantizer output) take the persistent f16-MFMA kernel
+// in gemm_mx.hip, which dequantizes with gfx950's scaled conversions.
 //
 // gfx950's scaled MFMA only takes power-of-two (E8M0) block scales, and an
 // E2M1 code times an E4M3 scale needs up to 6 significant bits, more than
@@ -51,7 +54,7 @@ __device__ __forceinline__ v8bf dequant8(uint32_t w, float scale) {
 }
 
 template <int BF16OUT, int RESID>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nv_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_nv_bytes_kernel(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ as, int64_t ld_as,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ b, int64_t ldb, const uint8_t* __restrict__ bs,
     int64_t ld_bs, const float* __restrict__ b_ts, int M, int N, int K, void* __restrict__ c, int64_t ldc,
@@ -126,7 +129,7 @@ hipError_t launch(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_a
                   int64_t n, int64_t k, void* c, int64_t ldc, const float* residual, hipStream_t st) {
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const size_t smem = sizeof(Smem<SB>);
-  auto kern = gemm_nv_kernel<BF16OUT, RESID>;
+  auto kern = gemm_nv_bytes_kernel<BF16OUT, RESID>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   kern<<<(unsigned)(tiles_m * tiles_n), kThreads, smem, st>>>(a, lda, as, ld_as, a_ts, b, ldb, bs, ld_bs, b_ts,
@@ -141,6 +144,9 @@ hipError_t launch_gemm_nv(const uint8_t* a, int64_t lda, const uint8_t* as, int6
                           const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc, const float* residual,
                           hipStream_t st) {
+  if (ld_as % 4 == 0 && ld_bs % 4 == 0 && reinterpret_cast<uintptr_t>(as) % 4 == 0 &&
+      reinterpret_cast<uintptr_t>(bs) % 4 == 0)
+    return launch_gemm_nv_f16(a, lda, as, ld_as, a_ts, b, ldb, bs, ld_bs, b_ts, m, n, k, c, c_bf16, ldc, residual, st);
   if (c_bf16) return launch<1, 0>(a, lda, as, ld_as, a_ts, b, ldb, bs, ld_bs, b_ts, m, n, k, c, ldc, nullptr, st);
   if (residual) return launch<0, 1>(a, lda, as, ld_as, a_ts, b, ldb, bs, ld_bs, b_ts, m, n, k, c, ldc, residual, st);
   return launch<0, 0>(a, lda, as, ld_as, a_ts, b, ldb, bs, ld_bs, b_ts, m, n, k, c, ldc, nullptr, st);

@@ -17,6 +17,11 @@ Recipe:
   * rollout: candidate c's noise from default_rng([seed, c]), block b's
     weights from default_rng([seed, 1000 + b]) (W1 then W2), the reward
     vector from default_rng([seed, 9999]).
+  * timing-only inputs (class_linear_device): the same distributions drawn
+    on the GPU with torch's generator, for full-size timing runs where the
+    numpy draw would take minutes; their values differ from the numpy draw
+    and no parity check uses them. Student-t(4) is drawn as
+    Z0 / sqrt((Z1^2 + ... + Z4^2) / 4) with independent standard normals.
 """
 import numpy as np
 
@@ -87,6 +92,33 @@ def class_linear(name, which, rows=None):
     rng_a = np.random.default_rng([cfg["seed"], which, 0])
     a = activations(rng_a, m, k, cfg["act"])
     return a, w
+
+
+def class_linear_device(name, which, device, draw=0, chunk_rows=8192):
+    """Like class_linear, drawn on `device` with torch's generator (seeded
+    from the class seed, `which` and `draw`): bf16 activation [M, K] and bf16
+    weight [N, K]."""
+    import torch
+    cfg = CLASS_SHAPES[name]
+    k, n = (cfg["hidden"], cfg["mlp"]) if which == 1 else (cfg["mlp"], cfg["hidden"])
+    m = cfg["m"]
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg["seed"] * 1000003 + which * 1009 + draw)
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * 0.02
+    n_out = int(round(0.001 * w.numel()))
+    pos = torch.randperm(w.numel(), generator=g, device=device)[:n_out]
+    w.view(-1)[pos] *= 20.0
+    a = torch.empty((m, k), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, m, chunk_rows):
+        r = min(chunk_rows, m - r0)
+        z = torch.randn((r, k), generator=g, device=device, dtype=torch.float32)
+        if cfg["act"] == "student_t":
+            chi2 = torch.zeros_like(z)
+            for _ in range(4):
+                chi2 += torch.randn((r, k), generator=g, device=device, dtype=torch.float32) ** 2
+            z = z / torch.sqrt(chi2 / 4.0)
+        a[r0:r0 + r] = z.to(torch.bfloat16)
+    return a, w.to(torch.bfloat16)
 
 
 def rollout_noise(seed, cand, tokens, dim):

@@ -194,3 +194,100 @@ def test_full_size_sampled(gpu_lib, cls, which):
     c_s = to_np(c.float())[np.ix_(rows, cols)]
     ok, worst = gemm_within_tol(c_s, c_exact, s_abs, bf16_out=True)
     assert ok, worst
+
+
+def nv_operand(codes, scales, ts, k, code_garbage=None, scale_ld=None, scale_fill=0x7F):
+    """An NVFP4-style QTensor from host codes [rows, k/2] and E4M3 scale
+    bytes [rows, k/16]. Code rows are padded to a multiple of 16 bytes with
+    `code_garbage` (random bytes; zeros if None); scale rows get stride
+    `scale_ld` (default k/16 rounded up to 4), the padding filled with
+    `scale_fill` (0x7F: an E4M3 NaN)."""
+    from fp4_quantized_diffusion_amd.binding import QTensor, FMT_NV
+    rows = codes.shape[0]
+    lda = ((k // 2 + 15) // 16) * 16
+    cbuf = np.zeros((rows, lda), np.uint8) if code_garbage is None else code_garbage.integers(
+        0, 256, size=(rows, lda), dtype=np.uint8)
+    cbuf[:, : k // 2] = codes
+    nb = k // 16
+    ld = scale_ld or ((nb + 3) // 4) * 4
+    sbuf = np.full((rows, ld), scale_fill, np.uint8)
+    sbuf[:, :nb] = scales
+    sd = dev(sbuf)[:, :nb]
+    return QTensor(dev(cbuf), sd, torch.tensor([ts], dtype=torch.float32, device=DEV), FMT_NV, k)
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (300, 260, 512), (129, 515, 4096), (16, 16, 48),
+                                   (70, 33, 400)])
+def test_nv_exact_integer_case_bit_exact(gpu_lib, m, n, k):
+    """NVFP4-style operands with every block scale 1.0 (E4M3 0x38) and tensor
+    scales 1: products are multiples of 1/4 and partial sums stay below 2^22,
+    so the GPU must equal the oracle bit for bit (operand layout, K order,
+    K tails that end mid-chunk, row padding holding random bytes)."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = np.full((m, k // 16), 0x38, np.uint8)
+    bs = np.full((n, k // 16), 0x38, np.uint8)
+    qa = nv_operand(ac, as_, 1.0, k, code_garbage=rng)
+    qb = nv_operand(bc, bs, 1.0, k, code_garbage=rng)
+    c = to_np(gpu_lib.gemm(qa, qb, "f32"))
+    c_exact, _ = ogemm.gemm_nv(ac, as_, 1.0, bc, bs, 1.0)
+    np.testing.assert_array_equal(c.astype(np.float64), c_exact)
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 260, 400), (257, 513, 2240), (64, 48, 9728), (1, 1, 16)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_nv_random_scales_and_garbage_padding(gpu_lib, m, n, k, out):
+    """Random codes with random E4M3 block scales over the whole finite range
+    (subnormals included) and arbitrary fp32 tensor scales; code rows padded
+    with random bytes and scale rows with 0x7F (NaN): nothing past K may
+    reach the sum."""
+    rng = np.random.default_rng(7 * m + n + k)
+    ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(0, 127, size=(m, k // 16), dtype=np.uint8)
+    bs = rng.integers(0, 127, size=(n, k // 16), dtype=np.uint8)
+    ta, tb = np.float32(3.7e-3), np.float32(0.0123)
+    qa = nv_operand(ac, as_, ta, k, code_garbage=rng, scale_ld=k // 16 + 4)
+    qb = nv_operand(bc, bs, tb, k, code_garbage=rng, scale_ld=k // 16 + 4)
+    c = to_np(gpu_lib.gemm(qa, qb, out).float())
+    c_exact, s_abs = ogemm.gemm_nv(ac, as_, ta, bc, bs, tb)
+    ok, worst = gemm_within_tol(c, c_exact, s_abs, bf16_out=(out == "bf16"))
+    assert ok, worst
+
+
+@pytest.mark.parametrize("k", [592, 80])
+def test_nv_unaligned_scale_rows(gpu_lib, k):
+    """Scale rows of K/16 bytes with no padding (odd stride): the byte-wise
+    NVFP4-style kernel."""
+    rng = np.random.default_rng(k)
+    m, n = 130, 200
+    ac = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(40, 70, size=(m, k // 16), dtype=np.uint8)
+    bs = rng.integers(40, 70, size=(n, k // 16), dtype=np.uint8)
+    qa = nv_operand(ac, as_, 0.5, k, scale_ld=k // 16)
+    qb = nv_operand(bc, bs, 2.0, k, scale_ld=k // 16)
+    assert qa.scales.stride(0) % 4 != 0
+    c = to_np(gpu_lib.gemm(qa, qb, "f32"))
+    c_exact, s_abs = ogemm.gemm_nv(ac, as_, 0.5, bc, bs, 2.0)
+    ok, worst = gemm_within_tol(c, c_exact, s_abs)
+    assert ok, worst
+
+
+def test_nv_full_size_flux_sampled(gpu_lib):
+    """FLUX-class 36864 x 3072 -> 12288 with NVFP4-style operands quantized on
+    the GPU, bf16 output, in the benchmark's launch configuration: sampled
+    outputs within tolerance of the oracle product of the same codes."""
+    a, w = inputs.class_linear("flux", 1)
+    qa, qb = quantize_both(gpu_lib, a, w, "nv", torch.bfloat16)
+    c = gpu_lib.gemm(qa, qb, "bf16")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(36)
+    rows = np.sort(rng.choice(a.shape[0], 48, replace=False))
+    rows[-1] = a.shape[0] - 1
+    cols = np.sort(rng.choice(w.shape[0], 64, replace=False))
+    cols[-1] = w.shape[0] - 1
+    c_exact, s_abs = oracle_c(qa, qb, "nv", rows, cols)
+    ok, worst = gemm_within_tol(to_np(c.float())[np.ix_(rows, cols)], c_exact, s_abs, bf16_out=True)
+    assert ok, worst
