@@ -172,6 +172,23 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
   }
 }
 
+FP4_API fp4_status fp4_gemm_panel_euler(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                                        int64_t k, const float* residual, const float* x, float* x_out, int64_t ldx,
+                                        float t_cur, float t_next, void* stream) {
+  try {
+    if (!residual || !x || !aligned(x, 16)) return FP4_INVALID_ARGUMENT;
+    const fp4_status s =
+        check_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, x_out, FP4_DT_F32, ldx, residual);
+    if (s != FP4_OK) return s;
+    const float dt = t_next - t_cur;  // fp32 subtraction, as euler_step
+    return from_hip(fp4r::launch_gemm_mx_panel_euler(a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x,
+                                                     x_out, ldx, dt, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
 FP4_API fp4_status euler_step(float* x_out, const float* x, const void* v, int v_dtype, int64_t numel, float t_cur,
                               float t_next, void* stream) {
   try {
@@ -226,6 +243,6 @@ FP4_API const char* fp4_status_str(fp4_status s) {
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 101; }
+FP4_API int fp4_abi_version(void) { return 102; }
 
 }  // extern "C"

@@ -86,6 +86,8 @@ using Stage = StageT<LD == LD_NV ? SCB_NV : SCB>;
 struct Problem {
   const uint8_t *a, *as, *b, *bs;
   const float *a_ts, *b_ts;        // NVFP4-style tensor scales
+  const float* ex;                 // Euler epilogue: the state x, and the step dt
+  float dt;
   int64_t lda, ld_as, ldb, ld_bs;  // row-major layouts
   int M, N, kbytes, nblk;
   int nkc;                         // K chunks of 128 elements (stages per tile)
@@ -510,8 +512,9 @@ __device__ __forceinline__ void gather16(v16f v, float o[16]) {
 
 // Vector-memory instructions store_tile<FULL = true> issues per wave: per
 // MFMA tile two 16-byte stores (bf16) or four (fp32), plus four residual loads.
+// (RESID 2: the Euler epilogue, which also loads x.)
 template <int BF16OUT, int RESID>
-constexpr int full_tile_vmem() { return 16 * (BF16OUT ? 2 : (RESID ? 8 : 4)); }
+constexpr int full_tile_vmem() { return 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -558,19 +561,30 @@ __device__ __forceinline__ void store16(float o[16], void* c, int64_t off, bool 
 // element-wise tails at the N edge and the caller drains the stores.
 // SCALE: multiply the sums by `mul` (the NVFP4-style tensor scales) before
 // the residual is added.
+// RESID 2 (the Euler epilogue, fp32 out): v = fl(sum + residual), then
+// C = fmaf(dt, v, x) with x = p.ex and dt = p.dt -- the operations of a
+// residual GEMM into v followed by the Euler kernel, so bit-identical to
+// them. Every element is read and written by the same lane, so C may alias
+// x or residual.
 template <int BF16OUT, int RESID, bool FULL, bool SCALE>
 __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
                                            int64_t ldc, const float* residual, float mul) {
   const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+  constexpr bool EULER = RESID == 2;
   if (FULL) {
-    float4 rq[3][4];
+    float4 rq[3][4], xq[3][4];
     if (RESID) {
       load_res16(rq[0], residual + tile_offset(0, m_base, n_base, ldc, r32, h));
+      if (EULER) load_res16(xq[0], p.ex + tile_offset(0, m_base, n_base, ldc, r32, h));
       load_res16(rq[1], residual + tile_offset(1, m_base, n_base, ldc, r32, h));
+      if (EULER) load_res16(xq[1], p.ex + tile_offset(1, m_base, n_base, ldc, r32, h));
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      if (RESID && t + 2 < 16) load_res16(rq[(t + 2) % 3], residual + tile_offset(t + 2, m_base, n_base, ldc, r32, h));
+      if (RESID && t + 2 < 16) {
+        load_res16(rq[(t + 2) % 3], residual + tile_offset(t + 2, m_base, n_base, ldc, r32, h));
+        if (EULER) load_res16(xq[(t + 2) % 3], p.ex + tile_offset(t + 2, m_base, n_base, ldc, r32, h));
+      }
       float o[16];
       gather16(acc[t & 3][t >> 2], o);
       if (SCALE) {
@@ -582,6 +596,14 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 r4 = rq[t % 3][g4];
           o[4 * g4] += r4.x; o[4 * g4 + 1] += r4.y; o[4 * g4 + 2] += r4.z; o[4 * g4 + 3] += r4.w;
+        }
+      }
+      if (EULER) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 x4 = xq[t % 3][g4];
+          o[4 * g4] = fmaf(p.dt, o[4 * g4], x4.x); o[4 * g4 + 1] = fmaf(p.dt, o[4 * g4 + 1], x4.y);
+          o[4 * g4 + 2] = fmaf(p.dt, o[4 * g4 + 2], x4.z); o[4 * g4 + 3] = fmaf(p.dt, o[4 * g4 + 3], x4.w);
         }
       }
       store16<BF16OUT>(o, c, tile_offset(t, m_base, n_base, ldc, r32, h), true);
@@ -611,6 +633,15 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
           o[4 * g4] += r[g4].x; o[4 * g4 + 1] += r[g4].y; o[4 * g4 + 2] += r[g4].z; o[4 * g4 + 3] += r[g4].w;
         }
       }
+      if (EULER) {
+        float4 x4[4];
+        load_res16(x4, p.ex + off);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          o[4 * g4] = fmaf(p.dt, o[4 * g4], x4[g4].x); o[4 * g4 + 1] = fmaf(p.dt, o[4 * g4 + 1], x4[g4].y);
+          o[4 * g4 + 2] = fmaf(p.dt, o[4 * g4 + 2], x4[g4].z); o[4 * g4 + 3] = fmaf(p.dt, o[4 * g4 + 3], x4[g4].w);
+        }
+      }
       store16<BF16OUT>(o, c, off, rows16);
     } else {
 #pragma unroll
@@ -618,6 +649,7 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
         if (n + e >= p.N) continue;
         float x = o[e];
         if (RESID) x += residual[off + e];
+        if (EULER) x = fmaf(p.dt, x, p.ex[off + e]);
         if (BF16OUT)
           reinterpret_cast<__bf16*>(c)[off + e] = (__bf16)x;
         else
@@ -750,6 +782,8 @@ Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, cons
   Problem p;
   p.a = a; p.as = as; p.b = b; p.bs = bs;
   p.a_ts = p.b_ts = nullptr;
+  p.ex = nullptr;
+  p.dt = 0.0f;
   p.lda = p.ld_as = p.ldb = p.ld_bs = 0;
   p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
   p.nkc = (int)((k + 127) >> 7);
@@ -782,6 +816,20 @@ hipError_t launch_gemm_nv_f16(const uint8_t* a, int64_t lda, const uint8_t* as, 
   p.nblk = (int)(k >> 4);
   p.a_ts = a_ts; p.b_ts = b_ts;
   return dispatch(p, c, c_bf16, ldc, residual, st, LD_NV);
+}
+
+// The last velocity block fused with the Euler step: x_out = x + dt (residual
+// + A_hat B_hat^T), MXFP4 panel operands, fp32 [m, ldx] state.
+hipError_t launch_gemm_mx_panel_euler(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                      int64_t m, int64_t n, int64_t k, const float* residual, const float* x,
+                                      float* x_out, int64_t ldx, float dt, hipStream_t st) {
+  Problem p = make_problem(a, as, b, bs, m, n, k);
+  p.ex = x;
+  p.dt = dt;
+  const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
+  const unsigned grid = (unsigned)min(p.total, cu_count());
+  gemm_fp4_kernel<0, 2, LD_PANEL><<<grid, kThreads, 0, st>>>(p, x_out, ldx, residual, nst4);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx_panel(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m,

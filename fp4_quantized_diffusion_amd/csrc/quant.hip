@@ -372,19 +372,29 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_panel_kernel(
 __global__ void nv_zero_kernel(float* ts) { *reinterpret_cast<uint32_t*>(ts) = 0u; }
 
 // Tensor amax: |x| bit patterns order like the values, so an integer max is
-// exact and order-independent (deterministic).
+// exact and order-independent (deterministic). Work comes in the row-major
+// kernels' steps (256 consecutive octets of one row, workgroup-uniform row
+// and segment), kUnroll steps per pass with all loads issued first.
 template <int BF16>
-__global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restrict__ x, int64_t k, int64_t ldx,
-                                                           int64_t total_oct, float* ts) {
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restrict__ x, int64_t ldx, int64_t opr,
+                                                           int64_t segs, int64_t steps, float* ts) {
   __shared__ uint32_t sh[kThreads / 64];
-  const int64_t oct_per_row = k >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t G = gridDim.x;
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
-    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
-    float v[8];
-    load8<BF16>(x, row * ldx + oct * 8, v);
-    m = max(m, amax_bits8(v));
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
+    float v[kUnroll][8];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t st = st0 + u * G;
+      const int64_t row = st / segs;
+      const int64_t oct = (st - row * segs) * kThreads + threadIdx.x;
+      ok[u] = st < steps && oct < opr;
+      load8<BF16>(x, ok[u] ? row * ldx + oct * 8 : 0, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ok[u]) m = max(m, amax_bits8(v[u]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
@@ -425,18 +435,33 @@ __device__ __forceinline__ float e4m3_value(uint32_t S) {
   return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
 }
 
+// Codes and E4M3 block scales, in the row-major kernels' steps (a 16-block is
+// two adjacent lanes of one step), kUnroll steps per pass.
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
-    const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t total_oct, const float* __restrict__ ts) {
-  const int64_t oct_per_row = k >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps,
+    const float* __restrict__ ts) {
   const float sg = *ts;
   const float tau = 6.0f * sg;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total_oct; i += stride) {
-    const int64_t row = i / oct_per_row, oct = i - row * oct_per_row;
-    float v[8];
-    load8<BF16>(x, row * ldx + oct * 8, v);
+  const int64_t G = gridDim.x;
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
+    float vv[kUnroll][8];
+    int64_t rows[kUnroll], octs[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t st = st0 + u * G;
+      rows[u] = st / segs;
+      octs[u] = (st - rows[u] * segs) * kThreads + threadIdx.x;
+      const bool ok = st < steps && octs[u] < opr;
+      load8<BF16>(x, ok ? rows[u] * ldx + octs[u] * 8 : 0, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+    // whole 16-blocks drop out: opr is even
+    if (st0 + u * G >= steps || octs[u] >= opr) continue;
+    const int64_t row = rows[u], oct = octs[u];
+    float* v = vv[u];
     uint32_t am = amax_bits8(v);
     am = max(am, (uint32_t)__shfl_xor((int)am, 1));  // the 2 octets of a 16-block
     const float sf = __uint_as_float(am) / tau;
@@ -447,11 +472,19 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) w |= ((__float_as_uint(v[j]) >> 28) & 8u) << (4 * j);
     } else {
+      // fl(x / d) (correctly rounded division), then its E2M1 code through
+      // the same scaled convert as the MX path, with scale 1
+      float q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w |= e2m1_nibble(v[j] / d) << (4 * j);
+      for (int j = 0; j < 8; ++j) q[j] = v[j] / d;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
     }
     *reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4) = w;
     if ((oct & 1) == 0) scales[row * ld_scales + (oct >> 1)] = (uint8_t)S;
+    }
   }
 }
 
@@ -540,21 +573,24 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
 hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            float* tensor_scale, int scale_given, hipStream_t st) {
-  const int64_t total = rows * (k >> 3);
-  const unsigned g = grid_for(total);
+  const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
+  const unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
   if (!scale_given) {
     nv_zero_kernel<<<1, 1, 0, st>>>(tensor_scale);
-    const unsigned ga = g < 4096 ? g : 4096;
+    // a resident-sized grid: each workgroup issues one atomic at its end
+    const unsigned ga = g < 2048 ? g : 2048;
     if (x_bf16)
-      nv_amax_kernel<1><<<ga, kThreads, 0, st>>>(x, k, ldx, total, tensor_scale);
+      nv_amax_kernel<1><<<ga, kThreads, 0, st>>>(x, ldx, opr, segs, steps, tensor_scale);
     else
-      nv_amax_kernel<0><<<ga, kThreads, 0, st>>>(x, k, ldx, total, tensor_scale);
+      nv_amax_kernel<0><<<ga, kThreads, 0, st>>>(x, ldx, opr, segs, steps, tensor_scale);
     nv_finalize_kernel<<<1, 1, 0, st>>>(tensor_scale);
   }
   if (x_bf16)
-    quant_nv_kernel<1><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total, tensor_scale);
+    quant_nv_kernel<1><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                tensor_scale);
   else
-    quant_nv_kernel<0><<<g, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales, total, tensor_scale);
+    quant_nv_kernel<0><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                tensor_scale);
   return hipGetLastError();
 }
 

@@ -17,25 +17,47 @@ constexpr int kRewardThreads = 1024;
 constexpr int kRankThreads = 256;
 constexpr int kRankChunk = 4096;
 
-// One workgroup per candidate; the candidate's rows_per_cand x dim block is
-// read once as float4 columns. u == NULL gives the plain mean.
+// One workgroup per candidate, read once as float4 column groups: with
+// dim % 4 == 0 and dim / 4 <= 1024 (the rollout's 3072 dims are 768 groups),
+// thread t owns column group t for every row -- its weights u stay in
+// registers, there is no index division, and each thread keeps kRows
+// 16-byte loads in flight. Other shapes take the flat loop. u == NULL gives
+// the plain mean. The sum runs in a fixed order (per thread, then a fixed
+// shuffle tree and a fixed LDS order), so it is bitwise repeatable.
+constexpr int kRows = 8;
+
+__device__ __forceinline__ float dot4(float4 a, float4 w) { return a.x * w.x + a.y * w.y + a.z * w.z + a.w * w.w; }
+
 __global__ __launch_bounds__(kRewardThreads) void proxy_reward_kernel(
     const float* __restrict__ x, int64_t rows, int64_t dim, int64_t ldx, const float* __restrict__ u,
     float* __restrict__ rewards) {
   __shared__ float sh[kRewardThreads / 64];
   const int64_t c = blockIdx.x;
   const int64_t d4 = dim >> 2;
-  const int64_t total = rows * d4;
   const float* base = x + c * rows * ldx;
   float acc = 0.f;
-  for (int64_t i = threadIdx.x; i < total; i += kRewardThreads) {
-    const int64_t r = i / d4, q = i - r * d4;
-    const float4 a = *reinterpret_cast<const float4*>(base + r * ldx + q * 4);
-    if (u) {
-      const float4 w = reinterpret_cast<const float4*>(u)[q];
-      acc += a.x * w.x + a.y * w.y + a.z * w.z + a.w * w.w;
-    } else {
-      acc += (a.x + a.y) + (a.z + a.w);
+  if ((dim & 3) == 0 && (ldx & 3) == 0 && d4 <= kRewardThreads) {
+    const int t = threadIdx.x;
+    if (t < d4) {
+      const float4 w = u ? reinterpret_cast<const float4*>(u)[t] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float* col = base + 4 * t;
+      int64_t r = 0;
+      for (; r + kRows <= rows; r += kRows) {
+        float4 a[kRows];
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) a[j] = *reinterpret_cast<const float4*>(col + (r + j) * ldx);
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) acc += u ? dot4(a[j], w) : (a[j].x + a[j].y) + (a[j].z + a[j].w);
+      }
+      for (; r < rows; ++r) {
+        const float4 a = *reinterpret_cast<const float4*>(col + r * ldx);
+        acc += u ? dot4(a, w) : (a.x + a.y) + (a.z + a.w);
+      }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < rows * dim; i += kRewardThreads) {
+      const int64_t r = i / dim, q = i - r * dim;
+      acc += u ? base[r * ldx + q] * u[q] : base[r * ldx + q];
     }
   }
 #pragma unroll

@@ -14,11 +14,16 @@ uniform grid t_i = 1 - i/steps. Per block the device work is:
     fp4_gemm(A1, W1q) -> z (bf16)
     fp4_quantize(z, GELU prologue)        -> A2 (MXFP4)
     fp4_gemm(A2, W2q, residual = h) -> h  (fp32, in place)
-and per step euler_step(x, v = h). The hidden activation z is stored as bf16
-between the two kernels (the float64 oracle keeps it unrounded). The FP4
-operands use the panel layout by default (fp4_quantize with FP4_LAYOUT_PANEL,
-fp4_gemm_panel): the same codes and scales, stored so that every GEMM stage
-load is contiguous; layout="row" runs the row-major entry points instead.
+and per step euler_step(x, v = h). With the panel layout (the default) the
+last block's second GEMM and the Euler step are one call,
+fp4_gemm_panel_euler(A2, W2q, residual = h, x) -> x_next, which applies
+x + dt (h + A2 W2q^T) in the GEMM's epilogue -- bit-identical to the GEMM into
+v followed by euler_step, without writing v or reading it back. The hidden
+activation z is stored as bf16 between the two kernels (the float64 oracle
+keeps it unrounded). The FP4 operands use the panel layout by default
+(fp4_quantize with FP4_LAYOUT_PANEL, fp4_gemm_panel): the same codes and
+scales, stored so that every GEMM stage load is contiguous; layout="row" runs
+the row-major entry points (and a separate euler_step) instead.
 
 Two-stream schedule (overlap=True): the candidates are split into
 two halves A and B; the GEMMs run on the caller's stream and the quantizers
@@ -89,20 +94,28 @@ class Fp4Rollout:
     def _gemm(self, a, b, out_dtype, residual=None, out=None):
         return self._call("gemm", lambda: fb.gemm(a, b, out_dtype, residual=residual, out=out))
 
-    def velocity(self, x, h):
+    def velocity(self, x, h, step=None):
         """h <- v(x) for x, h fp32 [rows, dim] (h_0 = x is never copied: the
-        first block's GEMM takes x as its residual)."""
+        first block's GEMM takes x as its residual). step = (t_cur, t_next,
+        x_out): the last block's second GEMM also takes the Euler step,
+        x_out = x + (t_next - t_cur) v, and h is left at the previous block's
+        value."""
         import torch
         rows, dim = x.shape
         hidden = self.w1[0].shape[0]
         z = self._buf("z", (rows, hidden), torch.bfloat16, x.device)
         src = x
+        last = len(self.w1) - 1
         for b in range(len(self.w1)):
             a1 = self._call("quant_rmsnorm", lambda: fb.quantize(
                 src, self.fmt, prologue="rmsnorm", out=self._qbuf("a1", rows, dim, x.device)))
             self._gemm(a1, self.q1[b], "bf16", out=z)
             a2 = self._call("quant_gelu", lambda: fb.quantize(
                 z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
+            if b == last and step is not None:
+                t_cur, t_next, x_out = step
+                self._call("gemm", lambda: fb.gemm_euler(a2, self.q2[b], src, x, t_cur, t_next, out=x_out))
+                return x_out
             self._gemm(a2, self.q2[b], "f32", residual=src, out=h)
             src = h
         return h
@@ -207,8 +220,11 @@ class Fp4Rollout:
             for c0 in range(0, n_cand, chunk):
                 r0, rows = c0 * tokens, min(chunk, n_cand - c0) * tokens
                 xs, xd = src[r0:r0 + rows], x[r0:r0 + rows]
-                hc = self.velocity(xs, h[:rows])
-                self._call("euler", lambda: fb.euler(xs, hc, t[i], t[i + 1], out=xd))
+                if self.layout == "panel":  # Euler step fused into the last GEMM
+                    self.velocity(xs, h[:rows], step=(t[i], t[i + 1], xd))
+                else:
+                    hc = self.velocity(xs, h[:rows])
+                    self._call("euler", lambda: fb.euler(xs, hc, t[i], t[i + 1], out=xd))
         rewards = self._call("reward", lambda: fb.proxy_reward(x, n_cand, tokens, self.u))
         top, bottom, rn = self._call("select", lambda: fb.select(rewards, self.k_top, self.k_bottom))
         return rewards, top, bottom, rn

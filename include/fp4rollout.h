@@ -175,6 +175,28 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
                           void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
 
 /*
+ * fp4_gemm_panel_euler -- the last block of the velocity network fused with
+ * the Euler step that consumes it (aitrends summary, Stage-1 paragraph: a
+ * 6-step FP4 ODE solve; the velocity is the residual stream plus the last
+ * solver linear):
+ *   x_out[i, j] = x[i, j] + (t_next - t_cur) * (residual[i, j] + sum_k A_hat[i, k] B_hat[j, k])
+ * evaluated as fmaf(dt, fl(acc + residual), x) with dt = fl32(t_next - t_cur):
+ * the same operations as fp4_gemm_panel(..., residual) into an fp32 v
+ * followed by euler_step(x_out, x, v), so the result is bit-identical to
+ * that pair -- without writing v or reading it back.
+ *   fmt, a_*, b_*, m, n, k  as in fp4_gemm_panel (FP4_FMT_MX only).
+ *   residual, x, x_out      fp32 [m, ldx], 16-byte aligned, ldx a multiple of 4,
+ *                           ldx >= n; x_out may equal x and/or residual (in place).
+ *   t_cur, t_next           the step's two times.
+ * Accuracy: as fp4_gemm for the product; the update as euler_step.
+ */
+FP4_API fp4_status fp4_gemm_panel_euler(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales,
+                                int64_t m, int64_t n, int64_t k,
+                                const float* residual, const float* x, float* x_out, int64_t ldx,
+                                float t_cur, float t_next, void* stream);
+
+/*
  * euler_step -- one explicit Euler step of the sampler's ODE,
  *   x_out = x + (t_next - t_cur) * v,
  * with dt = fl32(t_next - t_cur) and an fp32 multiply-add per element. The

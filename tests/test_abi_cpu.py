@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 101
+    assert fq.fp4_abi_version() == 102
 
 
 def test_status_strings(lib):
@@ -152,3 +152,23 @@ def test_gemm_panel_rejects(lib, kw):
 
 def test_gemm_panel_nv_unsupported(lib):
     assert gp(fmt=1) == fq.binding.UNSUPPORTED
+
+
+def ge(**kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=8, n=8, k=64, residual=P2, x=P3, x_out=P, ldx=8,
+             t_cur=1.0, t_next=5.0 / 6.0, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_panel_euler(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(b_s=None), dict(residual=None), dict(x=None), dict(x_out=None),
+    dict(x=P3 + 4), dict(residual=P2 + 8), dict(x_out=P + 4), dict(m=0), dict(k=48), dict(ldx=6), dict(ldx=10),
+    dict(a=P + 8), dict(a_s=P3 + 2),
+])
+def test_gemm_panel_euler_rejects(lib, kw):
+    assert ge(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_gemm_panel_euler_nv_unsupported(lib):
+    assert ge(fmt=1) == fq.binding.UNSUPPORTED

@@ -168,3 +168,48 @@ def test_gemm_panel_rollout_shape_sampled(gpu_lib):
     got = to_np(c[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float())
     ok, worst = gemm_within_tol(got, c_exact, s_abs, bf16_out=True)
     assert ok, worst
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 260, 416), (512, 256, 1024), (37, 72, 96), (1, 4, 32)])
+def test_gemm_euler_equals_gemm_then_euler(gpu_lib, m, n, k):
+    """fp4_gemm_panel_euler: bit-identical to fp4_gemm_panel(residual) into v
+    followed by euler_step (also in place, x_out == x), and within the GEMM
+    bound of the oracle's x + dt (residual + C_exact)."""
+    rng = np.random.default_rng(m + n + k)
+    qa = gpu_lib.quantize(dev(act(m, k, m)), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(wts(n, k, n)), "mx", layout="panel")
+    res = dev(rng.standard_normal((m, n)).astype(np.float32))
+    x = dev(rng.standard_normal((m, n)).astype(np.float32))
+    t0, t1 = 1.0 - 2 / 6, 1.0 - 3 / 6
+    v = gpu_lib.gemm(qa, qb, "f32", residual=res, out=torch.empty((m, n), dtype=torch.float32, device=DEV))
+    ref = gpu_lib.euler(x, v, t0, t1)
+    out = gpu_lib.gemm_euler(qa, qb, res, x, t0, t1)
+    np.testing.assert_array_equal(to_np(out), to_np(ref))
+    xin = x.clone()
+    gpu_lib.gemm_euler(qa, qb, res, xin, t0, t1, out=xin)
+    np.testing.assert_array_equal(to_np(xin), to_np(ref))
+    ac, as_, _ = panel_to_rows(to_np(qa.codes), to_np(qa.scales), m, k)
+    bc, bs, _ = panel_to_rows(to_np(qb.codes), to_np(qb.scales), n, k)
+    c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+    dt = np.float64(np.float32(t1) - np.float32(t0))
+    want = to_np(x).astype(np.float64) + dt * (to_np(res).astype(np.float64) + c_exact)
+    tol = abs(dt) * (1e-4 * s_abs + 1e-6 * np.abs(to_np(res))) + 1e-6 * np.abs(want) + 1e-30
+    assert np.all(np.abs(to_np(out).astype(np.float64) - want) <= tol)
+
+
+def test_gemm_euler_row_stride(gpu_lib):
+    """Strided state (ldx > n): only the [m, n] window is read and written."""
+    m, n, k, ldx = 260, 100, 128, 112
+    rng = np.random.default_rng(41)
+    qa = gpu_lib.quantize(dev(act(m, k, 3)), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(wts(n, k, 4)), "mx", layout="panel")
+    base = dev(rng.standard_normal((m, ldx)).astype(np.float32))
+    res = dev(rng.standard_normal((m, ldx)).astype(np.float32))
+    keep = to_np(base).copy()
+    out = base[:, :n]
+    gpu_lib.gemm_euler(qa, qb, res[:, :n], base[:, :n], 1.0, 5.0 / 6.0, out=out)
+    v = gpu_lib.gemm(qa, qb, "f32", residual=res[:, :n].contiguous(),
+                     out=torch.empty((m, n), dtype=torch.float32, device=DEV))
+    ref = gpu_lib.euler(dev(keep[:, :n]), v, 1.0, 5.0 / 6.0)
+    np.testing.assert_array_equal(to_np(base)[:, :n], to_np(ref))
+    np.testing.assert_array_equal(to_np(base)[:, n:], keep[:, n:])

@@ -102,6 +102,41 @@ def test_nv_given_tensor_scale(gpu_lib):
     assert to_np(q.tensor_scale)[0] == sg
 
 
+@pytest.mark.parametrize("block_amax", [6.0, 2.5, 3.1])
+def test_element_rounding_sweep_nv(gpu_lib, block_amax):
+    """NVFP4-style element rounding around every E2M1 decision and grid
+    point: with tensor scale 10 / 2688 given, each 16-block holds its amax
+    (first element) and 15 values x chosen so that x / d lies within 64 ulps
+    of a decision point (d the block's divisor: 1.0 for amax 6 at tensor amax
+    6, otherwise not a power of two), both signs and -0. Codes and scales
+    must equal the oracle's bit for bit -- the rounded quotient fl(x / d)
+    decides each code."""
+    sg = np.float32(np.float32(10.0) / np.float32(2688.0)) if block_amax != 6.0 else \
+        np.float32(np.float32(6.0) / np.float32(2688.0))
+    _, s_blk, _ = nvfp4.quantize(np.full((1, 16), block_amax, np.float32), s_g=sg)
+    d = np.float32(nvfp4.e4m3_decode(s_blk[0, 0]).astype(np.float32) * sg)
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0], np.float32)
+    q = (pts.view(np.uint32)[:, None].astype(np.int64) + np.arange(-64, 65)[None, :]).reshape(-1)
+    x = (q.astype(np.uint32).view(np.float32) * d).astype(np.float32)     # quotients near the points
+    x = np.concatenate([x, np.nextafter(x, np.float32(0)), np.nextafter(x, np.float32(10))])
+    x = x[np.abs(x) < np.float32(block_amax)]
+    per = 15
+    rows = (x.size + per - 1) // per
+    flat = np.zeros(rows * per, np.float32)
+    flat[: x.size] = x
+    blocks = np.zeros((rows, 16), np.float32)
+    blocks[:, 1:] = flat.reshape(rows, per)
+    blocks[:, 0] = block_amax
+    blocks[1::2] = -blocks[1::2]
+    blocks[2::7, 5] = -0.0
+    xr = blocks.reshape(-1, 64) if rows % 4 == 0 else blocks[: rows - rows % 4].reshape(-1, 64)
+    xt = torch.from_numpy(np.ascontiguousarray(xr)).to(DEV)
+    q = gpu_lib.quantize(xt, "nv", tensor_scale=torch.tensor([sg], device=DEV))
+    oc, os_, _ = nvfp4.quantize(xr, s_g=sg)
+    np.testing.assert_array_equal(to_np(q.scales), os_)
+    np.testing.assert_array_equal(to_np(q.codes)[:, :32], oc)
+
+
 def test_element_rounding_sweep_mx(gpu_lib):
     """fp32 values with exponent in [2^-3, 2^3): every 5th mantissa of each
     binade plus every value within 256 ulps of each E2M1 decision point and
