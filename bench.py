@@ -32,11 +32,11 @@ PEAK_HBM = 8.0e12       # bytes/s
 # Bytes each GEMM launch moves between L2 and the memory fabric (Infinity
 # Cache or HBM), from rocprofv3 FETCH_SIZE (x2: every read request is
 # 128 bytes, which the counter's formula weighs as 64) and WRITE_SIZE (x1)
-# runs of this workload, averaged over the two rollout GEMMs; valid only for
+# runs of this workload, averaged over a step's GEMM launches; valid only for
 # the kernel sources they were taken with (reported as null once those
 # change). See profiles/rollout_96x4096x3072_kernels.md.
-GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "4915163ea7bfaaf7", "gemm_common.h": "d8952e405ad1a5b1"},
-                "bytes_per_launch": 22.84e9}
+GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "365364e016824ca4", "gemm_common.h": "d8952e405ad1a5b1"},
+                "bytes_per_launch": 22.78e9}
 
 
 def gemm_traffic():
@@ -351,7 +351,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4),
                      "traffic": (None if gemm_traffic() is None else round(gemm_traffic() / 1e9, 2)),
                      "traffic_unit": "GB per launch (L2 <-> fabric reads + writes, rocprofv3 counters)",
-                     "kernel": f"gemm_mx_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate)",
+                     "kernel": f"gemm_fp4_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate; the last "
+                               "block's launches also apply the Euler step in their epilogue)",
                      "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "gemm_tflops": round(achieved / 1e12, 2),
         "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),
