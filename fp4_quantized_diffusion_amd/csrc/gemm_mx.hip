@@ -559,6 +559,116 @@ __device__ __forceinline__ void store16(float o[16], void* c, int64_t off, bool 
 // tiles ahead of their use (three 16-register buffers in rotation), so one
 // memory round trip is exposed per tile, not one per MFMA tile. Otherwise
 // element-wise tails at the N edge and the caller drains the stores.
+// LDS staging area of one wave for the epilogue of a full tile: 32 rows of
+// 128 bytes (two MFMA tiles of bf16, or one of fp32), rows padded to 144
+// bytes so that the accumulator-order writes and the row-order reads are
+// both free of bank conflicts.
+constexpr int kEpiPitch = 144;
+constexpr int kEpiWaveBytes = 32 * kEpiPitch;
+
+// Stored straight from the accumulator layout, a store instruction covers 32
+// rows x two 16-byte pieces (64 scattered pieces). Instead each lane writes
+// its 16 consecutive n of one row (after the lane-half swap of gather16) to
+// the staging area and reads back 16 bytes of a row, so that lanes
+// 8 r' .. 8 r' + 7 cover one row's 128 bytes: every store (and residual /
+// state load) instruction then touches 8 whole 128-byte row segments. The
+// instruction counts stay those of the direct epilogue (full_tile_vmem),
+// which the pipeline's waits count.
+
+// bf16 output: MFMA tiles (2k, j) and (2k + 1, j) share the staging area, 4
+// stores per pair.
+__device__ __forceinline__ void store_tile_bf16_lds(v16f acc[4][4], int m_base, int n_base, void* c, int64_t ldc,
+                                                    uint8_t* stage) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
+  const int r32 = lane & 31, h = lane >> 5;
+  const int rq = lane >> 3, cq = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        float o[16];
+        gather16(acc[2 * k + ii][j], o);  // 16 consecutive n of row r32: 32 bytes at column byte 32 h
+        uint32_t wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)  // hardware round-to-nearest-even conversion
+          wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
+        uint4* dst = reinterpret_cast<uint4*>(stage + r32 * kEpiPitch + ii * 64 + h * 32);
+        dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 8 * q + rq;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kEpiPitch + cq * 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + (int64_t)(m_base + 32 * j + row) * ldc + n_base +
+                                  64 * k + 8 * cq) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the next pair's writes stay behind these reads
+    }
+}
+
+// fp32 output, RESID 1: + residual, RESID 2: then the Euler step
+// fmaf(dt, v, x) (see store_tile). One MFMA tile at a time (t = 4 j + i), 4
+// stores plus 4 residual (and 4 state) loads each; the loads run two MFMA
+// tiles ahead of their use.
+template <int RESID>
+__device__ __forceinline__ void store_tile_f32_lds(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
+                                                   int64_t ldc, const float* residual, uint8_t* stage) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
+  const int r32 = lane & 31, h = lane >> 5;
+  const int rq = lane >> 3, cq = lane & 7;
+  constexpr bool EULER = RESID == 2;
+  constexpr int LA = EULER ? 1 : 2;  // MFMA tiles of load look-ahead (registers allow one with two inputs)
+  constexpr int NB = LA + 1;
+  auto goff = [&](int t, int q) -> int64_t {
+    return (int64_t)(m_base + 32 * (t >> 2) + 8 * q + rq) * ldc + n_base + 32 * (t & 3) + 4 * cq;
+  };
+  float4 rb[NB][4], xb[NB][4];
+  if (RESID) {
+#pragma unroll
+    for (int t = 0; t < LA; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rb[t][q] = *reinterpret_cast<const float4*>(residual + goff(t, q));
+        if (EULER) xb[t][q] = *reinterpret_cast<const float4*>(p.ex + goff(t, q));
+      }
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if (RESID && t + LA < 16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rb[(t + LA) % NB][q] = *reinterpret_cast<const float4*>(residual + goff(t + LA, q));
+        if (EULER) xb[(t + LA) % NB][q] = *reinterpret_cast<const float4*>(p.ex + goff(t + LA, q));
+      }
+    }
+    float o16[16];
+    gather16(acc[t & 3][t >> 2], o16);  // 16 consecutive n of row r32: 64 bytes at column byte 64 h
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<float4*>(stage + r32 * kEpiPitch + h * 64 + g4 * 16) =
+          make_float4(o16[4 * g4], o16[4 * g4 + 1], o16[4 * g4 + 2], o16[4 * g4 + 3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 o = *reinterpret_cast<const float4*>(stage + (8 * q + rq) * kEpiPitch + cq * 16);
+      if (RESID) {
+        const float4 r = rb[t % NB][q];
+        o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+      }
+      if (EULER) {
+        const float4 x = xb[t % NB][q];
+        o.x = fmaf(p.dt, o.x, x.x); o.y = fmaf(p.dt, o.y, x.y); o.z = fmaf(p.dt, o.z, x.z); o.w = fmaf(p.dt, o.w, x.w);
+      }
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + goff(t, q)) = o;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads' look-ahead, and the next writes behind these reads
+  }
+}
+
 // SCALE: multiply the sums by `mul` (the NVFP4-style tensor scales) before
 // the residual is added.
 // RESID 2 (the Euler epilogue, fp32 out): v = fl(sum + residual), then
@@ -669,6 +779,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
   constexpr bool NV = LD == LD_NV;
   const bool rows16 = BF16OUT ? (ldc % 8 == 0) : true;  // 16-byte aligned output rows
   __shared__ Stage<LD> s0, s1, s2, s3;
+  // full tiles' epilogue through an LDS staging area (the MXFP4 ring leaves
+  // room for it; the NVFP4-style ring, with twice the scale bytes, does not)
+  constexpr bool EPI_LDS = !NV;
+  __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
@@ -733,7 +847,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
     asm volatile("" : "+v"(mb), "+v"(nb));  // keep epilogue address math out of the main loop
     counted = rows16 && (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
     if (counted) {
-      store_tile<BF16OUT, RESID, true, NV>(acc, mb, nb, p, c, ldc, residual, mul);
+      if (EPI_LDS && BF16OUT)
+        store_tile_bf16_lds(acc, mb, nb, c, ldc, epi_stage + wave * kEpiWaveBytes);
+      else if (EPI_LDS)
+        store_tile_f32_lds<RESID>(acc, mb, nb, p, c, ldc, residual, epi_stage + wave * kEpiWaveBytes);
+      else
+        store_tile<BF16OUT, RESID, true, NV>(acc, mb, nb, p, c, ldc, residual, mul);
     } else {
       store_tile<BF16OUT, RESID, false, NV>(acc, mb, nb, p, c, ldc, residual, mul);
       __builtin_amdgcn_s_waitcnt(0);  // an edge tile's stores are not counted: drain them here
