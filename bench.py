@@ -35,8 +35,8 @@ PEAK_HBM = 8.0e12       # bytes/s
 # runs of this workload, averaged over a step's GEMM launches; valid only for
 # the kernel sources they were taken with (reported as null once those
 # change). See profiles/rollout_96x4096x3072_kernels.md.
-GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "365364e016824ca4", "gemm_common.h": "d8952e405ad1a5b1"},
-                "bytes_per_launch": 22.78e9}
+GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "e3399c141784a1df", "gemm_common.h": "d8952e405ad1a5b1"},
+                "bytes_per_launch": 24.69e9}
 
 
 def gemm_traffic():
@@ -128,7 +128,7 @@ def rank_stats(a, b, k):
             "bottom_overlap": len(ba & bb), "k": k}
 
 
-def cpu_baseline(cfg, tokens_sample=32, w_rows_sample=256):
+def cpu_baseline(cfg, tokens_sample=128, w_rows_sample=1024):
     """The CPU oracle on a bounded sample of the rollout, scaled to candidates/s:
     (a) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one W1,
         scaled by element count to all 8 weights (once per rollout);
