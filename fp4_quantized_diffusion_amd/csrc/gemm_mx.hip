@@ -559,6 +559,9 @@ __device__ __forceinline__ void store16(float o[16], void* c, int64_t off, bool 
 // tiles ahead of their use (three 16-register buffers in rotation), so one
 // memory round trip is exposed per tile, not one per MFMA tile. Otherwise
 // element-wise tails at the N edge and the caller drains the stores.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // LDS staging area of one wave for the epilogue of a full tile: 32 rows of
 // 128 bytes (two MFMA tiles of bf16, or one of fp32), rows padded to 144
 // bytes so that the accumulator-order writes and the row-order reads are
@@ -602,9 +605,12 @@ __device__ __forceinline__ void store_tile_bf16_lds(v16f acc[4][4], int m_base, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = 8 * q + rq;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kEpiPitch + cq * 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + (int64_t)(m_base + 32 * j + row) * ldc + n_base +
-                                  64 * k + 8 * cq) = v;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kEpiPitch + cq * 16);
+        // non-temporal: the output is not read again by this kernel, and the
+        // L2 is left to the operand panels
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(c) +
+                                                                (int64_t)(m_base + 32 * j + row) * ldc + n_base +
+                                                                64 * k + 8 * cq));
       }
       __builtin_amdgcn_sched_barrier(0);  // the next pair's writes stay behind these reads
     }
@@ -663,7 +669,7 @@ __device__ __forceinline__ void store_tile_f32_lds(v16f acc[4][4], int m_base, i
         const float4 x = xb[t % NB][q];
         o.x = fmaf(p.dt, o.x, x.x); o.y = fmaf(p.dt, o.y, x.y); o.z = fmaf(p.dt, o.z, x.z); o.w = fmaf(p.dt, o.w, x.w);
       }
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + goff(t, q)) = o;
+      __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(c) + goff(t, q)));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads' look-ahead, and the next writes behind these reads
   }
