@@ -3,10 +3,10 @@
 Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
   * the raw entry points under their C names (fp4_quantize, fp4_panel_bytes,
-    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_euler, euler_step, fp4_proxy_reward,
+    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
-  * torch-tensor helpers (quantize, gemm, gemm_euler, euler, proxy_reward, select) that
+  * torch-tensor helpers (quantize, gemm, gemm_gelu, gemm_euler, euler, proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
 Loading fails loudly when the library has not been built; there is no
@@ -32,6 +32,7 @@ _SIGS = {
     "fp4_panel_bytes": [_i64, _i64, _p, _p],
     "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
+    "fp4_gemm_panel_gelu": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p],
     "fp4_gemm_panel_euler": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p],
     "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
     "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
@@ -89,6 +90,11 @@ def fp4_panel_bytes(rows, k, code_bytes, scale_bytes):
 def fp4_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype, ldc, residual, stream):
     return load_library().fp4_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype, ldc,
                                          residual, stream)
+
+
+def fp4_gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales, stream):
+    return load_library().fp4_gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes,
+                                              out_scales, stream)
 
 
 def fp4_gemm_panel_euler(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x, x_out, ldx, t_cur, t_next,
@@ -236,6 +242,25 @@ def gemm(a, b, out_dtype="bf16", residual=None, out=None):
                   b.scales.stride(0), _ptr(b.tensor_scale), m, n, k, out.data_ptr(), _dtype_code(out),
                   out.stride(0), _ptr(residual), _stream())
     _check(st, "fp4_gemm")
+    return out
+
+
+def gemm_gelu(a, b, out=None):
+    """MXFP4 panel QTensor of GELU(bf16(A_hat B_hat^T)) for panel-layout
+    QTensors a [m, k], b [n, k] (m, n multiples of 256)."""
+    torch = _torch()
+    if a.layout != "panel" or b.layout != "panel" or a.k != b.k:
+        raise ValueError("gemm_gelu takes panel-layout operands of one k")
+    m, n, k = a.n_rows, b.n_rows, a.k
+    if out is None:
+        cb, sb = panel_bytes(m, n)
+        out = QTensor(torch.empty(cb, dtype=torch.uint8, device=a.codes.device),
+                      torch.empty(sb, dtype=torch.uint8, device=a.codes.device), None, FMT_MX, n, "panel", m)
+    if out.layout != "panel" or out.rows != m or out.k != n:
+        raise ValueError("out was allocated for another shape")
+    st = fp4_gemm_panel_gelu(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                             m, n, k, out.codes.data_ptr(), out.scales.data_ptr(), _stream())
+    _check(st, "fp4_gemm_panel_gelu")
     return out
 
 

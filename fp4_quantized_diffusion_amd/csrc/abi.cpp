@@ -172,6 +172,27 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
   }
 }
 
+FP4_API fp4_status fp4_gemm_panel_gelu(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                                       int64_t k, uint8_t* out_codes, uint8_t* out_scales, void* stream) {
+  try {
+    if (fmt != FP4_FMT_MX && fmt != FP4_FMT_NV) return FP4_INVALID_ARGUMENT;
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !out_codes || !out_scales) return FP4_INVALID_ARGUMENT;
+    if (m < 1 || n < 1 || k < 32 || k % 32 != 0) return FP4_INVALID_ARGUMENT;
+    if (m >= kMaxDim - 256 || n >= kMaxDim - 256 || k > ((int64_t)1 << 23)) return FP4_INVALID_ARGUMENT;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+        !aligned(out_codes, 16) || !aligned(out_scales, 4))
+      return FP4_INVALID_ARGUMENT;
+    const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles >= kMaxDim) return FP4_INVALID_ARGUMENT;
+    if (fmt == FP4_FMT_NV || m % 256 != 0 || n % 256 != 0) return FP4_UNSUPPORTED;
+    return from_hip(fp4r::launch_gemm_mx_panel_gelu(a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes,
+                                                    out_scales, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
 FP4_API fp4_status fp4_gemm_panel_euler(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
                                         int64_t k, const float* residual, const float* x, float* x_out, int64_t ldx,
@@ -243,6 +264,6 @@ FP4_API const char* fp4_status_str(fp4_status s) {
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 102; }
+FP4_API int fp4_abi_version(void) { return 103; }
 
 }  // extern "C"

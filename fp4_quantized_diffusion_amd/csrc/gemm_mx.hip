@@ -42,6 +42,7 @@
 //    kGroupM tile-rows, so tiles that run together on an XCD share A and B
 //    panels in its L2.
 #include "gemm_common.h"
+#include "mx_common.h"
 
 namespace fp4r {
 namespace {
@@ -88,6 +89,8 @@ struct Problem {
   const float *a_ts, *b_ts;        // NVFP4-style tensor scales
   const float* ex;                 // Euler epilogue: the state x, and the step dt
   float dt;
+  uint8_t *qc, *qs;                // GELU + MXFP4 epilogue: output codes / scales (panel layout)
+  int qnc;                         //   and the output's 128-element chunks per panel row (n / 128)
   int64_t lda, ld_as, ldb, ld_bs;  // row-major layouts
   int M, N, kbytes, nblk;
   int nkc;                         // K chunks of 128 elements (stages per tile)
@@ -512,9 +515,12 @@ __device__ __forceinline__ void gather16(v16f v, float o[16]) {
 
 // Vector-memory instructions store_tile<FULL = true> issues per wave: per
 // MFMA tile two 16-byte stores (bf16) or four (fp32), plus four residual loads.
-// (RESID 2: the Euler epilogue, which also loads x.)
+// (RESID 2: the Euler epilogue, which also loads x; RESID 3: the GELU + MXFP4
+// epilogue, 2 code stores and 1 scale store per 32 rows.)
 template <int BF16OUT, int RESID>
-constexpr int full_tile_vmem() { return 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))); }
+constexpr int full_tile_vmem() {
+  return RESID == 3 ? 12 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4)));
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -675,6 +681,64 @@ __device__ __forceinline__ void store_tile_f32_lds(v16f acc[4][4], int m_base, i
   }
 }
 
+// Staging of one wave's codes in the GELU + MXFP4 epilogue: 32 rows of 64
+// code bytes (the wave's 128 columns), 72-byte pitch (conflict-free 8-byte
+// writes and 16-byte reads).
+constexpr int kQPitch = 72;
+constexpr int kQWaveBytes = 32 * kQPitch;
+
+// GELU + MXFP4 quantization of a full tile's output, written in the panel
+// layout for the next GEMM: z = bf16(sum) (the rounding the unfused path
+// stores), g = GELU(z) from the LDS table, and each 32-block along n
+// quantized by the MX rule -- the same operations as a bf16-out GEMM followed
+// by fp4_quantize(z, GELU prologue, panel layout), so the same bits. After
+// the lane-half swap lane (r, h) holds 16 consecutive n of row r; the other
+// 16 of its 32-block are in lane r + 32 (h ^ 1), so one exchange gives the
+// block amax. The wave's 128 columns are one chunk of the output's panel
+// layout (block `blk`), its 128 rows rows m0 .. m0 + 127 of the panel: codes
+// of 32 rows are staged in LDS and leave as 2 KiB contiguous (two 16-byte
+// stores per lane), the 4 scale bytes of a row as one 4-byte store.
+__device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
+                                                   uint8_t* stage, const float* tab) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
+  const int r32 = lane & 31, h = lane >> 5;
+  uint8_t* qc = p.qc + blk * 16384;
+  uint8_t* qs = p.qs + blk * 1024;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t sreg = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float o[16];
+      gather16(acc[i][j], o);
+      float g[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16, back to fp32 exactly
+        const uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
+        g[2 * e] = __uint_as_float(u << 16);
+        g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
+      uint32_t am = max(amax_bits8(g), amax_bits8(g + 8));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const uint32_t S = mx_scale(am);
+      const uint32_t w0 = mx_pack8(g, S), w1 = mx_pack8(g + 8, S);
+      *reinterpret_cast<uint2*>(stage + r32 * kQPitch + 16 * i + 8 * h) = make_uint2(w0, w1);
+      sreg |= S << (8 * i);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 16 * half + (lane >> 2), col = lane & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kQPitch + col * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(qc + (int64_t)(m0 + 32 * j + row) * 64 + col * 16));
+    }
+    if (h == 0) __builtin_nontemporal_store(sreg, reinterpret_cast<uint32_t*>(qs + (int64_t)(m0 + 32 * j + r32) * 4));
+    __builtin_amdgcn_sched_barrier(0);  // the next rows' staging writes stay behind these reads
+  }
+}
+
 // SCALE: multiply the sums by `mul` (the NVFP4-style tensor scales) before
 // the residual is added.
 // RESID 2 (the Euler epilogue, fp32 out): v = fl(sum + residual), then
@@ -786,9 +850,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
   const bool rows16 = BF16OUT ? (ldc % 8 == 0) : true;  // 16-byte aligned output rows
   __shared__ Stage<LD> s0, s1, s2, s3;
   // full tiles' epilogue through an LDS staging area (the MXFP4 ring leaves
-  // room for it; the NVFP4-style ring, with twice the scale bytes, does not)
-  constexpr bool EPI_LDS = !NV;
-  __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : 16];
+  // room for it; the NVFP4-style ring, with twice the scale bytes, does not);
+  // the GELU + MXFP4 epilogue has its own, smaller one and the GELU table
+  constexpr bool GELU_Q = RESID == 3;
+  constexpr bool EPI_LDS = !NV && !GELU_Q;
+  __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : (GELU_Q ? 4 * kQWaveBytes : 16)];
+  __shared__ float gtab[GELU_Q ? kGeluTab : 1];
+  if (GELU_Q) gelu_table_fill(gtab);  // visible to all waves after the first pipeline barrier
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
@@ -852,7 +920,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
     int mb = tm * BM + wm * 128, nb = tn * BN + wn * 128;
     asm volatile("" : "+v"(mb), "+v"(nb));  // keep epilogue address math out of the main loop
     counted = rows16 && (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
-    if (counted) {
+    if (GELU_Q) {
+      // every tile is full (the host launches this epilogue only for m, n multiples of 256)
+      store_tile_gelu_mx(acc, (int64_t)tm * p.qnc + 2 * tn + wn, wm * 128, p, epi_stage + wave * kQWaveBytes, gtab);
+      counted = true;
+    } else if (counted) {
       if (EPI_LDS && BF16OUT)
         store_tile_bf16_lds(acc, mb, nb, c, ldc, epi_stage + wave * kEpiWaveBytes);
       else if (EPI_LDS)
@@ -909,6 +981,8 @@ Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, cons
   p.a_ts = p.b_ts = nullptr;
   p.ex = nullptr;
   p.dt = 0.0f;
+  p.qc = p.qs = nullptr;
+  p.qnc = 0;
   p.lda = p.ld_as = p.ldb = p.ld_bs = 0;
   p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
   p.nkc = (int)((k + 127) >> 7);
@@ -954,6 +1028,23 @@ hipError_t launch_gemm_mx_panel_euler(const uint8_t* a, const uint8_t* as, const
   const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
   const unsigned grid = (unsigned)min(p.total, cu_count());
   gemm_fp4_kernel<0, 2, LD_PANEL><<<grid, kThreads, 0, st>>>(p, x_out, ldx, residual, nst4);
+  return hipGetLastError();
+}
+
+// The first solver linear with GELU and MXFP4 quantization of its output in
+// its epilogue: codes / scales of GELU(bf16(A_hat B_hat^T)) in the panel
+// layout of an [m, n] operand. m and n must be multiples of 256 (checked by
+// the caller).
+hipError_t launch_gemm_mx_panel_gelu(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                     int64_t m, int64_t n, int64_t k, uint8_t* out_codes, uint8_t* out_scales,
+                                     hipStream_t st) {
+  Problem p = make_problem(a, as, b, bs, m, n, k);
+  p.qc = out_codes;
+  p.qs = out_scales;
+  p.qnc = (int)(n / 128);
+  const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
+  const unsigned grid = (unsigned)min(p.total, cu_count());
+  gemm_fp4_kernel<0, 3, LD_PANEL><<<grid, kThreads, 0, st>>>(p, nullptr, 0, nullptr, nst4);
   return hipGetLastError();
 }
 

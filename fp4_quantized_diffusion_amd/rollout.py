@@ -14,8 +14,12 @@ uniform grid t_i = 1 - i/steps. Per block the device work is:
     fp4_gemm(A1, W1q) -> z (bf16)
     fp4_quantize(z, GELU prologue)        -> A2 (MXFP4)
     fp4_gemm(A2, W2q, residual = h) -> h  (fp32, in place)
-and per step euler_step(x, v = h). With the panel layout (the default) the
-last block's second GEMM and the Euler step are one call,
+and per step euler_step(x, v = h). With the panel layout (the default) and
+row counts that are multiples of 256, the first two lines are one call,
+fp4_gemm_panel_gelu(A1, W1q) -> A2, which applies the bf16 rounding, the GELU
+and the MXFP4 quantization in the GEMM's epilogue (bit-identical to the pair,
+without writing z); and the last block's second GEMM and the Euler step are
+one call,
 fp4_gemm_panel_euler(A2, W2q, residual = h, x) -> x_next, which applies
 x + dt (h + A2 W2q^T) in the GEMM's epilogue -- bit-identical to the GEMM into
 v followed by euler_step, without writing v or reading it back. The hidden
@@ -103,15 +107,22 @@ class Fp4Rollout:
         import torch
         rows, dim = x.shape
         hidden = self.w1[0].shape[0]
-        z = self._buf("z", (rows, hidden), torch.bfloat16, x.device)
+        # the first linear quantizes GELU of its own output (fp4_gemm_panel_gelu)
+        # when the shapes allow; otherwise z goes through HBM as bf16
+        fused = self.layout == "panel" and rows % 256 == 0 and hidden % 256 == 0
+        z = None if fused else self._buf("z", (rows, hidden), torch.bfloat16, x.device)
         src = x
         last = len(self.w1) - 1
         for b in range(len(self.w1)):
             a1 = self._call("quant_rmsnorm", lambda: fb.quantize(
                 src, self.fmt, prologue="rmsnorm", out=self._qbuf("a1", rows, dim, x.device)))
-            self._gemm(a1, self.q1[b], "bf16", out=z)
-            a2 = self._call("quant_gelu", lambda: fb.quantize(
-                z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
+            if fused:
+                a2 = self._call("gemm", lambda: fb.gemm_gelu(a1, self.q1[b], out=self._qbuf("a2", rows, hidden,
+                                                                                          x.device)))
+            else:
+                self._gemm(a1, self.q1[b], "bf16", out=z)
+                a2 = self._call("quant_gelu", lambda: fb.quantize(
+                    z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
             if b == last and step is not None:
                 t_cur, t_next, x_out = step
                 self._call("gemm", lambda: fb.gemm_euler(a2, self.q2[b], src, x, t_cur, t_next, out=x_out))

@@ -175,6 +175,26 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
                           void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
 
 /*
+ * fp4_gemm_panel_gelu -- the first solver linear of a velocity block with the
+ * GELU and the MXFP4 quantization of its output in its epilogue: the codes
+ * and scales of GELU(bf16(A_hat B_hat^T)) in the panel layout of an [m, n]
+ * operand, ready for the block's second linear (project page, "Two-Stage
+ * Pipeline": every solver linear runs FP4 x FP4; the synthetic velocity block
+ * is h + W2 GELU(W1 RMSNorm(h))). The hidden activation is rounded to bf16
+ * before the GELU, as the unfused path stores it, so the output is
+ * bit-identical to fp4_gemm_panel(..., FP4_DT_BF16) into z followed by
+ * fp4_quantize(z, FP4_LAYOUT_PANEL | FP4_PRO_GELU) -- without writing z.
+ *   fmt, a_*, b_*, m, n, k  as in fp4_gemm_panel; m and n multiples of 256
+ *                           (otherwise FP4_UNSUPPORTED: use the unfused pair).
+ *   out_codes, out_scales   the panel layout of [m, n] (fp4_panel_bytes(m, n)
+ *                           bytes each), 16-byte and 4-byte aligned.
+ */
+FP4_API fp4_status fp4_gemm_panel_gelu(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                               const uint8_t* b_codes, const uint8_t* b_scales,
+                               int64_t m, int64_t n, int64_t k,
+                               uint8_t* out_codes, uint8_t* out_scales, void* stream);
+
+/*
  * fp4_gemm_panel_euler -- the last block of the velocity network fused with
  * the Euler step that consumes it (aitrends summary, Stage-1 paragraph: a
  * 6-step FP4 ODE solve; the velocity is the residual stream plus the last

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 102
+    assert fq.fp4_abi_version() == 103
 
 
 def test_status_strings(lib):
@@ -172,3 +172,22 @@ def test_gemm_panel_euler_rejects(lib, kw):
 
 def test_gemm_panel_euler_nv_unsupported(lib):
     assert ge(fmt=1) == fq.binding.UNSUPPORTED
+
+
+def gg(**kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=256, n=256, k=64, oc=P, os=P3, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_panel_gelu(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(b_s=None), dict(oc=None), dict(os=None), dict(m=0), dict(k=48),
+    dict(oc=P + 8), dict(os=P3 + 2), dict(a=P + 8), dict(a_s=P3 + 2),
+])
+def test_gemm_panel_gelu_rejects(lib, kw):
+    assert gg(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=300), dict(n=128)])
+def test_gemm_panel_gelu_unsupported(lib, kw):
+    assert gg(**kw) == fq.binding.UNSUPPORTED

@@ -213,3 +213,32 @@ def test_gemm_euler_row_stride(gpu_lib):
     ref = gpu_lib.euler(dev(keep[:, :n]), v, 1.0, 5.0 / 6.0)
     np.testing.assert_array_equal(to_np(base)[:, :n], to_np(ref))
     np.testing.assert_array_equal(to_np(base)[:, n:], keep[:, n:])
+
+
+@pytest.mark.parametrize("m,n,k,wscale", [(256, 256, 256, 1.0), (512, 768, 1024, 1.0), (768, 512, 3072, 1.0),
+                                          (512, 512, 416, 1.0), (256, 512, 3072, 10.0), (256, 256, 64, 0.001)])
+def test_gemm_gelu_equals_gemm_then_gelu_quantize(gpu_lib, m, n, k, wscale):
+    """fp4_gemm_panel_gelu: bit-identical codes and scales to the bf16 GEMM
+    followed by the GELU quantizer (panel layout), also with hidden values far
+    in the GELU tails (weights x 10) and tiny ones (x 0.001)."""
+    qa = gpu_lib.quantize(dev(act(m, k, m + k)), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(wts(n, k, n + 1) * np.float32(wscale)), "mx", layout="panel")
+    z = gpu_lib.gemm(qa, qb, "bf16", out=torch.empty((m, n), dtype=torch.bfloat16, device=DEV))
+    ref = gpu_lib.quantize(z, "mx", prologue="gelu", layout="panel")
+    out = gpu_lib.gemm_gelu(qa, qb)
+    np.testing.assert_array_equal(to_np(out.scales), to_np(ref.scales))
+    np.testing.assert_array_equal(to_np(out.codes), to_np(ref.codes))
+
+
+def test_gemm_gelu_full_size_flux(gpu_lib):
+    """The FLUX-class first linear (36864 x 3072 -> 12288) in the benchmark's
+    launch configuration: fused and unfused outputs agree byte for byte."""
+    a, w = inputs.class_linear("flux", 1)
+    qa = gpu_lib.quantize(dev(a).to(torch.bfloat16), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(w).to(torch.bfloat16), "mx", layout="panel")
+    z = gpu_lib.gemm(qa, qb, "bf16", out=torch.empty((a.shape[0], w.shape[0]), dtype=torch.bfloat16, device=DEV))
+    ref = gpu_lib.quantize(z, "mx", prologue="gelu", layout="panel")
+    del z
+    out = gpu_lib.gemm_gelu(qa, qb)
+    assert torch.equal(out.scales, ref.scales)
+    assert torch.equal(out.codes, ref.codes)

@@ -94,3 +94,25 @@ def test_two_stream_schedule_matches_one_stream(gpu_lib, n_cand):
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(outs[0][5], noise)  # noise left intact
+
+
+def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
+    """Row counts that are multiples of 256 (2 candidates x 256 tokens per
+    chunk) take the fused first linear (GEMM + GELU + MXFP4 in one call) and
+    the fused Euler step on the panel layout; the row-major path runs every
+    step separately. Whole rollouts agree bit for bit."""
+    seed, n_cand, tokens, dim, hidden = 7, 4, 256, 256, 1024
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
+    u = torch.from_numpy(inputs.reward_vector(seed, dim)).to(DEV)
+    w1 = [torch.from_numpy(w[0]).to(DEV).bfloat16() for w in ws]
+    w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
+    outs = []
+    for layout in ("panel", "row"):
+        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, chunk=2, layout=layout)
+        xd = torch.from_numpy(noise).to(DEV)
+        r, top, bottom, rn = ro.run(xd)
+        torch.cuda.synchronize()
+        outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
