@@ -513,6 +513,16 @@ __device__ __forceinline__ void gather16(v16f v, float o[16]) {
   }
 }
 
+// One accumulator, read out of its AGPR where it is used: left to itself the
+// compiler copies most of the 256 accumulators to VGPRs at once at the end
+// of the K loop, which leaves the GELU epilogue no registers to overlap its
+// table lookups with.
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // Vector-memory instructions store_tile<FULL = true> issues per wave: per
 // MFMA tile two 16-byte stores (bf16) or four (fp32), plus four residual loads.
 // (RESID 2: the Euler epilogue, which also loads x; RESID 3: the GELU + MXFP4
@@ -691,13 +701,17 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // layout for the next GEMM: z = bf16(sum) (the rounding the unfused path
 // stores), g = GELU(z) from the LDS table, and each 32-block along n
 // quantized by the MX rule -- the same operations as a bf16-out GEMM followed
-// by fp4_quantize(z, GELU prologue, panel layout), so the same bits. After
-// the lane-half swap lane (r, h) holds 16 consecutive n of row r; the other
-// 16 of its 32-block are in lane r + 32 (h ^ 1), so one exchange gives the
-// block amax. The wave's 128 columns are one chunk of the output's panel
-// layout (block `blk`), its 128 rows rows m0 .. m0 + 127 of the panel: codes
-// of 32 rows are staged in LDS and leave as 2 KiB contiguous (two 16-byte
-// stores per lane), the 4 scale bytes of a row as one 4-byte store.
+// by fp4_quantize(z, GELU prologue, panel layout), so the same bits.
+// Straight from the MFMA layout: for MFMA tile (i, j) lane (r, h) holds
+// n = 32 i + 8 q + 4 h + s of row m = 32 j + r in register 4 q + s, i.e. half
+// of row r's 32-block, the other half in lane (r, h ^ 1); one exchange gives
+// the block amax, and each lane packs its 16 codes (bytes 4 q + 2 h and
+// 4 q + 2 h + 1 of the block's 16) into two words, of which one half swap
+// and two byte permutes make bytes 8 h .. 8 h + 7. The wave's 128 columns
+// are one chunk of the output's panel layout (block `blk`), its 128 rows
+// rows m0 .. m0 + 127 of the panel: codes of 32 rows are staged in LDS and
+// leave as 2 KiB contiguous (two 16-byte stores per lane), the 4 scale bytes
+// of a row as one 4-byte store.
 __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
                                                    uint8_t* stage, const float* tab) {
   int lane = threadIdx.x & 63;
@@ -710,21 +724,28 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
     uint32_t sreg = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float o[16];
-      gather16(acc[i][j], o);
       float g[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16, back to fp32 exactly
-        const uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o[2 * e], (__bf16)o[2 * e + 1]});
+      for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
+        const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
+        uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
+        asm("" : "+v"(u));  // one pair conversion (the compiler would convert the even element again on its own)
         g[2 * e] = __uint_as_float(u << 16);
         g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
-      uint32_t am = max(amax_bits8(g), amax_bits8(g + 8));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      uint32_t am = amax_bits<16>(g);
+      {  // the other lane half's amax: one of each swapped pair is this lane's own
+        const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+        am = max(sw[0], sw[1]);
+      }
       const uint32_t S = mx_scale(am);
-      const uint32_t w0 = mx_pack8(g, S), w1 = mx_pack8(g + 8, S);
+      // x: block bytes 2h, 2h+1, 4+2h, 5+2h (q = 0, 1); y: the same for q = 2, 3.
+      // After the swap lane half 0 holds x of both halves, half 1 y of both.
+      const auto xy = __builtin_amdgcn_permlane32_swap(mx_pack8(g, S), mx_pack8(g + 8, S), false, false);
+      const uint32_t w0 = __builtin_amdgcn_perm(xy[1], xy[0], 0x05040100u);
+      const uint32_t w1 = __builtin_amdgcn_perm(xy[1], xy[0], 0x07060302u);
       *reinterpret_cast<uint2*>(stage + r32 * kQPitch + 16 * i + 8 * h) = make_uint2(w0, w1);
       sreg |= S << (8 * i);
     }
@@ -854,6 +875,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
   // the GELU + MXFP4 epilogue has its own, smaller one and the GELU table
   constexpr bool GELU_Q = RESID == 3;
   constexpr bool EPI_LDS = !NV && !GELU_Q;
+  // The GELU + MXFP4 epilogue needs the registers that the next tile's first
+  // fragments would hold across it: it reads them afterwards.
+  constexpr bool DEFER_READ = GELU_Q;
   __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : (GELU_Q ? 4 * kQWaveBytes : 16)];
   __shared__ float gtab[GELU_Q ? kGeluTab : 1];
   if (GELU_Q) gelu_table_fill(gtab);  // visible to all waves after the first pipeline barrier
@@ -935,6 +959,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
       store_tile<BF16OUT, RESID, false, NV>(acc, mb, nb, p, c, ldc, residual, mul);
       __builtin_amdgcn_s_waitcnt(0);  // an edge tile's stores are not counted: drain them here
     }
+    // DEFER_READ: the next tile's first fragments, read by the last step,
+    // are read again here, so that they need no registers during the
+    // epilogue. Buffer s0 holds that stage (landed: the last step waited for
+    // it) until every wave has passed the next step's barrier.
+    if (DEFER_READ) read_stage<LD>(s0, 0, p.nblk, rn0, rm0, h, fa);
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing (past-the-end) loads before the workgroup exits
 }

@@ -55,25 +55,26 @@ __device__ __forceinline__ float phi_tail(float a_in) {
 }
 #undef FP4R_L2E
 
-__device__ __forceinline__ float phi_erfc(float z) {
-#pragma clang fp contract(off)
-  const float q = phi_tail(fabsf(z));
-  return z < 0.0f ? q : 1.0f - q;
+// z Phi(z) from q = Q(|z|): z q for z < 0 and z (1 - q) = z - |z| q for
+// z >= 0, i.e. max(z, -0) - |z| q, formed by one fma (one rounding). The
+// IEEE maximum (gfx950's v_maximum3_f32) orders -0 below +0, so the addend
+// is -0 for every z <= -0 and the result keeps the sign of z, zeros and
+// underflows included.
+__device__ __forceinline__ float gelu_q(float z, float q) {
+  return fmaf(-fabsf(z), q, __builtin_elementwise_maximum(z, -0.0f));
 }
 
 __device__ __forceinline__ float gelu_erfc(float z) {
-#pragma clang fp contract(off)
-  return z * phi_erfc(z);
+  return gelu_q(z, phi_tail(fabsf(z)));
 }
 
 // GELU of a bf16 input through a table of Q(|z|). A bf16 value has 8
 // significant bits, so the magnitudes 2^-22 .. 16 are 26 binades of 128
 // values plus 16 itself: 3329 entries (13 KiB in LDS), holding phi_tail of
-// exactly those values; Phi is then Q or 1 - Q by the sign, as in phi_erfc,
-// and z * Phi is bit-identical to gelu_erfc(z) for 2^-22 <= |z| <= 16, and
-// beyond 16 too, because phi_tail clamps |z| at 16. Below 2^-22 the index
-// clamps to the 2^-22 entry: Phi there differs from Phi(z) by less than
-// 0.4 * 2^-22 (2e-7 relative).
+// exactly those values, so gelu_q(z, table entry) is bit-identical to
+// gelu_erfc(z) for 2^-22 <= |z| <= 16, and beyond 16 too, because phi_tail
+// clamps |z| at 16. Below 2^-22 the index clamps to the 2^-22 entry: Phi
+// there differs from Phi(z) by less than 0.4 * 2^-22 (2e-7 relative).
 constexpr uint32_t kGeluLo = (127u - 22u) << 7;  // bf16 magnitude bits of 2^-22
 constexpr uint32_t kGeluHi = (127u + 4u) << 7;   // and of 16
 constexpr int kGeluTab = (int)(kGeluHi - kGeluLo + 1);
@@ -86,19 +87,25 @@ __device__ __forceinline__ void gelu_table_fill(float* tab) {
 }
 
 __device__ __forceinline__ float gelu_bf16(float z, const float* tab) {
-#pragma clang fp contract(off)
-  const uint32_t b = __float_as_uint(z) >> 16;  // z is a bf16 value: no bits are lost
-  const uint32_t m = min(max(b & 0x7FFFu, kGeluLo), kGeluHi);
-  const float q = tab[m - kGeluLo];
-  return z * ((b >> 15) ? q : 1.0f - q);
+  const uint32_t m = min(max((__float_as_uint(z) >> 16) & 0x7FFFu, kGeluLo), kGeluHi);  // z is a bf16 value
+  return gelu_q(z, tab[m - kGeluLo]);
 }
 
-__device__ __forceinline__ uint32_t amax_bits8(const float v[8]) {
-  uint32_t m = 0;
+// Bits of max |v_j| by the IEEE maximum (v_maximum3_f32, absolute values as
+// source modifiers): for non-NaN inputs the bits of the largest magnitude,
+// and a NaN input gives a NaN, whose exponent field, like that of every
+// larger-than-finite value, is all ones. mx_scale reads only the exponent
+// field, so it sees what the maximum of the bit patterns (sign cleared)
+// would give.
+template <int N>
+__device__ __forceinline__ uint32_t amax_bits(const float* v) {
+  float m = fabsf(v[0]);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
-  return m;
+  for (int j = 1; j < N; ++j) m = __builtin_elementwise_maximum(m, fabsf(v[j]));
+  return __float_as_uint(m);
 }
+
+__device__ __forceinline__ uint32_t amax_bits8(const float v[8]) { return amax_bits<8>(v); }
 
 // MX: E8M0 scale byte and the packed codes of one octet, given the block amax bits.
 // S = max(biased_exponent(amax) - 2, 0) is floor(log2 amax) - 2 + 127 clamped at
