@@ -3,10 +3,10 @@
 // The rollout re-quantizes its weights every iteration and quantizes the
 // activations entering every solver linear (Sol-RL project page, "Two-Stage
 // Pipeline"). Both are HBM-bound streams: the kernels read each input element
-// once (RMSNorm: the row's second read hits L2), write half a byte of code per
-// element and one scale byte per block, and keep every decision in integer
-// or exactly-rounded fp32 arithmetic so the codes are bit-identical to the
-// format's definition.
+// once (RMSNorm rows longer than 4096 elements twice, the second time from
+// L2), write half a byte of code per element and one scale byte per block,
+// and keep every decision in integer or exactly-rounded fp32 arithmetic so
+// the codes are bit-identical to the format's definition.
 //
 // Thread layout: every thread owns 8 consecutive elements of one row
 // ("octet"); the 4 (MX, block 32) or 2 (NV, block 16) threads of a block are
@@ -190,8 +190,9 @@ __device__ float block_sum(float v, float* sh) {
   return t;
 }
 
-// RMSNorm prologue: one workgroup per row. Pass 1 sums squares, pass 2
-// normalizes (y = x * (1 / sqrt(mean + 1e-6)), unit gain) and quantizes.
+// RMSNorm prologue for rows of more than 4096 elements: one workgroup per
+// row. Pass 1 sums squares, pass 2 normalizes (y = x * (1 / sqrt(mean +
+// 1e-6)), unit gain) and quantizes.
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_kernel(
     const void* __restrict__ x, int64_t k, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
@@ -263,6 +264,88 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_panel_kernel(
     *reinterpret_cast<uint32_t*>(codes + (blk * 256 + rr) * 64 + (oct & 15) * 4) = valid ? mx_pack8(v, S) : 0u;
     if ((oct & 3) == 0) scales[(blk * 256 + rr) * 4 + ((oct & 15) >> 2)] = (uint8_t)(valid ? S : 127u);
   }
+}
+
+// RMSNorm prologue with the row in registers: one wave per row (four rows
+// per workgroup), lane l holding octets l, l + 64, ..., l + 64 (NO - 1), so
+// the row is read once and no workgroup-wide synchronization is needed. The
+// sum of squares runs over the lane's octets in order, then over a fixed
+// xor-shuffle tree (fp32 addition commutes, so every lane ends with the same
+// total). The row-major and panel layouts run this same arithmetic, for any
+// K with ceil(K / 512) <= 8 in both (K <= 4096); larger K takes the two-pass
+// kernels above in both layouts. Octets past K (panel padding) hold zeros,
+// which add nothing to the sum. PANEL: rows past `rows` up to the panel edge
+// (nrows) write padding only.
+template <int BF16, int NO, bool PANEL>
+__global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_wave_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t nrows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales, int64_t nc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // uniform over the wave
+  const bool row_valid = row < rows;
+  const int opr = (int)(k >> 3);
+  float v[NO][8];
+#pragma unroll
+  for (int t = 0; t < NO; ++t) {
+    const int o = lane + 64 * t;
+    if (row_valid && o < opr) {
+      load8<BF16>(x, row * ldx + (int64_t)o * 8, v[t]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[t][j] = 0.f;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < NO; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[t][j] * v[t][j];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float inv = 1.0f / sqrtf(ss / (float)k + 1e-6f);
+  const int64_t pnl = row >> 8, rr = row & 255;
+#pragma unroll
+  for (int t = 0; t < NO; ++t) {
+    const int o = lane + 64 * t;
+    const bool valid = row_valid && o < opr;  // shared by a 32-block's 4 octets
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[t][j] = v[t][j] * inv;
+    uint32_t S;
+    const uint32_t w = mx_block(v[t], S);
+    if (PANEL) {
+      if (o < nc * 16) {
+        const int64_t blk = pnl * nc + (o >> 4);
+        *reinterpret_cast<uint32_t*>(codes + (blk * 256 + rr) * 64 + (o & 15) * 4) = valid ? w : 0u;
+        if ((o & 3) == 0) scales[(blk * 256 + rr) * 4 + ((o & 15) >> 2)] = (uint8_t)(valid ? S : 127u);
+      }
+    } else if (valid) {
+      *reinterpret_cast<uint32_t*>(codes + row * ld_codes + (int64_t)o * 4) = w;
+      if ((o & 3) == 0) scales[row * ld_scales + (o >> 2)] = (uint8_t)S;
+    }
+  }
+}
+
+// Launch the register-resident RMSNorm quantizer when the row fits (NO <= 8
+// octets per lane); false otherwise.
+template <bool PANEL>
+bool launch_rmsnorm_wave(const void* x, int x_bf16, int64_t rows, int64_t nrows, int64_t k, int64_t ldx,
+                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, int64_t nc,
+                         hipStream_t st) {
+  const int64_t octs = PANEL ? nc * 16 : (k >> 3);
+  const int64_t no = (octs + 63) / 64;
+  if (no < 1 || no > 8) return false;
+  const unsigned g = (unsigned)((nrows + 3) / 4);
+#define FP4R_RMS(B, N)                                                                                            quant_mx_rmsnorm_wave_kernel<B, N, PANEL><<<g, kThreads, 0, st>>>(x, rows, nrows, k, ldx, codes, ld_codes, scales,                                                                    ld_scales, nc)
+#define FP4R_RMS_NO(B)            switch (no) {                     case 1: FP4R_RMS(B, 1); break;     case 2: FP4R_RMS(B, 2); break;     case 3: FP4R_RMS(B, 3); break;     case 4: FP4R_RMS(B, 4); break;     case 5: FP4R_RMS(B, 5); break;     case 6: FP4R_RMS(B, 6); break;     case 7: FP4R_RMS(B, 7); break;     default: FP4R_RMS(B, 8); break;   }
+  if (x_bf16) {
+    FP4R_RMS_NO(1)
+  } else {
+    FP4R_RMS_NO(0)
+  }
+#undef FP4R_RMS_NO
+#undef FP4R_RMS
+  return true;
 }
 
 // ---------------------------- NVFP4-style ----------------------------------
@@ -421,6 +504,8 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            int prologue, hipStream_t st) {
   if (prologue == PRO_RMSNORM) {
+    if (launch_rmsnorm_wave<false>(x, x_bf16, rows, rows, k, ldx, codes, ld_codes, scales, ld_scales, 0, st))
+      return hipGetLastError();
     if (x_bf16)
       quant_mx_rmsnorm_kernel<1><<<(unsigned)rows, kThreads, 0, st>>>(x, k, ldx, codes, ld_codes, scales, ld_scales);
     else
@@ -446,6 +531,8 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
                                  uint8_t* scales, int prologue, hipStream_t st) {
   const int64_t panels = (rows + 255) >> 8, nc = (k + 127) >> 7;
   if (prologue == PRO_RMSNORM) {
+    if (launch_rmsnorm_wave<true>(x, x_bf16, rows, panels * 256, k, ldx, codes, 0, scales, 0, nc, st))
+      return hipGetLastError();
     const unsigned g = (unsigned)(panels * 256);
     if (x_bf16)
       quant_mx_rmsnorm_panel_kernel<1><<<g, kThreads, 0, st>>>(x, rows, k, ldx, codes, scales, nc);

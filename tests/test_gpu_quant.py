@@ -184,6 +184,26 @@ def test_mx_prologues(gpu_lib, prologue, dtype):
 
 
 @pytest.mark.parametrize("layout", ["row", "panel"])
+@pytest.mark.parametrize("rows,k", [(5, 32), (67, 512), (9, 544), (130, 3072), (33, 4096), (6, 4128), (3, 8192)])
+def test_mx_rmsnorm_row_lengths(gpu_lib, layout, rows, k):
+    """RMSNorm prologue at row lengths around the register-resident kernel's
+    limits (one to eight octets per lane, K <= 4096; the two-pass kernel
+    beyond), with row counts that leave a workgroup's waves idle: the same
+    2e-6 decision band against the float64 oracle."""
+    rng = np.random.default_rng(k + rows)
+    x = (rng.standard_normal((rows, k)) * 3).astype(np.float32)
+    q = gpu_lib.quantize(torch.from_numpy(x).to(DEV), "mx", prologue="rmsnorm", layout=layout)
+    if layout == "panel":
+        gc, gs, pad = panel_to_rows(to_np(q.codes), to_np(q.scales), rows, k)
+        assert (pad["code_rows"] == 0).all() and (pad["code_cols"] == 0).all()
+        assert (pad["scale_rows"] == 127).all() and (pad["scale_cols"] == 127).all()
+    else:
+        gc, gs = to_np(q.codes)[:, : k // 2], to_np(q.scales)[:, : k // 32]
+    bad, flips = mx_codes_near_boundary_ok(orollout.rmsnorm(x.astype(np.float64)), gc, gs)
+    assert bad == 0, (bad, flips)
+
+
+@pytest.mark.parametrize("layout", ["row", "panel"])
 def test_mx_gelu_negative_tail(gpu_lib, layout):
     """GELU blocks drawn from narrow bands of the negative tail ([-3.5, -2.5]
     down to [-10, -7]): every block's scale and codes are then set by
