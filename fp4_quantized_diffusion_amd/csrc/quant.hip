@@ -328,6 +328,21 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rmsnorm_wave_kernel(
 
 // Launch the register-resident RMSNorm quantizer when the row fits (NO <= 8
 // octets per lane); false otherwise.
+template <int BF16, bool PANEL, int NO = 1>
+void launch_rmsnorm_wave_no(int64_t no, unsigned g, const void* x, int64_t rows, int64_t nrows, int64_t k,
+                            int64_t ldx, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                            int64_t nc, hipStream_t st) {
+  if constexpr (NO < 8) {
+    if (no > NO) {
+      launch_rmsnorm_wave_no<BF16, PANEL, NO + 1>(no, g, x, rows, nrows, k, ldx, codes, ld_codes, scales, ld_scales,
+                                                  nc, st);
+      return;
+    }
+  }
+  quant_mx_rmsnorm_wave_kernel<BF16, NO, PANEL>
+      <<<g, kThreads, 0, st>>>(x, rows, nrows, k, ldx, codes, ld_codes, scales, ld_scales, nc);
+}
+
 template <bool PANEL>
 bool launch_rmsnorm_wave(const void* x, int x_bf16, int64_t rows, int64_t nrows, int64_t k, int64_t ldx,
                          uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, int64_t nc,
@@ -336,15 +351,10 @@ bool launch_rmsnorm_wave(const void* x, int x_bf16, int64_t rows, int64_t nrows,
   const int64_t no = (octs + 63) / 64;
   if (no < 1 || no > 8) return false;
   const unsigned g = (unsigned)((nrows + 3) / 4);
-#define FP4R_RMS(B, N)                                                                                            quant_mx_rmsnorm_wave_kernel<B, N, PANEL><<<g, kThreads, 0, st>>>(x, rows, nrows, k, ldx, codes, ld_codes, scales,                                                                    ld_scales, nc)
-#define FP4R_RMS_NO(B)            switch (no) {                     case 1: FP4R_RMS(B, 1); break;     case 2: FP4R_RMS(B, 2); break;     case 3: FP4R_RMS(B, 3); break;     case 4: FP4R_RMS(B, 4); break;     case 5: FP4R_RMS(B, 5); break;     case 6: FP4R_RMS(B, 6); break;     case 7: FP4R_RMS(B, 7); break;     default: FP4R_RMS(B, 8); break;   }
-  if (x_bf16) {
-    FP4R_RMS_NO(1)
-  } else {
-    FP4R_RMS_NO(0)
-  }
-#undef FP4R_RMS_NO
-#undef FP4R_RMS
+  if (x_bf16)
+    launch_rmsnorm_wave_no<1, PANEL>(no, g, x, rows, nrows, k, ldx, codes, ld_codes, scales, ld_scales, nc, st);
+  else
+    launch_rmsnorm_wave_no<0, PANEL>(no, g, x, rows, nrows, k, ldx, codes, ld_codes, scales, ld_scales, nc, st);
   return true;
 }
 
