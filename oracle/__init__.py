@@ -37,7 +37,10 @@ Parity status per function:
   rollout.gelu / rmsnorm ...... pinned (normal-CDF table values, the identity
                                 GELU(z) - GELU(-z) = z, Mills-ratio tail series;
                                 hand row, constant rows, mean-square identity)
+  lora.merge .................. pinned (exact rationals on small non-square
+                                shapes, all-ones and rank-one closed forms,
+                                s = 0 and B = 0 identities)
   rollout (composite) ......... parity unpinned beyond the pinned pieces it
                                 composes (statistical comparison only)
 """
-from . import e2m1, mxfp4, nvfp4, gemm, euler, reward, rollout  # noqa: F401
+from . import e2m1, mxfp4, nvfp4, gemm, euler, reward, rollout, lora  # noqa: F401
