@@ -248,7 +248,19 @@ def class_benchmarks(dev, n_sets=4):
                 wq_us = time_launches([lambda i=i: fq.quantize(draws[i][1], "mx", out=qb[i]) for i in range(n_sets)])
                 mem[f"mx_quantize_weight_{name}_{n}x{k}"] = {"us": [round(v, 1) for v in wq_us],
                                                              "tbps": round(n * k * 2.53125 / wq_us[0] / 1e6, 3)}
-                del qn_a, qn_b
+                # LoRA (rank 32, fp32 adapters) merged and re-quantized in one pass: the
+                # weight's 2.53 B/elem plus the adapters, and 2 r + 2 fp32 FLOP per element
+                r = 32
+                lb = [torch.randn(n, r, device=dev) * 0.01 for _ in range(n_sets)]
+                la = [torch.randn(r, k, device=dev) * 0.05 for _ in range(n_sets)]
+                lq_us = time_launches([lambda i=i: fq.quantize_lora(draws[i][1], lb[i], la[i], 2.0, out=qb[i])
+                                       for i in range(n_sets)])
+                lbytes = n * k * 2.53125 + (n + k) * r * 4
+                mem[f"mx_quantize_lora_r{r}_weight_{name}_{n}x{k}"] = {
+                    "us": [round(v, 1) for v in lq_us], "tbps": round(lbytes / lq_us[0] / 1e6, 3),
+                    "fp32_tflops": round((2 * r + 2) * n * k / lq_us[0] / 1e6, 2),
+                    "vs_plain_requantize": round(lq_us[0] / wq_us[0], 2)}
+                del qn_a, qn_b, lb, la
             gemms[key] = g
             log(f"class {key}: mxfp4 {f_us[0]:.0f} us ({g['mxfp4_tflops']} TF/s), bf16 {b_us[0]:.0f} us "
                 f"({g['bf16_tflops']} TF/s) [{time.time() - t0:.1f}s]")

@@ -2,11 +2,11 @@
 
 Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
-  * the raw entry points under their C names (fp4_quantize, fp4_panel_bytes,
+  * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_panel_bytes,
     fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
-  * torch-tensor helpers (quantize, gemm, gemm_gelu, gemm_euler, euler, proxy_reward, select) that
+  * torch-tensor helpers (quantize, quantize_lora, gemm, gemm_gelu, gemm_euler, euler, proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
 Loading fails loudly when the library has not been built; there is no
@@ -29,6 +29,8 @@ _LIB = None
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 _SIGS = {
     "fp4_quantize": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
+    "fp4_quantize_lora": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _i32, _i64, _f32, _p, _i64, _p, _i64,
+                          _i32, _p],
     "fp4_panel_bytes": [_i64, _i64, _p, _p],
     "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
@@ -74,6 +76,12 @@ def status_str(s):
 def fp4_quantize(fmt, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales, tensor_scale, flags, stream):
     return load_library().fp4_quantize(fmt, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales,
                                        tensor_scale, flags, stream)
+
+
+def fp4_quantize_lora(fmt, w, w_dtype, rows, k, ldw, lora_b, ld_b, lora_a, ld_a, ab_dtype, rank, scale, codes,
+                      ld_codes, scales, ld_scales, flags, stream):
+    return load_library().fp4_quantize_lora(fmt, w, w_dtype, rows, k, ldw, lora_b, ld_b, lora_a, ld_a, ab_dtype,
+                                            rank, scale, codes, ld_codes, scales, ld_scales, flags, stream)
 
 
 def fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts, m, n, k, c, c_dtype,
@@ -177,22 +185,38 @@ def panel_bytes(rows, k):
     return cb.value, sb.value
 
 
+def _alloc_panel(rows, k, device):
+    torch = _torch()
+    cb, sb = panel_bytes(rows, k)
+    return QTensor(torch.empty(cb, dtype=torch.uint8, device=device), torch.empty(sb, dtype=torch.uint8, device=device),
+                   None, FMT_MX, k, "panel", rows)
+
+
+def _alloc_rows(rows, k, device, f):
+    torch = _torch()
+    blk = 32 if f == FMT_MX else 16
+    ldc = ((k // 2 + 15) // 16) * 16
+    codes = torch.empty((rows, ldc), dtype=torch.uint8, device=device)
+    # scale rows padded to a multiple of 4 bytes: the GEMM then loads each
+    # stage's scale bytes as whole words
+    lds = ((max(k // blk, 1) + 3) // 4) * 4
+    scales = torch.empty((rows, lds), dtype=torch.uint8, device=device)[:, : max(k // blk, 1)]
+    ts = torch.empty(1, dtype=torch.float32, device=device) if f == FMT_NV else None
+    return QTensor(codes, scales, ts, f, k)
+
+
 def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None, layout="row"):
     """x: 2-D CUDA tensor (fp32 or bf16, unit inner stride). prologue: None,
     "rmsnorm" or "gelu" (MX only). tensor_scale: a 1-element fp32 tensor whose
     value is used as s_g (NV only). layout: "row" or "panel" (MX only).
     out: a QTensor to write into (its layout wins)."""
-    torch = _torch()
     if not _row_view_ok(x):
         raise ValueError("x must be 2-D with unit inner stride")
     f = {"mx": FMT_MX, "nv": FMT_NV}[fmt]
     rows, k = x.shape
-    blk = 32 if f == FMT_MX else 16
     flags = {None: 0, "rmsnorm": PRO_RMSNORM, "gelu": PRO_GELU}[prologue]
     if out is None and layout == "panel":
-        cb, sb = panel_bytes(rows, k)
-        out = QTensor(torch.empty(cb, dtype=torch.uint8, device=x.device),
-                      torch.empty(sb, dtype=torch.uint8, device=x.device), None, f, k, "panel", rows)
+        out = _alloc_panel(rows, k, x.device)
     if out is not None and out.layout == "panel":
         if out.rows != rows or out.k != k:
             raise ValueError("out was allocated for another shape")
@@ -201,16 +225,7 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None, layout="ro
         _check(st, "fp4_quantize")
         return out
     if out is None:
-        ldc = ((k // 2 + 15) // 16) * 16
-        codes = torch.empty((rows, ldc), dtype=torch.uint8, device=x.device)
-        # scale rows padded to a multiple of 4 bytes: the GEMM then loads each
-        # stage's scale bytes as whole words
-        lds = ((max(k // blk, 1) + 3) // 4) * 4
-        scales = torch.empty((rows, lds), dtype=torch.uint8, device=x.device)[:, : max(k // blk, 1)]
-        ts = None
-        if f == FMT_NV:
-            ts = torch.empty(1, dtype=torch.float32, device=x.device)
-        out = QTensor(codes, scales, ts, f, k)
+        out = _alloc_rows(rows, k, x.device, f)
     ts = out.tensor_scale
     if f == FMT_NV and tensor_scale is not None:
         ts.copy_(tensor_scale.reshape(1))
@@ -218,6 +233,35 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None, layout="ro
     st = fp4_quantize(f, x.data_ptr(), _dtype_code(x), rows, k, x.stride(0), out.codes.data_ptr(),
                       out.codes.stride(0), out.scales.data_ptr(), out.scales.stride(0), _ptr(ts), flags, _stream())
     _check(st, "fp4_quantize")
+    return out
+
+
+def quantize_lora(w, lora_b, lora_a, scale, out=None, layout="row"):
+    """MXFP4 QTensor of W + scale * (B A) -- a LoRA adapter merged into the
+    weight in fp32 and re-quantized in one pass (fp4_quantize_lora).
+    w: [rows, k] fp32 or bf16; lora_b: [rows, rank] and lora_a: [rank, k] of
+    one dtype (fp32 or bf16); all 2-D with unit inner stride. layout: "row" or
+    "panel"; out: a QTensor to write into (its layout wins)."""
+    for t in (w, lora_b, lora_a):
+        if not _row_view_ok(t):
+            raise ValueError("w, lora_b and lora_a must be 2-D with unit inner stride")
+    if lora_b.dtype != lora_a.dtype:
+        raise ValueError("lora_b and lora_a must have one dtype")
+    rows, k = w.shape
+    rank = lora_b.shape[1]
+    if lora_b.shape[0] != rows or tuple(lora_a.shape) != (rank, k):
+        raise ValueError("shapes do not chain: w [rows, k], lora_b [rows, rank], lora_a [rank, k]")
+    if out is None:
+        out = _alloc_panel(rows, k, w.device) if layout == "panel" else _alloc_rows(rows, k, w.device, FMT_MX)
+    if out.rows not in (0, rows) or out.k != k or out.fmt != FMT_MX:
+        raise ValueError("out was allocated for another shape or format")
+    panel = out.layout == "panel"
+    st = fp4_quantize_lora(FMT_MX, w.data_ptr(), _dtype_code(w), rows, k, w.stride(0), lora_b.data_ptr(),
+                           lora_b.stride(0), lora_a.data_ptr(), lora_a.stride(0), _dtype_code(lora_a), rank,
+                           float(scale), out.codes.data_ptr(), 0 if panel else out.codes.stride(0),
+                           out.scales.data_ptr(), 0 if panel else out.scales.stride(0),
+                           LAYOUT_PANEL if panel else 0, _stream())
+    _check(st, "fp4_quantize_lora")
     return out
 
 

@@ -29,6 +29,7 @@ HIP_COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-fvisibil
               "-fhip-fp32-correctly-rounded-divide-sqrt", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
+    "lora.hip": ["-ffp-contract=off"],
     "gemm_mx.hip": [],
     "gemm_nv.hip": [],
     "euler.hip": [],

@@ -14,7 +14,7 @@
 // reads are 16-byte vector loads, code writes one 32-bit store per thread.
 // This file is compiled with -ffp-contract=off: every fp32 operation below
 // rounds on its own.
-#include "mx_common.h"
+#include "quant_common.h"
 
 namespace fp4r {
 namespace {
@@ -35,24 +35,6 @@ __device__ __forceinline__ void st_out(T* p, T v) {
 }
 
 enum { PRO_NONE = 0, PRO_RMSNORM = 1, PRO_GELU = 2 };
-
-template <int BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
-  if (BF16) {
-    uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(w[j] << 16);
-      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
 
 // Elementwise prologue of one loaded octet (tab: the GELU table, bf16 input).
 template <int BF16, int PRO>
@@ -77,16 +59,6 @@ struct GeluLds<1, PRO_GELU> {
     return tab;
   }
 };
-
-// Block scale of a 32-block held as 4 octets in lanes 4q..4q+3, and the
-// octet's code word.
-__device__ __forceinline__ uint32_t mx_block(const float v[8], uint32_t& S) {
-  uint32_t am = amax_bits8(v);
-  am = max(am, (uint32_t)__shfl_xor((int)am, 1));
-  am = max(am, (uint32_t)__shfl_xor((int)am, 2));
-  S = mx_scale(am);
-  return mx_pack8(v, S);
-}
 
 // Steps a thread works on at once in the elementwise kernels: their loads
 // are all issued before the first is used, so each wave keeps four 16-byte

@@ -55,8 +55,12 @@ from . import binding as fb
 
 class Fp4Rollout:
     def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None,
-                 layout="panel", overlap=False):
+                 layout="panel", overlap=False, lora=None):
         """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
+        lora: optional (lora1, lora2), one entry per block each, None or a
+        LoRA adapter (B, A, scale) of that weight; the per-iteration
+        re-quantization then merges it in the same pass (fp4_quantize_lora).
+        Update adapters between iterations with set_lora.
         chunk: candidates per pass through the network on one stream (None =
         all); ignored by the two-stream schedule.
         overlap: two-stream schedule over two halves of the candidates (needs
@@ -75,13 +79,27 @@ class Fp4Rollout:
         self.timer = timer
         self.q1 = self.q2 = None
         self._bufs = {}
+        self.set_lora(lora)
+
+    def set_lora(self, lora):
+        """Adapters for the next re-quantization: None, or (lora1, lora2) as
+        in the constructor."""
+        n = len(self.w1)
+        self.lora1, self.lora2 = ([None] * n, [None] * n) if lora is None else (list(lora[0]), list(lora[1]))
+        if len(self.lora1) != n or len(self.lora2) != n:
+            raise ValueError("one adapter entry (or None) per block and weight")
 
     def requantize(self):
-        """Per-iteration weight re-quantization (all weights, on device)."""
-        self.q1 = [fb.quantize(w, self.fmt, out=None if self.q1 is None else self.q1[i], layout=self.layout)
-                   for i, w in enumerate(self.w1)]
-        self.q2 = [fb.quantize(w, self.fmt, out=None if self.q2 is None else self.q2[i], layout=self.layout)
-                   for i, w in enumerate(self.w2)]
+        """Per-iteration weight re-quantization (all weights, on device), with
+        each weight's LoRA adapter merged in when one is set."""
+        def one(w, ad, prev):
+            if ad is None:
+                return fb.quantize(w, self.fmt, out=prev, layout=self.layout)
+            b, a, scale = ad
+            return fb.quantize_lora(w, b, a, scale, out=prev, layout=self.layout)
+
+        self.q1 = [one(w, self.lora1[i], None if self.q1 is None else self.q1[i]) for i, w in enumerate(self.w1)]
+        self.q2 = [one(w, self.lora2[i], None if self.q2 is None else self.q2[i]) for i, w in enumerate(self.w2)]
 
     def _buf(self, name, shape, dtype, device):
         import torch

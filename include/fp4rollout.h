@@ -121,6 +121,40 @@ FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t row
                         float* tensor_scale, int flags, void* stream);
 
 /*
+ * fp4_quantize_lora -- merge a LoRA adapter into a weight and re-quantize the
+ * result to MXFP4, in one pass: the merged weight is never written.
+ *
+ * The policy is trained with LoRA adapters (rank 32 on the aitrends summary)
+ * and after each update the adapted weights are re-quantized at run time for
+ * the next FP4 rollout, with no compile step (aitrends summary, Stage-2
+ * paragraph; project page, "Two-Stage Pipeline", Stage 2). The merge is the
+ * standard LoRA form W' = W + scale * (B A), evaluated in fp32 as
+ *     acc = sum over j = 0 .. rank-1, in order, of fmaf(B[n, j], A[j, k], acc)
+ *     W'[n, k] = fmaf(scale, acc, W[n, k])
+ * and W' is then quantized exactly as fp4_quantize(FP4_FMT_MX, W', ...) would.
+ *
+ *   fmt          FP4_FMT_MX (FP4_FMT_NV: FP4_UNSUPPORTED).
+ *   w            [rows, ldw] weight (nn.Linear layout: rows = output features,
+ *                k = input features) of type w_dtype, with the alignment and
+ *                size rules of fp4_quantize's x.
+ *   lora_b       [rows, ld_b] elements (ld_b >= rank), B of the adapter.
+ *   lora_a       [rank, ld_a] elements (ld_a >= k), A of the adapter.
+ *   ab_dtype     element type of lora_a and lora_b (FP4_DT_F32 or FP4_DT_BF16);
+ *                both aligned to their element size.
+ *   rank         1 .. 64.
+ *   scale        the adapter's scale (alpha / rank in the usual
+ *                parametrisation); finite.
+ *   codes, ld_codes, scales, ld_scales
+ *                as for fp4_quantize with FP4_FMT_MX (row-major, or the panel
+ *                layout with FP4_LAYOUT_PANEL and ld_codes = ld_scales = 0).
+ *   flags        0 or FP4_LAYOUT_PANEL.
+ */
+FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_t rows, int64_t k, int64_t ldw,
+                        const void* lora_b, int64_t ld_b, const void* lora_a, int64_t ld_a, int ab_dtype,
+                        int64_t rank, float scale, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                        int64_t ld_scales, int flags, void* stream);
+
+/*
  * fp4_panel_bytes -- sizes of the panel layout of a [rows, k] MXFP4 operand:
  *   *code_bytes  = ceil(rows / 256) * ceil(k / 128) * 16384,
  *   *scale_bytes = ceil(rows / 256) * ceil(k / 128) * 1024.

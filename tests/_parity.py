@@ -20,12 +20,14 @@ def gemm_within_tol(c_gpu, c_exact, s_abs, bf16_out=False, rel=1e-4):
     return (not bad.any()), float((err / np.maximum(tol, 1e-300)).max())
 
 
-def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6):
+def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6, band=None):
     """Codes/scales of a quantizer whose input the GPU computes in fp32 (a
     fused prologue) against the float64 reference input x_ref: every code and
-    scale must equal the oracle's, except where x_ref sits within `rel` of a
-    decision point (a scale binade edge for the block max, or an E2M1
-    threshold) -- there either neighbour is a valid result.
+    scale must equal the oracle's, except where x_ref sits within `rel`
+    (relative) -- plus `band` (absolute, per element, when given: a bound on
+    the GPU's fp32 evaluation error) -- of a decision point (a scale binade
+    edge for the block max, or an E2M1 threshold); there either neighbour is a
+    valid result.
     Returns (n_exact_mismatch_outside_tolerance, n_boundary_flips)."""
     x_ref = np.asarray(x_ref, dtype=np.float64)
     rows, k = x_ref.shape
@@ -38,10 +40,14 @@ def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6):
     flips = 0
     xb = x_ref.reshape(rows, k // 32, 32)
     amax = np.abs(xb).max(-1)
-    # scale: may differ by one only when amax is within rel of a power of two
+    band = np.zeros_like(x_ref) if band is None else np.broadcast_to(np.asarray(band, dtype=np.float64), x_ref.shape)
+    bmax = band.reshape(rows, k // 32, 32).max(-1)
+    # scale: may differ by one only when amax is within the tolerance of a power of two
     ds = gs != osc
     if ds.any():
-        near_pow2 = np.abs(np.log2(np.maximum(amax, 1e-300)) - np.round(np.log2(np.maximum(amax, 1e-300)))) < rel * 2
+        l2 = np.log2(np.maximum(amax, 1e-300))
+        p2 = np.exp2(np.round(l2))
+        near_pow2 = (np.abs(l2 - np.round(l2)) < rel * 2) | (np.abs(amax - p2) <= bmax)
         okay = ds & near_pow2 & (np.abs(gs - osc) == 1)
         bad += int((ds & ~okay).sum())
         flips += int(okay.sum())
@@ -51,13 +57,25 @@ def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6):
     if dc.any():
         E = np.repeat(osc - 127, 32, axis=1)
         y = np.abs(np.ldexp(x_ref, -E))
+        yb = np.ldexp(band, -E)
         thr = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-        dist = np.min(np.abs(y[..., None] - thr) / thr, axis=-1)
+        slack = np.min(np.abs(y[..., None] - thr) - rel * thr - yb[..., None], axis=-1)
         adjacent = np.abs((gn & 7).astype(int) - (on & 7).astype(int)) == 1
-        okay = dc & (dist < rel) & adjacent & ((gn & 8) == (on & 8))
+        okay_mag = (slack < 0) & adjacent & ((gn & 8) == (on & 8))
+        # the sign (decision point 0) may differ only for a value within the band of zero
+        okay_sign = (band > 0) & (np.abs(x_ref) <= band) & ((gn & 7) == 0) & ((on & 7) == 0)
+        okay = dc & (okay_mag | okay_sign)
         bad += int((dc & ~okay).sum())
         flips += int(okay.sum())
     return bad, flips
+
+
+def lora_merge_band(w, b, a, scale):
+    """Bound on |fp32 LoRA merge - exact| for the GPU's evaluation order
+    (rank fmas into acc, then fma(scale, acc, w); every input exact in fp32):
+    (rank + 2) 2^-24 (|W| + |scale| |B| |A|)."""
+    w, b, a = (np.abs(np.asarray(t, dtype=np.float64)) for t in (w, b, a))
+    return (b.shape[1] + 2) * 2.0 ** -24 * (w + abs(float(scale)) * (b @ a))
 
 
 def panel_to_rows(codes, scales, rows, k):

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 103
+    assert fq.fp4_abi_version() == 104
 
 
 def test_status_strings(lib):
@@ -191,3 +191,36 @@ def test_gemm_panel_gelu_rejects(lib, kw):
 @pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=300), dict(n=128)])
 def test_gemm_panel_gelu_unsupported(lib, kw):
     assert gg(**kw) == fq.binding.UNSUPPORTED
+
+
+def ql(**kw):
+    a = dict(fmt=0, w=P, w_dtype=0, rows=4, k=64, ldw=64, b=P2, ld_b=8, a=P3, ld_a=64, ab_dtype=0, rank=8, scale=0.25,
+             codes=P2, ld_codes=32, scales=P3, ld_scales=2, flags=0, stream=None)
+    a.update(kw)
+    return fq.fp4_quantize_lora(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=2), dict(w=None), dict(b=None), dict(a=None), dict(codes=None), dict(scales=None), dict(w_dtype=5),
+    dict(ab_dtype=3), dict(rank=0), dict(rank=65), dict(ld_b=7), dict(ld_a=32), dict(rows=0), dict(k=48),
+    dict(ldw=32), dict(w=P + 4), dict(b=P2 + 2), dict(ab_dtype=1, a=P3 + 1), dict(scale=float("nan")),
+    dict(scale=float("inf")), dict(flags=0x1), dict(flags=0x2), dict(flags=0x100), dict(ld_codes=16),
+    dict(flags=0x200), dict(rows=1 << 31),
+])
+def test_quantize_lora_rejects(lib, kw):
+    assert ql(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_quantize_lora_nv_unsupported(lib):
+    assert ql(fmt=1) == fq.binding.UNSUPPORTED
+
+
+def test_rollout_lora_entries_per_block():
+    """Host-side check of the rollout's adapter list (no device work)."""
+    import torch
+    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
+    w = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        Fp4Rollout([w] * 4, [w] * 4, torch.zeros(4), lora=([None] * 3, [None] * 4))
+    ro = Fp4Rollout([w] * 4, [w] * 4, torch.zeros(4))
+    assert ro.lora1 == [None] * 4 and ro.lora2 == [None] * 4

@@ -1,0 +1,134 @@
+"""GPU parity of the LoRA merge + MXFP4 re-quantization (fp4_quantize_lora)
+against the oracle: W' = W + s (B A) (oracle/lora.py), quantized by the MX
+rule (oracle/mxfp4.py).
+
+  * Exactly representable case: small integers times powers of two, so that
+    every fp32 operation of the merge is exact -- codes and scales must be
+    the oracle's bit for bit (any indexing, transposition or order slip
+    shows), in both layouts.
+  * Realistic case (FLUX-like bf16 weight, fp32 adapters): the GPU merges in
+    fp32, so a code or scale may differ only where the exact merged value
+    lies within the fp32 evaluation bound of a decision point
+    (tests/_parity.lora_merge_band).
+  * scale 0 gives fp4_quantize(W) bit for bit; the panel layout equals the
+    row-major one bit for bit, with zero / 127 padding.
+Shapes leave ragged tails (rows not a multiple of 32 or 256, k not a
+multiple of 256 or 128) and cover ranks 1 .. 64 (above 56 the kernel needs
+more than 64 KiB of dynamic LDS)."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_quantized_diffusion_amd import inputs
+from oracle import lora, mxfp4
+from tests._parity import lora_merge_band, mx_codes_near_boundary_ok, panel_to_rows, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype)
+
+
+def gpu_codes(q, rows, k):
+    if q.layout == "panel":
+        c, s, pad = panel_to_rows(to_np(q.codes), to_np(q.scales), rows, k)
+        assert (pad["code_rows"] == 0).all() and (pad["code_cols"] == 0).all()
+        assert (pad["scale_rows"] == 127).all() and (pad["scale_cols"] == 127).all()
+        return c, s
+    return to_np(q.codes)[:, : k // 2], to_np(q.scales)[:, : k // 32]
+
+
+def exact_operands(rows, k, rank, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(-64, 65, size=(rows, k)) / 16.0
+    b = rng.integers(-2, 3, size=(rows, rank)) / 4.0
+    a = rng.integers(-3, 4, size=(rank, k)) / 8.0
+    return w.astype(np.float32), b.astype(np.float32), a.astype(np.float32)
+
+
+@pytest.mark.parametrize("layout", ["row", "panel"])
+@pytest.mark.parametrize("rows,k,rank", [(1, 32, 1), (37, 288, 3), (300, 4160, 32), (64, 512, 64), (257, 160, 57)])
+def test_exact_case_bit_for_bit(gpu_lib, layout, rows, k, rank):
+    w, b, a = exact_operands(rows, k, rank, rows * 31 + k + rank)
+    s = 0.5
+    q = gpu_lib.quantize_lora(dev(w), dev(b), dev(a), s, layout=layout)
+    gc, gs = gpu_codes(q, rows, k)
+    oc, os_ = mxfp4.quantize(lora.merge(w, b, a, s))
+    np.testing.assert_array_equal(gs, os_)
+    np.testing.assert_array_equal(gc, oc)
+
+
+@pytest.mark.parametrize("layout", ["row", "panel"])
+@pytest.mark.parametrize("ab_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,k,rank", [(300, 4160, 32), (512, 3072, 16), (96, 1024, 7)])
+def test_random_case_within_fp32_bound(gpu_lib, layout, ab_dtype, rows, k, rank):
+    rng = np.random.default_rng(rows + k + rank)
+    w = inputs.to_bf16((rng.standard_normal((rows, k)) * 0.02).astype(np.float32))
+    b = (rng.standard_normal((rows, rank)) * 0.01).astype(np.float32)
+    a = (rng.standard_normal((rank, k)) * 0.05).astype(np.float32)
+    if ab_dtype == torch.bfloat16:
+        b, a = inputs.to_bf16(b), inputs.to_bf16(a)
+    s = 2.0  # alpha / rank with alpha = 2 rank
+    q = gpu_lib.quantize_lora(dev(w, torch.bfloat16), dev(b, ab_dtype), dev(a, ab_dtype), s, layout=layout)
+    gc, gs = gpu_codes(q, rows, k)
+    ref = lora.merge(w, b, a, s)
+    bad, flips = mx_codes_near_boundary_ok(ref, gc, gs, band=lora_merge_band(w, b, a, s))
+    assert bad == 0, (bad, flips)
+    assert flips <= ref.size // 10000 + 5
+
+
+def test_scale_zero_is_plain_quantization(gpu_lib):
+    rng = np.random.default_rng(3)
+    rows, k, rank = 200, 2432, 32
+    w = dev(rng.standard_normal((rows, k)).astype(np.float32))
+    b = dev(rng.standard_normal((rows, rank)).astype(np.float32))
+    a = dev(rng.standard_normal((rank, k)).astype(np.float32))
+    q = gpu_lib.quantize_lora(w, b, a, 0.0)
+    p = gpu_lib.quantize(w)
+    np.testing.assert_array_equal(to_np(q.codes)[:, : k // 2], to_np(p.codes)[:, : k // 2])
+    np.testing.assert_array_equal(to_np(q.scales), to_np(p.scales))
+
+
+@pytest.mark.parametrize("rows,k,rank", [(300, 4160, 32), (513, 96, 5)])
+def test_panel_equals_row_major(gpu_lib, rows, k, rank):
+    rng = np.random.default_rng(rows * k)
+    w = dev(rng.standard_normal((rows, k)).astype(np.float32), torch.bfloat16)
+    b = dev(rng.standard_normal((rows, rank)).astype(np.float32))
+    a = dev(rng.standard_normal((rank, k)).astype(np.float32))
+    qp = gpu_lib.quantize_lora(w, b, a, 0.125, layout="panel")
+    qr = gpu_lib.quantize_lora(w, b, a, 0.125)
+    c, s = gpu_codes(qp, rows, k)
+    np.testing.assert_array_equal(c, to_np(qr.codes)[:, : k // 2])
+    np.testing.assert_array_equal(s, to_np(qr.scales))
+
+
+def test_full_flux_w1_rank32_sampled_rows(gpu_lib):
+    """FLUX-class W1 [12288, 3072] bf16 with a rank-32 fp32 adapter, full
+    size, panel layout (as the rollout uses it); sampled rows against the
+    oracle within the fp32 bound."""
+    rows, k, rank = 12288, 3072, 32
+    rng = np.random.default_rng(12)
+    w = inputs.to_bf16((rng.standard_normal((rows, k)) * 0.02).astype(np.float32))
+    b = (rng.standard_normal((rows, rank)) * 0.01).astype(np.float32)
+    a = (rng.standard_normal((rank, k)) * 0.05).astype(np.float32)
+    q = gpu_lib.quantize_lora(dev(w, torch.bfloat16), dev(b), dev(a), 2.0, layout="panel")
+    gc, gs = gpu_codes(q, rows, k)
+    sel = np.sort(rng.choice(rows, 96, replace=False))
+    ref = lora.merge(w[sel], b[sel], a, 2.0)
+    bad, flips = mx_codes_near_boundary_ok(ref, gc[sel], gs[sel], band=lora_merge_band(w[sel], b[sel], a, 2.0))
+    assert bad == 0, (bad, flips)
+
+
+def test_reuses_out(gpu_lib):
+    rng = np.random.default_rng(5)
+    rows, k, rank = 256, 256, 4
+    w, b, a = exact_operands(rows, k, rank, 9)
+    q = gpu_lib.quantize(dev(w), layout="panel")
+    q2 = gpu_lib.quantize_lora(dev(w), dev(b), dev(a), 1.0, out=q)
+    assert q2.codes.data_ptr() == q.codes.data_ptr()
+    gc, gs = gpu_codes(q2, rows, k)
+    oc, os_ = mxfp4.quantize(lora.merge(w, b, a, 1.0))
+    np.testing.assert_array_equal(gc, oc)
+    np.testing.assert_array_equal(gs, os_)

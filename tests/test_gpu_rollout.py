@@ -116,3 +116,34 @@ def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
         outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("layout", ["panel", "row"])
+def test_lora_rollout_equals_rollout_on_merged_weights(gpu_lib, layout):
+    """A rollout whose re-quantization merges LoRA adapters (fp4_quantize_lora)
+    equals, bit for bit, the plain rollout on the merged weights, for adapters
+    whose merge is exact in fp32 (small integers times powers of two) -- so
+    the adapters reach the right weights, with the right orientation."""
+    seed, n_cand, tokens, dim, hidden, rank = 11, 2, 256, 256, 512, 4
+    rng = np.random.default_rng(seed)
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    u = torch.from_numpy(inputs.reward_vector(seed, dim)).to(DEV)
+    w1, w2, m1, m2, l1, l2 = [], [], [], [], [], []
+    for _ in range(4):
+        for shape, ws, ms, ls in (((hidden, dim), w1, m1, l1), ((dim, hidden), w2, m2, l2)):
+            w = (rng.integers(-32, 33, size=shape) / 1024.0).astype(np.float32)
+            b = (rng.integers(-2, 3, size=(shape[0], rank)) / 16.0).astype(np.float32)
+            a = (rng.integers(-2, 3, size=(rank, shape[1])) / 16.0).astype(np.float32)
+            merged = (w.astype(np.float64) + 0.5 * (b.astype(np.float64) @ a)).astype(np.float32)
+            ws.append(torch.from_numpy(w).to(DEV))
+            ms.append(torch.from_numpy(merged).to(DEV))
+            ls.append((torch.from_numpy(b).to(DEV), torch.from_numpy(a).to(DEV), 0.5))
+    outs = []
+    for weights, lora in (((w1, w2), (l1, l2)), ((m1, m2), None)):
+        ro = Fp4Rollout(weights[0], weights[1], u, k_top=1, k_bottom=1, layout=layout, lora=lora)
+        xd = torch.from_numpy(noise).to(DEV)
+        r, top, bottom, rn = ro.run(xd)
+        torch.cuda.synchronize()
+        outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
