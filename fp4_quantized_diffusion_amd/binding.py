@@ -3,10 +3,11 @@
 Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
   * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_panel_bytes,
-    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, euler_step, fp4_proxy_reward,
+    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, fp4_gemm_panel_euler_reward, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
-  * torch-tensor helpers (quantize, quantize_lora, gemm, gemm_gelu, gemm_euler, euler, proxy_reward, select) that
+  * torch-tensor helpers (quantize, quantize_lora, gemm, gemm_gelu, gemm_euler, gemm_euler_reward, euler,
+    proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
 Loading fails loudly when the library has not been built; there is no
@@ -36,6 +37,8 @@ _SIGS = {
     "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "fp4_gemm_panel_gelu": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p],
     "fp4_gemm_panel_euler": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p],
+    "fp4_gemm_panel_euler_reward": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p, _i64,
+                                    _p, _p, _p],
     "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
     "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
     "select_topk_bottomk": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
@@ -109,6 +112,13 @@ def fp4_gemm_panel_euler(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, res
                          stream):
     return load_library().fp4_gemm_panel_euler(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x,
                                                x_out, ldx, t_cur, t_next, stream)
+
+
+def fp4_gemm_panel_euler_reward(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x, x_out, ldx, t_cur,
+                                t_next, u, rows_per_cand, partials, rewards, stream):
+    return load_library().fp4_gemm_panel_euler_reward(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual,
+                                                      x, x_out, ldx, t_cur, t_next, u, rows_per_cand, partials,
+                                                      rewards, stream)
 
 
 def euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream):
@@ -326,6 +336,34 @@ def gemm_euler(a, b, residual, x, t_cur, t_next, out=None):
                               x.stride(0), float(t_cur), float(t_next), _stream())
     _check(st, "fp4_gemm_panel_euler")
     return out
+
+
+def gemm_euler_reward(a, b, residual, x, t_cur, t_next, u, rows_per_cand, out=None, rewards=None, partials=None):
+    """gemm_euler plus the proxy reward of each candidate (rows_per_cand rows
+    each) from the new state: returns (out, rewards). u: fp32 [n]; partials:
+    optional fp32 workspace of (m / 256) (n / 256) 4 elements."""
+    torch = _torch()
+    if a.layout != "panel" or b.layout != "panel" or a.k != b.k:
+        raise ValueError("gemm_euler_reward takes panel-layout operands of one k")
+    m, n, k = a.n_rows, b.n_rows, a.k
+    if out is None:
+        out = torch.empty_like(x)
+    for t in (residual, x, out):
+        if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) != x.stride(0) or tuple(t.shape) != (m, n):
+            raise ValueError("residual, x and out must be [m, n] with one row stride")
+    if rows_per_cand < 1 or m % rows_per_cand:
+        raise ValueError("rows_per_cand must divide m")
+    if rewards is None:
+        rewards = torch.empty(m // rows_per_cand, dtype=torch.float32, device=x.device)
+    need = max(m // 256, 1) * max(n // 256, 1) * 4
+    if partials is None or partials.numel() < need:
+        partials = torch.empty(need, dtype=torch.float32, device=x.device)
+    st = fp4_gemm_panel_euler_reward(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                     b.scales.data_ptr(), m, n, k, residual.data_ptr(), x.data_ptr(), out.data_ptr(),
+                                     x.stride(0), float(t_cur), float(t_next), u.data_ptr(), rows_per_cand,
+                                     partials.data_ptr(), rewards.data_ptr(), _stream())
+    _check(st, "fp4_gemm_panel_euler_reward")
+    return out, rewards
 
 
 def euler(x, v, t_cur, t_next, out=None):

@@ -231,6 +231,31 @@ FP4_API fp4_status fp4_gemm_panel_euler(int fmt, const uint8_t* a_codes, const u
   }
 }
 
+FP4_API fp4_status fp4_gemm_panel_euler_reward(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                                               int64_t k, const float* residual, const float* x, float* x_out,
+                                               int64_t ldx, float t_cur, float t_next, const float* u,
+                                               int64_t rows_per_cand, float* partials, float* rewards, void* stream) {
+  try {
+    if (!residual || !x || !aligned(x, 16)) return FP4_INVALID_ARGUMENT;
+    if (!u || !aligned(u, 16) || !partials || !aligned(partials, 4) || !rewards || !aligned(rewards, 4))
+      return FP4_INVALID_ARGUMENT;
+    if (rows_per_cand < 1 || rows_per_cand >= kMaxDim) return FP4_INVALID_ARGUMENT;
+    const fp4_status s =
+        check_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, x_out, FP4_DT_F32, ldx, residual);
+    if (s != FP4_OK) return s;
+    if (m % rows_per_cand != 0) return FP4_INVALID_ARGUMENT;
+    // the epilogue sums whole waves (128 x 128 values) of full 256 x 256 tiles
+    if (m % 256 != 0 || n % 256 != 0 || rows_per_cand % 128 != 0) return FP4_UNSUPPORTED;
+    const float dt = t_next - t_cur;  // fp32 subtraction, as euler_step
+    return from_hip(fp4r::launch_gemm_mx_panel_euler_reward(a_codes, a_scales, b_codes, b_scales, m, n, k, residual,
+                                                            x, x_out, ldx, dt, u, rows_per_cand, partials, rewards,
+                                                            static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
 FP4_API fp4_status euler_step(float* x_out, const float* x, const void* v, int v_dtype, int64_t numel, float t_cur,
                               float t_next, void* stream) {
   try {
@@ -302,6 +327,6 @@ FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 104; }
+FP4_API int fp4_abi_version(void) { return 105; }
 
 }  // extern "C"

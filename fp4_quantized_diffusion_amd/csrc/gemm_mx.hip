@@ -89,6 +89,8 @@ struct Problem {
   const float *a_ts, *b_ts;        // NVFP4-style tensor scales
   const float* ex;                 // Euler epilogue: the state x, and the step dt
   float dt;
+  const float* ru;                 // Euler + reward epilogue: the reward weights u [N]
+  float* rp;                       //   and the per-wave partial sums [tiles][4]
   uint8_t *qc, *qs;                // GELU + MXFP4 epilogue: output codes / scales (panel layout)
   int qnc;                         //   and the output's 128-element chunks per panel row (n / 128)
   int64_t lda, ld_as, ldb, ld_bs;  // row-major layouts
@@ -529,7 +531,7 @@ __device__ __forceinline__ float acc_read(float a) {
 // epilogue, 2 code stores and 1 scale store per 32 rows.)
 template <int BF16OUT, int RESID>
 constexpr int full_tile_vmem() {
-  return RESID == 3 ? 12 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4)));
+  return RESID == 3 ? 12 : (RESID == 4 ? 16 * 12 + 5 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -633,17 +635,29 @@ __device__ __forceinline__ void store_tile_bf16_lds(v16f acc[4][4], int m_base, 
 }
 
 // fp32 output, RESID 1: + residual, RESID 2: then the Euler step
-// fmaf(dt, v, x) (see store_tile). One MFMA tile at a time (t = 4 j + i), 4
+// fmaf(dt, v, x) (see store_tile), RESID 4: the Euler step and the proxy
+// reward's partial sum of the new state times u over the wave's 128 x 128
+// values, written to *rslot. One MFMA tile at a time (t = 4 j + i), 4
 // stores plus 4 residual (and 4 state) loads each; the loads run two MFMA
-// tiles ahead of their use.
+// tiles ahead of their use (one with the state).
 template <int RESID>
 __device__ __forceinline__ void store_tile_f32_lds(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
-                                                   int64_t ldc, const float* residual, uint8_t* stage) {
+                                                   int64_t ldc, const float* residual, uint8_t* stage,
+                                                   float* rslot = nullptr) {
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
   const int r32 = lane & 31, h = lane >> 5;
   const int rq = lane >> 3, cq = lane & 7;
-  constexpr bool EULER = RESID == 2;
+  constexpr bool EULER = RESID == 2 || RESID == 4;
+  constexpr bool REWARD = RESID == 4;
+  // reward: this lane's columns n_base + 32 i + 4 cq .. +3 of u, and its sum
+  // over its values in (t, q) order, one fma each
+  float4 uu[4];
+  float racc = 0.0f;
+  if (REWARD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) uu[i] = *reinterpret_cast<const float4*>(p.ru + n_base + 32 * i + 4 * cq);
+  }
   constexpr int LA = EULER ? 1 : 2;  // MFMA tiles of load look-ahead (registers allow one with two inputs)
   constexpr int NB = LA + 1;
   auto goff = [&](int t, int q) -> int64_t {
@@ -685,9 +699,20 @@ __device__ __forceinline__ void store_tile_f32_lds(v16f acc[4][4], int m_base, i
         const float4 x = xb[t % NB][q];
         o.x = fmaf(p.dt, o.x, x.x); o.y = fmaf(p.dt, o.y, x.y); o.z = fmaf(p.dt, o.z, x.z); o.w = fmaf(p.dt, o.w, x.w);
       }
+      if (REWARD) {
+        const float4 w = uu[t & 3];
+        racc = fmaf(o.x, w.x, racc); racc = fmaf(o.y, w.y, racc); racc = fmaf(o.z, w.z, racc);
+        racc = fmaf(o.w, w.w, racc);
+      }
       __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(c) + goff(t, q)));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads' look-ahead, and the next writes behind these reads
+  }
+  if (REWARD) {
+    // fixed xor tree: fp32 addition commutes, so every lane ends with the same sum
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) racc += __shfl_xor(racc, o);
+    if (lane == 0) *rslot = racc;
   }
 }
 
@@ -952,7 +977,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
       if (EPI_LDS && BF16OUT)
         store_tile_bf16_lds(acc, mb, nb, c, ldc, epi_stage + wave * kEpiWaveBytes);
       else if (EPI_LDS)
-        store_tile_f32_lds<RESID>(acc, mb, nb, p, c, ldc, residual, epi_stage + wave * kEpiWaveBytes);
+        store_tile_f32_lds<RESID>(acc, mb, nb, p, c, ldc, residual, epi_stage + wave * kEpiWaveBytes,
+                                  RESID == 4 ? p.rp + ((int64_t)tm * p.tiles_n + tn) * 4 + wave : nullptr);
       else
         store_tile<BF16OUT, RESID, true, NV>(acc, mb, nb, p, c, ldc, residual, mul);
     } else {
@@ -1012,6 +1038,8 @@ Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, cons
   p.dt = 0.0f;
   p.qc = p.qs = nullptr;
   p.qnc = 0;
+  p.ru = nullptr;
+  p.rp = nullptr;
   p.lda = p.ld_as = p.ldb = p.ld_bs = 0;
   p.M = (int)m; p.N = (int)n; p.kbytes = (int)(k >> 1); p.nblk = (int)(k >> 5);
   p.nkc = (int)((k + 127) >> 7);
@@ -1057,6 +1085,57 @@ hipError_t launch_gemm_mx_panel_euler(const uint8_t* a, const uint8_t* as, const
   const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
   const unsigned grid = (unsigned)min(p.total, cu_count());
   gemm_fp4_kernel<0, 2, LD_PANEL><<<grid, kThreads, 0, st>>>(p, x_out, ldx, residual, nst4);
+  return hipGetLastError();
+}
+
+// The proxy reward of each candidate from the Euler + reward epilogue's
+// per-wave partial sums: candidate c owns the waves whose 128 rows lie in its
+// rows_per_cand rows (wave w of tile (tm, tn) covers rows tm 256 + 128 (w & 1)
+// ..., columns tn 256 + 128 (w >> 1) ...). Sum in a fixed order (per thread,
+// then a fixed shuffle tree and LDS order), divided by rows_per_cand.
+namespace {
+__global__ __launch_bounds__(256) void reward_partials_kernel(const float* __restrict__ rp, int tiles_n,
+                                                              int rows_per_cand, float* __restrict__ rewards) {
+  __shared__ float sh[4];
+  const int c = blockIdx.x;
+  const int wrows = rows_per_cand / 128;  // wave rows per candidate
+  const int per_wr = tiles_n * 2;         // partials per wave row: every tile column, both column halves
+  const int total = wrows * per_wr;
+  float acc = 0.0f;
+  for (int f = threadIdx.x; f < total; f += 256) {
+    const int wr = c * wrows + f / per_wr;  // global wave row: tm = wr / 2, row half wr % 2
+    const int tn = (f % per_wr) >> 1, wn = f & 1;
+    acc += rp[((int64_t)(wr >> 1) * tiles_n + tn) * 4 + (wr & 1) + 2 * wn];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) rewards[c] = (((sh[0] + sh[1]) + sh[2]) + sh[3]) / (float)rows_per_cand;
+}
+}  // namespace
+
+// The last block of the last Euler step with the proxy reward in the same
+// pass: x_out as launch_gemm_mx_panel_euler, then rewards[c] = mean over the
+// candidate's rows of <x_out row, u>. m and n are multiples of 256 and
+// rows_per_cand of 128, dividing m (checked by the caller); partials holds
+// (m / 256) (n / 256) 4 floats.
+hipError_t launch_gemm_mx_panel_euler_reward(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                             int64_t m, int64_t n, int64_t k, const float* residual, const float* x,
+                                             float* x_out, int64_t ldx, float dt, const float* u, int64_t rows_per_cand,
+                                             float* partials, float* rewards, hipStream_t st) {
+  Problem p = make_problem(a, as, b, bs, m, n, k);
+  p.ex = x;
+  p.dt = dt;
+  p.ru = u;
+  p.rp = partials;
+  const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
+  const unsigned grid = (unsigned)min(p.total, cu_count());
+  gemm_fp4_kernel<0, 4, LD_PANEL><<<grid, kThreads, 0, st>>>(p, x_out, ldx, residual, nst4);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reward_partials_kernel<<<(unsigned)(m / rows_per_cand), 256, 0, st>>>(partials, p.tiles_n, (int)rows_per_cand,
+                                                                        rewards);
   return hipGetLastError();
 }
 

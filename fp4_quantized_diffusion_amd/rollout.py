@@ -55,12 +55,16 @@ from . import binding as fb
 
 class Fp4Rollout:
     def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None,
-                 layout="panel", overlap=False, lora=None):
+                 layout="panel", overlap=False, lora=None, fuse_reward=True):
         """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
         lora: optional (lora1, lora2), one entry per block each, None or a
         LoRA adapter (B, A, scale) of that weight; the per-iteration
         re-quantization then merges it in the same pass (fp4_quantize_lora).
         Update adapters between iterations with set_lora.
+        fuse_reward: on the panel layout, take the proxy reward in the last
+        GEMM of the last step (fp4_gemm_panel_euler_reward) when the shapes
+        allow, instead of re-reading the final state (fp4_proxy_reward): the
+        same quantity in another fp32 summation order.
         chunk: candidates per pass through the network on one stream (None =
         all); ignored by the two-stream schedule.
         overlap: two-stream schedule over two halves of the candidates (needs
@@ -75,6 +79,7 @@ class Fp4Rollout:
             raise ValueError(f"unknown layout {layout!r}")
         self.fmt, self.chunk, self.layout = fmt, chunk, layout
         self.overlap = overlap
+        self.fuse_reward = fuse_reward
         self._side = None
         self.timer = timer
         self.q1 = self.q2 = None
@@ -116,12 +121,14 @@ class Fp4Rollout:
     def _gemm(self, a, b, out_dtype, residual=None, out=None):
         return self._call("gemm", lambda: fb.gemm(a, b, out_dtype, residual=residual, out=out))
 
-    def velocity(self, x, h, step=None):
+    def velocity(self, x, h, step=None, reward=None):
         """h <- v(x) for x, h fp32 [rows, dim] (h_0 = x is never copied: the
         first block's GEMM takes x as its residual). step = (t_cur, t_next,
         x_out): the last block's second GEMM also takes the Euler step,
         x_out = x + (t_next - t_cur) v, and h is left at the previous block's
-        value."""
+        value. reward = (rewards, tokens) with step: that GEMM also writes the
+        proxy reward of each candidate (tokens rows each) of x_out into
+        rewards (fp4_gemm_panel_euler_reward)."""
         import torch
         rows, dim = x.shape
         hidden = self.w1[0].shape[0]
@@ -143,7 +150,13 @@ class Fp4Rollout:
                     z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
             if b == last and step is not None:
                 t_cur, t_next, x_out = step
-                self._call("gemm", lambda: fb.gemm_euler(a2, self.q2[b], src, x, t_cur, t_next, out=x_out))
+                if reward is not None:
+                    rw, tokens = reward
+                    part = self._buf("rpart", (max(rows // 256, 1) * max(dim // 256, 1) * 4,), torch.float32, x.device)
+                    self._call("gemm", lambda: fb.gemm_euler_reward(a2, self.q2[b], src, x, t_cur, t_next, self.u,
+                                                                    tokens, out=x_out, rewards=rw, partials=part))
+                else:
+                    self._call("gemm", lambda: fb.gemm_euler(a2, self.q2[b], src, x, t_cur, t_next, out=x_out))
                 return x_out
             self._gemm(a2, self.q2[b], "f32", residual=src, out=h)
             src = h
@@ -244,16 +257,28 @@ class Fp4Rollout:
         x = x0 if work is None else work.view(n_cand * tokens, dim)
         h = self._buf("h", (chunk * tokens, dim), torch.float32, noise.device)
         t = [1.0 - i / self.steps for i in range(self.steps + 1)]
+        rewards = torch.empty(n_cand, dtype=torch.float32, device=noise.device)
+        fused_reward = True
         for i in range(self.steps):
             src = x0 if i == 0 else x
             for c0 in range(0, n_cand, chunk):
-                r0, rows = c0 * tokens, min(chunk, n_cand - c0) * tokens
+                nc = min(chunk, n_cand - c0)
+                r0, rows = c0 * tokens, nc * tokens
                 xs, xd = src[r0:r0 + rows], x[r0:r0 + rows]
                 if self.layout == "panel":  # Euler step fused into the last GEMM
-                    self.velocity(xs, h[:rows], step=(t[i], t[i + 1], xd))
+                    # and, after the last step, the proxy reward too when whole wave tiles fit
+                    rw = None
+                    if i == self.steps - 1 and self.fuse_reward and rows % 256 == 0 and dim % 256 == 0 \
+                            and tokens % 128 == 0:
+                        rw = (rewards[c0:c0 + nc], tokens)
+                    elif i == self.steps - 1:
+                        fused_reward = False
+                    self.velocity(xs, h[:rows], step=(t[i], t[i + 1], xd), reward=rw)
                 else:
+                    fused_reward = False
                     hc = self.velocity(xs, h[:rows])
                     self._call("euler", lambda: fb.euler(xs, hc, t[i], t[i + 1], out=xd))
-        rewards = self._call("reward", lambda: fb.proxy_reward(x, n_cand, tokens, self.u))
+        if self.steps == 0 or not fused_reward:
+            rewards = self._call("reward", lambda: fb.proxy_reward(x, n_cand, tokens, self.u))
         top, bottom, rn = self._call("select", lambda: fb.select(rewards, self.k_top, self.k_bottom))
         return rewards, top, bottom, rn

@@ -251,6 +251,35 @@ FP4_API fp4_status fp4_gemm_panel_euler(int fmt, const uint8_t* a_codes, const u
                                 float t_cur, float t_next, void* stream);
 
 /*
+ * fp4_gemm_panel_euler_reward -- fp4_gemm_panel_euler for the last block of
+ * the last solver step, with the candidates' proxy reward (project page,
+ * "Two-Stage Pipeline": candidates are scored with proxy rewards) taken from
+ * the new state in the same pass, so x_out is not read back:
+ *   x_out      exactly as fp4_gemm_panel_euler (bit-identical);
+ *   rewards[c] = (1 / rows_per_cand) * sum over the candidate's rows i and all
+ *                columns j of x_out[i, j] * u[j], c = 0 .. m / rows_per_cand - 1
+ *                (the quantity fp4_proxy_reward computes with u, in another
+ *                fp32 summation order: per lane fmas, per 128 x 128 wave a
+ *                fixed shuffle tree, then the waves of a candidate in a fixed
+ *                order; deterministic).
+ *   fmt, a_*, b_*, m, n, k, residual, x, x_out, ldx, t_cur, t_next
+ *              as in fp4_gemm_panel_euler.
+ *   u          fp32 [n], 16-byte aligned.
+ *   rows_per_cand  rows (tokens) per candidate; divides m.
+ *   partials   caller workspace, fp32 [(m / 256) * (n / 256) * 4], 4-byte
+ *              aligned (per-wave partial sums; contents undefined on return).
+ *   rewards    fp32 [m / rows_per_cand] out, 4-byte aligned.
+ * FP4_UNSUPPORTED unless m and n are multiples of 256 and rows_per_cand of
+ * 128 (the sums cover whole 128 x 128 wave tiles).
+ */
+FP4_API fp4_status fp4_gemm_panel_euler_reward(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales,
+                                int64_t m, int64_t n, int64_t k,
+                                const float* residual, const float* x, float* x_out, int64_t ldx,
+                                float t_cur, float t_next, const float* u, int64_t rows_per_cand,
+                                float* partials, float* rewards, void* stream);
+
+/*
  * euler_step -- one explicit Euler step of the sampler's ODE,
  *   x_out = x + (t_next - t_cur) * v,
  * with dt = fl32(t_next - t_cur) and an fp32 multiply-add per element. The

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 104
+    assert fq.fp4_abi_version() == 105
 
 
 def test_status_strings(lib):
@@ -224,3 +224,25 @@ def test_rollout_lora_entries_per_block():
         Fp4Rollout([w] * 4, [w] * 4, torch.zeros(4), lora=([None] * 3, [None] * 4))
     ro = Fp4Rollout([w] * 4, [w] * 4, torch.zeros(4))
     assert ro.lora1 == [None] * 4 and ro.lora2 == [None] * 4
+
+
+def ger(**kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=256, n=256, k=64, residual=P2, x=P3, x_out=P, ldx=256,
+             t_cur=1.0, t_next=5.0 / 6.0, u=P2, rows_per_cand=128, partials=P3, rewards=P, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_panel_euler_reward(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(residual=None), dict(x=None), dict(x_out=None), dict(u=None), dict(u=P2 + 4),
+    dict(partials=None), dict(partials=P3 + 2), dict(rewards=None), dict(rewards=P + 1), dict(rows_per_cand=0),
+    dict(rows_per_cand=96), dict(m=0), dict(k=48), dict(ldx=250), dict(x=P3 + 4),
+])
+def test_gemm_panel_euler_reward_rejects(lib, kw):
+    assert ger(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=384, rows_per_cand=128), dict(n=128, ldx=128),
+                                dict(rows_per_cand=64)])
+def test_gemm_panel_euler_reward_unsupported(lib, kw):
+    assert ger(**kw) == fq.binding.UNSUPPORTED

@@ -10,7 +10,7 @@ import torch
 
 from fp4_quantized_diffusion_amd import inputs
 from fp4_quantized_diffusion_amd.binding import FMT_MX, QTensor
-from oracle import gemm as ogemm, mxfp4, rollout as orollout
+from oracle import gemm as ogemm, mxfp4, reward as oreward, rollout as orollout
 from tests._parity import gemm_within_tol, mx_codes_near_boundary_ok, panel_to_rows, to_np
 
 pytestmark = pytest.mark.gpu
@@ -242,3 +242,49 @@ def test_gemm_gelu_full_size_flux(gpu_lib):
     out = gpu_lib.gemm_gelu(qa, qb)
     assert torch.equal(out.scales, ref.scales)
     assert torch.equal(out.codes, ref.codes)
+
+
+@pytest.mark.parametrize("m,n,k,tokens", [(256, 256, 256, 128), (512, 768, 1024, 256), (1024, 512, 3072, 512),
+                                          (768, 256, 416, 256)])
+def test_gemm_euler_reward(gpu_lib, m, n, k, tokens):
+    """Euler + reward epilogue: the new state bit-identical to gemm_euler, and
+    each candidate's reward (mean over its rows of <x_out row, u>) against
+    the float64 oracle reward of that state within the fp32 summation bound
+    (|error| <= 2^-24 (count + 6) * mean |x_out u|), and against the
+    standalone fp4_proxy_reward within twice that."""
+    rng = np.random.default_rng(m + n + k)
+    a = act(m, k, 3) * 2.0
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    res = rng.standard_normal((m, n)).astype(np.float32)
+    x = rng.standard_normal((m, n)).astype(np.float32)
+    u = rng.standard_normal(n).astype(np.float32)
+    qa = gpu_lib.quantize(dev(a), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(w), "mx", layout="panel")
+    want = gpu_lib.gemm_euler(qa, qb, dev(res), dev(x), 1.0, 5.0 / 6.0)
+    got, r = gpu_lib.gemm_euler_reward(qa, qb, dev(res), dev(x), 1.0, 5.0 / 6.0, dev(u), tokens)
+    xo = to_np(got)
+    np.testing.assert_array_equal(xo, to_np(want))
+    r = to_np(r)
+    ref = oreward.proxy_reward(xo, tokens, u)
+    mag = np.abs(xo.astype(np.float64) * u).reshape(-1, tokens, n).sum(axis=(1, 2)) / tokens
+    bound = 2.0 ** -24 * (tokens * n + 6) * mag
+    assert (np.abs(r - ref) <= bound).all(), (np.abs(r - ref) / mag).max()
+    r_std = to_np(gpu_lib.proxy_reward(got, m // tokens, tokens, u=dev(u)))
+    assert (np.abs(r - r_std) <= 2 * bound).all()
+
+
+def test_gemm_euler_reward_in_place(gpu_lib):
+    """x_out = x in place, as the rollout calls it."""
+    m, n, k, tokens = 512, 256, 512, 256
+    rng = np.random.default_rng(4)
+    qa = gpu_lib.quantize(dev(act(m, k, 8)), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev((rng.standard_normal((n, k)) * 0.02).astype(np.float32)), "mx", layout="panel")
+    res = dev(rng.standard_normal((m, n)).astype(np.float32))
+    x = rng.standard_normal((m, n)).astype(np.float32)
+    u = dev(rng.standard_normal(n).astype(np.float32))
+    want = to_np(gpu_lib.gemm_euler(qa, qb, res, dev(x), 1.0, 0.5))
+    xd = dev(x)
+    out, r = gpu_lib.gemm_euler_reward(qa, qb, res, xd, 1.0, 0.5, u, tokens, out=xd)
+    np.testing.assert_array_equal(to_np(xd), want)
+    r2 = to_np(gpu_lib.gemm_euler_reward(qa, qb, res, dev(x), 1.0, 0.5, u, tokens)[1])
+    np.testing.assert_array_equal(to_np(r), r2)  # deterministic, in place or not

@@ -100,7 +100,9 @@ def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
     """Row counts that are multiples of 256 (2 candidates x 256 tokens per
     chunk) take the fused first linear (GEMM + GELU + MXFP4 in one call) and
     the fused Euler step on the panel layout; the row-major path runs every
-    step separately. Whole rollouts agree bit for bit."""
+    step separately. Whole rollouts agree bit for bit (the reward taken by
+    the standalone kernel in both; the fused reward sums in another order,
+    see the next test)."""
     seed, n_cand, tokens, dim, hidden = 7, 4, 256, 256, 1024
     noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
     ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
@@ -109,13 +111,45 @@ def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
     w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
     outs = []
     for layout in ("panel", "row"):
-        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, chunk=2, layout=layout)
+        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, chunk=2, layout=layout, fuse_reward=False)
         xd = torch.from_numpy(noise).to(DEV)
         r, top, bottom, rn = ro.run(xd)
         torch.cuda.synchronize()
         outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("chunk", [2, 3])
+def test_fused_reward_rollout(gpu_lib, chunk):
+    """The proxy reward taken in the last GEMM of the last step (per chunk of
+    candidates) against the standalone reward kernel on the same final
+    state: the state is bit-identical, the rewards agree within the fp32
+    summation bound, and the selection is the exact selection of the fused
+    rewards."""
+    from oracle import reward as oreward
+    seed, n_cand, tokens, dim, hidden = 9, 5, 256, 256, 512
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
+    u_np = inputs.reward_vector(seed, dim)
+    u = torch.from_numpy(u_np).to(DEV)
+    w1 = [torch.from_numpy(w[0]).to(DEV).bfloat16() for w in ws]
+    w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
+    outs = []
+    for fuse in (True, False):
+        ro = Fp4Rollout(w1, w2, u, k_top=2, k_bottom=2, chunk=chunk, fuse_reward=fuse)
+        xd = torch.from_numpy(noise).to(DEV)
+        r, top, bottom, rn = ro.run(xd)
+        torch.cuda.synchronize()
+        outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    xo = outs[0][0].reshape(n_cand, tokens, dim).astype(np.float64)
+    mag = np.abs(xo * u_np).sum(axis=(1, 2)) / tokens
+    bound = 2.0 ** -24 * (tokens * dim + 6) * mag
+    assert (np.abs(outs[0][1] - outs[1][1]) <= 2 * bound).all()
+    gt, gb = oreward.select(outs[0][1], 2, 2)
+    np.testing.assert_array_equal(outs[0][2], gt)
+    np.testing.assert_array_equal(outs[0][3], gb)
 
 
 @pytest.mark.parametrize("layout", ["panel", "row"])
