@@ -129,6 +129,52 @@ def rank_stats(a, b, k):
             "bottom_overlap": len(ba & bb), "k": k}
 
 
+def step_ablation(noise, w1, w2, u, cfg, chunk, fp4_steps=(2, 3, 4, 6, 8, 10), ref_steps=20):
+    """The step-count ablation and the Stage-2 regeneration cost (project
+    page, "Two-Stage Pipeline": FP4 rollouts rank the seeds, the selected K
+    are regenerated in BF16 with the full step budget; aitrends summary: 6 FP4
+    steps). The reference ranking is a BF16 rollout of all candidates with
+    ref_steps steps; each FP4 rollout with S steps is compared with it
+    (Spearman, Kendall, top/bottom-K overlap). Then the BF16 regeneration of
+    the K selected seeds of the 6-step FP4 rollout is timed against that FP4
+    exploration of all candidates. Synthetic weights: the numbers describe
+    this network, not a trained DiT."""
+    import torch
+    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
+    k_top, k_bottom, tokens = cfg["k_top"], cfg["k_bottom"], cfg["tokens"]
+    bchunk = min(chunk, 8)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = fn()
+        torch.cuda.synchronize()
+        return res, time.perf_counter() - t0
+
+    r_ref, t_ref = timed(lambda: bf16_rollout(noise, w1, w2, u, ref_steps, tokens, bchunk))
+    r_ref = r_ref.cpu().numpy()
+    out = {"reference": {"kind": "bf16 linears (torch)", "steps": ref_steps, "seconds": round(t_ref, 3)},
+           "fp4": {}}
+    work = torch.empty_like(noise)
+    sel = None
+    for s in fp4_steps:
+        ro = Fp4Rollout(w1, w2, u, steps=s, k_top=k_top, k_bottom=k_bottom, chunk=chunk)
+        ro.run(noise, work)  # warm (buffers, weights)
+        (r, top, bottom, _), t_s = timed(lambda: ro.run(noise, work))
+        out["fp4"][str(s)] = {"seconds": round(t_s, 3), **rank_stats(r.cpu().numpy(), r_ref, k_top)}
+        if s == cfg["steps"]:
+            sel, t_explore = torch.cat([top, bottom]).long(), t_s
+    if sel is not None:
+        seeds = noise.index_select(0, sel).contiguous()
+        _, t_regen = timed(lambda: bf16_rollout(seeds, w1, w2, u, ref_steps, tokens, bchunk))
+        out["stage2_regeneration"] = {"seeds": int(sel.numel()), "bf16_steps": ref_steps,
+                                      "seconds": round(t_regen, 3),
+                                      "fp4_exploration_seconds": round(t_explore, 3),
+                                      "fp4_exploration": f"{noise.shape[0]} seeds x {cfg['steps']} steps",
+                                      "regeneration_over_exploration": round(t_regen / t_explore, 3)}
+    return out
+
+
 def cpu_baseline(cfg, tokens_sample=128, w_rows_sample=1024):
     """The CPU oracle on a bounded sample of the rollout, scaled to candidates/s:
     (a) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one W1,
@@ -282,6 +328,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also run the FP4 step-count ablation (2..10 steps against a 20-step BF16 rollout) and "
+                         "time the BF16 regeneration of the selected seeds")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
@@ -388,6 +437,10 @@ def main():
             log(f"bf16 rollout for rank agreement: {time.time() - t0:.1f}s")
         except Exception as e:  # reported, never fatal
             out["rank_agreement_vs_bf16"] = {"error": repr(e)}
+    if args.ablation:
+        t0 = time.time()
+        out["step_ablation"] = step_ablation(noise, w1, w2, u, cfg, chunk)
+        log(f"step ablation: {time.time() - t0:.1f}s")
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(cfg)
