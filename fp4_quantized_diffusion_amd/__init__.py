@@ -12,7 +12,8 @@ _BINDING_NAMES = {
     "status_str", "EXPORTS", "LIB_PATH", "FMT_MX", "FMT_NV", "DT_F32", "DT_BF16", "PRO_RMSNORM", "PRO_GELU",
     "TENSOR_SCALE_GIVEN", "LAYOUT_PANEL", "fp4_panel_bytes", "fp4_gemm_panel", "panel_bytes",
     "fp4_gemm_panel_euler", "gemm_euler", "fp4_gemm_panel_gelu", "gemm_gelu", "fp4_quantize_lora", "quantize_lora",
-    "fp4_gemm_panel_euler_reward", "gemm_euler_reward",
+    "fp4_gemm_panel_euler_reward", "gemm_euler_reward", "fp4_quantize_nv_grouped", "quantize_nv_grouped",
+    "fp4_gemm_nv_grouped",
 }
 
 

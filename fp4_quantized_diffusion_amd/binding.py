@@ -2,11 +2,12 @@
 
 Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
-  * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_panel_bytes,
+  * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_quantize_nv_grouped,
+    fp4_panel_bytes, fp4_gemm_nv_grouped,
     fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, fp4_gemm_panel_euler_reward, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
-  * torch-tensor helpers (quantize, quantize_lora, gemm, gemm_gelu, gemm_euler, gemm_euler_reward, euler,
+  * torch-tensor helpers (quantize, quantize_lora, quantize_nv_grouped, gemm, gemm_gelu, gemm_euler, gemm_euler_reward, euler,
     proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
@@ -32,8 +33,11 @@ _SIGS = {
     "fp4_quantize": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
     "fp4_quantize_lora": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _i32, _i64, _f32, _p, _i64, _p, _i64,
                           _i32, _p],
+    "fp4_quantize_nv_grouped": [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
     "fp4_panel_bytes": [_i64, _i64, _p, _p],
     "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
+    "fp4_gemm_nv_grouped": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64,
+                            _p, _p],
     "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "fp4_gemm_panel_gelu": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p],
     "fp4_gemm_panel_euler": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p],
@@ -91,6 +95,18 @@ def fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, l
              ldc, residual, stream):
     return load_library().fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts,
                                    m, n, k, c, c_dtype, ldc, residual, stream)
+
+
+def fp4_quantize_nv_grouped(x, x_dtype, rows, k, ldx, rows_per_group, codes, ld_codes, scales, ld_scales,
+                            tensor_scales, flags, stream):
+    return load_library().fp4_quantize_nv_grouped(x, x_dtype, rows, k, ldx, rows_per_group, codes, ld_codes, scales,
+                                                  ld_scales, tensor_scales, flags, stream)
+
+
+def fp4_gemm_nv_grouped(a_codes, lda, a_scales, ld_as, a_ts, a_rows_per_group, b_codes, ldb, b_scales, ld_bs, b_ts,
+                        m, n, k, c, c_dtype, ldc, residual, stream):
+    return load_library().fp4_gemm_nv_grouped(a_codes, lda, a_scales, ld_as, a_ts, a_rows_per_group, b_codes, ldb,
+                                              b_scales, ld_bs, b_ts, m, n, k, c, c_dtype, ldc, residual, stream)
 
 
 def fp4_panel_bytes(rows, k, code_bytes, scale_bytes):
@@ -178,6 +194,7 @@ class QTensor(NamedTuple):
     k: int
     layout: str = "row"
     rows: int = 0
+    rows_per_group: int = 0  # NV: rows per tensor scale (0: one for all rows)
 
     @property
     def n_rows(self):
@@ -275,6 +292,31 @@ def quantize_lora(w, lora_b, lora_a, scale, out=None, layout="row"):
     return out
 
 
+def quantize_nv_grouped(x, rows_per_group, tensor_scales=None, out=None):
+    """NVFP4-style QTensor of x [rows, k] (fp32 or bf16) with one tensor scale
+    per group of rows_per_group rows (fp4_quantize_nv_grouped); tensor_scales:
+    optional fp32 [rows / rows_per_group] to use instead of computing them."""
+    torch = _torch()
+    if not _row_view_ok(x):
+        raise ValueError("x must be 2-D with unit inner stride")
+    rows, k = x.shape
+    if rows_per_group < 1 or rows % rows_per_group:
+        raise ValueError("rows_per_group must divide the row count")
+    if out is None:
+        out = _alloc_rows(rows, k, x.device, FMT_NV)
+        out = out._replace(tensor_scale=torch.empty(rows // rows_per_group, dtype=torch.float32, device=x.device))
+    out = out._replace(rows_per_group=rows_per_group)
+    flags = 0
+    if tensor_scales is not None:
+        out.tensor_scale.copy_(tensor_scales.reshape(-1))
+        flags = TENSOR_SCALE_GIVEN
+    st = fp4_quantize_nv_grouped(x.data_ptr(), _dtype_code(x), rows, k, x.stride(0), rows_per_group,
+                                 out.codes.data_ptr(), out.codes.stride(0), out.scales.data_ptr(),
+                                 out.scales.stride(0), out.tensor_scale.data_ptr(), flags, _stream())
+    _check(st, "fp4_quantize_nv_grouped")
+    return out
+
+
 def gemm(a, b, out_dtype="bf16", residual=None, out=None):
     """C = A_hat B_hat^T (+ residual) for QTensors a [m, k] and b [n, k] of
     one format and one layout."""
@@ -290,6 +332,13 @@ def gemm(a, b, out_dtype="bf16", residual=None, out=None):
         st = fp4_gemm_panel(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
                             m, n, k, out.data_ptr(), _dtype_code(out), out.stride(0), _ptr(residual), _stream())
         _check(st, "fp4_gemm_panel")
+        return out
+    if a.rows_per_group:  # NV with one tensor scale per row group of A
+        st = fp4_gemm_nv_grouped(a.codes.data_ptr(), a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(0),
+                                 a.tensor_scale.data_ptr(), a.rows_per_group, b.codes.data_ptr(), b.codes.stride(0),
+                                 b.scales.data_ptr(), b.scales.stride(0), _ptr(b.tensor_scale), m, n, k,
+                                 out.data_ptr(), _dtype_code(out), out.stride(0), _ptr(residual), _stream())
+        _check(st, "fp4_gemm_nv_grouped")
         return out
     st = fp4_gemm(a.fmt, a.codes.data_ptr(), a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(0),
                   _ptr(a.tensor_scale), b.codes.data_ptr(), b.codes.stride(0), b.scales.data_ptr(),

@@ -327,6 +327,43 @@ FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 105; }
+FP4_API fp4_status fp4_quantize_nv_grouped(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                                           int64_t rows_per_group, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                                           int64_t ld_scales, float* tensor_scales, int flags, void* stream) {
+  try {
+    const fp4_status s = check_quantize(FP4_FMT_NV, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales,
+                                        tensor_scales, flags);
+    if (s != FP4_OK) return s;
+    if (rows_per_group < 1 || rows % rows_per_group != 0) return FP4_INVALID_ARGUMENT;
+    return from_hip(fp4r::launch_quant_nv_grouped(x, x_dtype == FP4_DT_BF16, rows, k, ldx, rows_per_group, codes,
+                                                  ld_codes, scales, ld_scales, tensor_scales,
+                                                  (flags & FP4_TENSOR_SCALE_GIVEN) ? 1 : 0,
+                                                  static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API fp4_status fp4_gemm_nv_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_scales, int64_t ld_as,
+                                       const float* a_ts, int64_t a_rows_per_group, const uint8_t* b_codes,
+                                       int64_t ldb, const uint8_t* b_scales, int64_t ld_bs, const float* b_ts,
+                                       int64_t m, int64_t n, int64_t k, void* c, int c_dtype, int64_t ldc,
+                                       const float* residual, void* stream) {
+  try {
+    const fp4_status s = check_gemm(FP4_FMT_NV, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs,
+                                    b_ts, m, n, k, c, c_dtype, ldc, residual);
+    if (s != FP4_OK) return s;
+    if (a_rows_per_group < 1 || m % a_rows_per_group != 0) return FP4_INVALID_ARGUMENT;
+    // the grouped scales ride in the f16-MFMA kernel, which loads scale rows as words
+    if (ld_as % 4 != 0 || ld_bs % 4 != 0 || !aligned(a_scales, 4) || !aligned(b_scales, 4)) return FP4_UNSUPPORTED;
+    return from_hip(fp4r::launch_gemm_nv_f16(a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts,
+                                             m, n, k, c, c_dtype == FP4_DT_BF16, ldc, residual,
+                                             static_cast<hipStream_t>(stream), a_rows_per_group));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API int fp4_abi_version(void) { return 106; }
 
 }  // extern "C"

@@ -44,7 +44,10 @@ hipError_t launch_gemm_nv(const uint8_t* a, int64_t lda, const uint8_t* as, int6
 hipError_t launch_gemm_nv_f16(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
                               const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
                               int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc, const float* residual,
-                              hipStream_t st);
+                              hipStream_t st, int64_t a_rows_per_group = 0);
+hipError_t launch_quant_nv_grouped(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx, int64_t rpg,
+                                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                   float* tensor_scales, int scale_given, hipStream_t st);
 hipError_t launch_euler(float* x_out, const float* x, const void* v, int v_bf16, int64_t numel,
                         float t_cur, float t_next, hipStream_t st);
 hipError_t launch_proxy_reward(const float* x, int64_t n_cand, int64_t rows_per_cand, int64_t dim,

@@ -87,6 +87,7 @@ using Stage = StageT<LD == LD_NV ? SCB_NV : SCB>;
 struct Problem {
   const uint8_t *a, *as, *b, *bs;
   const float *a_ts, *b_ts;        // NVFP4-style tensor scales
+  int a_rpg;                       //   A's rows per tensor-scale group (0: one scale for all of A)
   const float* ex;                 // Euler epilogue: the state x, and the step dt
   float dt;
   const float* ru;                 // Euler + reward epilogue: the reward weights u [N]
@@ -792,6 +793,21 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
 // residual GEMM into v followed by the Euler kernel, so bit-identical to
 // them. Every element is read and written by the same lane, so C may alias
 // x or residual.
+// v = sum * scale + residual for four values, the tensor-scale product fused
+// into the add (one rounding; with no tensor scale, scale is 1 and this is
+// the plain add). Written out so that every epilogue path rounds alike.
+__device__ __forceinline__ void scale_add(float* o, float mt, float4 r) {
+  o[0] = fmaf(o[0], mt, r.x); o[1] = fmaf(o[1], mt, r.y); o[2] = fmaf(o[2], mt, r.z); o[3] = fmaf(o[3], mt, r.w);
+}
+
+// NVFP4-style: the product of the two tensor scales for output row m -- one
+// for the whole call, or A's scale of m's row group times B's.
+__device__ __forceinline__ float row_scale(const Problem& p, int m, float mul) {
+  if (p.a_rpg == 0) return mul;
+  const int mc = m < p.M ? m : p.M - 1;
+  return p.a_ts[(uint32_t)mc / (uint32_t)p.a_rpg] * (*p.b_ts);
+}
+
 template <int BF16OUT, int RESID, bool FULL, bool SCALE>
 __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_base, const Problem& p, void* c,
                                            int64_t ldc, const float* residual, float mul) {
@@ -813,16 +829,16 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
       }
       float o[16];
       gather16(acc[t & 3][t >> 2], o);
-      if (SCALE) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[e] *= mul;
-      }
+      const float mt = SCALE ? row_scale(p, m_base + 32 * (t >> 2) + r32, mul) : 1.0f;
       if (RESID) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 r4 = rq[t % 3][g4];
-          o[4 * g4] += r4.x; o[4 * g4 + 1] += r4.y; o[4 * g4 + 2] += r4.z; o[4 * g4 + 3] += r4.w;
+          scale_add(o + 4 * g4, mt, r4);
         }
+      } else if (SCALE) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] *= mt;
       }
       if (EULER) {
 #pragma unroll
@@ -842,11 +858,12 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
   for (int t = 0; t < 16; ++t) {
     float o[16];
     gather16(acc[t & 3][t >> 2], o);
-    if (SCALE) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[e] *= mul;
-    }
     const int m = m_base + 32 * (t >> 2) + r32;
+    const float mt = SCALE ? row_scale(p, m, mul) : 1.0f;
+    if (SCALE && !RESID) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] *= mt;
+    }
     const int n = n_base + 32 * (t & 3) + 16 * h;
     if (m >= p.M || n >= p.N) continue;
     const int64_t off = (int64_t)m * ldc + n;
@@ -855,9 +872,7 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
         float4 r[4];
         load_res16(r, residual + off);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          o[4 * g4] += r[g4].x; o[4 * g4 + 1] += r[g4].y; o[4 * g4 + 2] += r[g4].z; o[4 * g4 + 3] += r[g4].w;
-        }
+        for (int g4 = 0; g4 < 4; ++g4) scale_add(o + 4 * g4, mt, r[g4]);
       }
       if (EULER) {
         float4 x4[4];
@@ -874,7 +889,7 @@ __device__ __forceinline__ void store_tile(v16f acc[4][4], int m_base, int n_bas
       for (int e = 0; e < 16; ++e) {
         if (n + e >= p.N) continue;
         float x = o[e];
-        if (RESID) x += residual[off + e];
+        if (RESID) x = fmaf(x, mt, residual[off + e]);
         if (EULER) x = fmaf(p.dt, x, p.ex[off + e]);
         if (BF16OUT)
           reinterpret_cast<__bf16*>(c)[off + e] = (__bf16)x;
@@ -1034,6 +1049,7 @@ Problem make_problem(const uint8_t* a, const uint8_t* as, const uint8_t* b, cons
   Problem p;
   p.a = a; p.as = as; p.b = b; p.bs = bs;
   p.a_ts = p.b_ts = nullptr;
+  p.a_rpg = 0;
   p.ex = nullptr;
   p.dt = 0.0f;
   p.qc = p.qs = nullptr;
@@ -1066,11 +1082,12 @@ hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int6
 hipError_t launch_gemm_nv_f16(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
                               const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
                               int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc, const float* residual,
-                              hipStream_t st) {
+                              hipStream_t st, int64_t a_rows_per_group) {
   Problem p = make_problem(a, as, b, bs, m, n, k);
   p.lda = lda; p.ld_as = ld_as; p.ldb = ldb; p.ld_bs = ld_bs;
   p.nblk = (int)(k >> 4);
   p.a_ts = a_ts; p.b_ts = b_ts;
+  p.a_rpg = (int)a_rows_per_group;
   return dispatch(p, c, c_bf16, ldc, residual, st, LD_NV);
 }
 

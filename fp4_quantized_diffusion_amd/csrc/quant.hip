@@ -398,15 +398,58 @@ __device__ __forceinline__ float e4m3_value(uint32_t S) {
   return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
 }
 
-// Codes and E4M3 block scales, in the row-major kernels' steps (a 16-block is
-// two adjacent lanes of one step), kUnroll steps per pass.
+// Per-group tensor amax (GROUPED quantization: one tensor scale per group of
+// rpg rows, e.g. per candidate): workgroup (g, s) takes slice s of group g's
+// rows, one integer atomicMax at its end, as nv_amax_kernel.
 template <int BF16>
+__global__ __launch_bounds__(kThreads) void nv_amax_group_kernel(const void* __restrict__ x, int64_t ldx, int64_t opr,
+                                                                 int64_t rpg, int64_t rows_per_slice, float* ts) {
+  __shared__ uint32_t sh[kThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int64_t r0 = g * rpg + (int64_t)blockIdx.y * rows_per_slice;
+  const int64_t r1 = min(r0 + rows_per_slice, (g + 1) * rpg);
+  uint32_t m = 0;
+  for (int64_t row = r0; row < r1; ++row)
+    for (int64_t oct = threadIdx.x; oct < opr; oct += kThreads) {
+      float v[8];
+      load8<BF16>(x, row * ldx + oct * 8, v);
+      m = max(m, amax_bits8(v));
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t = max(t, sh[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(ts + g), t);
+  }
+}
+
+__global__ void nv_zero_groups_kernel(float* ts, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) reinterpret_cast<uint32_t*>(ts)[i] = 0u;
+}
+
+// s_g of every group, as nv_finalize_kernel.
+__global__ void nv_finalize_groups_kernel(float* ts, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float at = __uint_as_float(reinterpret_cast<const uint32_t*>(ts)[i]);
+  const float sg = at / 2688.0f;
+  ts[i] = (sg == 0.0f) ? 1.0f : sg;
+}
+
+// Codes and E4M3 block scales, in the row-major kernels' steps (a 16-block is
+// two adjacent lanes of one step), kUnroll steps per pass. GROUPED: the
+// tensor scale of row r is ts[r / rpg] (rows, rpg < 2^31).
+template <int BF16, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
     const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps,
-    const float* __restrict__ ts) {
-  const float sg = *ts;
-  const float tau = 6.0f * sg;
+    const float* __restrict__ ts, int64_t rpg) {
+  const float sg0 = GROUPED ? 0.0f : *ts;
+  const float tau0 = 6.0f * sg0;
   const int64_t G = gridDim.x;
   for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
     float vv[kUnroll][8];
@@ -424,6 +467,8 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
     // whole 16-blocks drop out: opr is even
     if (st0 + u * G >= steps || octs[u] >= opr) continue;
     const int64_t row = rows[u], oct = octs[u];
+    const float sg = GROUPED ? ts[(uint32_t)row / (uint32_t)rpg] : sg0;  // row is uniform over the workgroup
+    const float tau = GROUPED ? 6.0f * sg : tau0;
     float* v = vv[u];
     uint32_t am = amax_bits8(v);
     am = max(am, (uint32_t)__shfl_xor((int)am, 1));  // the 2 octets of a 16-block
@@ -553,11 +598,42 @@ hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, i
     nv_finalize_kernel<<<1, 1, 0, st>>>(tensor_scale);
   }
   if (x_bf16)
-    quant_nv_kernel<1><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                tensor_scale);
+    quant_nv_kernel<1, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                       tensor_scale, rows);
   else
-    quant_nv_kernel<0><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                tensor_scale);
+    quant_nv_kernel<0, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                       tensor_scale, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nv_grouped(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx, int64_t rpg,
+                                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                   float* tensor_scales, int scale_given, hipStream_t st) {
+  const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
+  const int64_t groups = rows / rpg;
+  const unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
+  if (!scale_given) {
+    const unsigned gz = (unsigned)((groups + 255) / 256);
+    nv_zero_groups_kernel<<<gz, 256, 0, st>>>(tensor_scales, groups);
+    // about 2048 workgroups in all: slices of each group's rows
+    int64_t slices = (2048 + groups - 1) / groups;
+    if (slices > rpg) slices = rpg;
+    if (slices > 65535) slices = 65535;
+    const int64_t rps = (rpg + slices - 1) / slices;
+    slices = (rpg + rps - 1) / rps;
+    const dim3 ga((unsigned)groups, (unsigned)slices);
+    if (x_bf16)
+      nv_amax_group_kernel<1><<<ga, kThreads, 0, st>>>(x, ldx, opr, rpg, rps, tensor_scales);
+    else
+      nv_amax_group_kernel<0><<<ga, kThreads, 0, st>>>(x, ldx, opr, rpg, rps, tensor_scales);
+    nv_finalize_groups_kernel<<<gz, 256, 0, st>>>(tensor_scales, groups);
+  }
+  if (x_bf16)
+    quant_nv_kernel<1, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                      tensor_scales, rpg);
+  else
+    quant_nv_kernel<0, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
+                                                      tensor_scales, rpg);
   return hipGetLastError();
 }
 

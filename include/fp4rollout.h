@@ -155,6 +155,27 @@ FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_
                         int64_t ld_scales, int flags, void* stream);
 
 /*
+ * fp4_quantize_nv_grouped -- fp4_quantize(FP4_FMT_NV, ...) with one tensor
+ * scale per group of rows_per_group consecutive rows instead of one for the
+ * whole argument: with the rollout's activations grouped per candidate, one
+ * candidate's values no longer set another's tensor scale (the NVFP4 format
+ * the pages name couples everything under one tensor scale). Group g's rows
+ * are quantized exactly as fp4_quantize(FP4_FMT_NV) would quantize those rows
+ * alone.
+ *   x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scales
+ *                   as for fp4_quantize with FP4_FMT_NV (row-major).
+ *   rows_per_group  >= 1, dividing rows.
+ *   tensor_scales   device float [rows / rows_per_group], 4-byte aligned:
+ *                   receives each group's s_g, or supplies them with
+ *                   FP4_TENSOR_SCALE_GIVEN (positive and finite); otherwise
+ *                   also the groups' amax accumulators while the call runs.
+ *   flags           0 or FP4_TENSOR_SCALE_GIVEN.
+ */
+FP4_API fp4_status fp4_quantize_nv_grouped(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                        int64_t rows_per_group, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                        int64_t ld_scales, float* tensor_scales, int flags, void* stream);
+
+/*
  * fp4_panel_bytes -- sizes of the panel layout of a [rows, k] MXFP4 operand:
  *   *code_bytes  = ceil(rows / 256) * ceil(k / 128) * 16384,
  *   *scale_bytes = ceil(rows / 256) * ceil(k / 128) * 1024.
@@ -190,6 +211,22 @@ FP4_API fp4_status fp4_gemm(int fmt,
                     const float* b_ts,
                     int64_t m, int64_t n, int64_t k,
                     void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
+
+/*
+ * fp4_gemm_nv_grouped -- fp4_gemm(FP4_FMT_NV, ...) for an A quantized by
+ * fp4_quantize_nv_grouped: row m of C takes the tensor scale of m's group,
+ *   C[m, n] = a_ts[m / a_rows_per_group] * b_ts[0] * sum_k (G dec(S))_A (G dec(S))_B  (+ residual)
+ * so each group's rows equal an fp4_gemm of that group alone, bit for bit.
+ *   a_ts              device float [m / a_rows_per_group] (4-byte aligned).
+ *   a_rows_per_group  >= 1, dividing m.
+ *   other arguments   as for fp4_gemm with FP4_FMT_NV; scale rows must be
+ *                     4-byte aligned (ld_as, ld_bs multiples of 4, as
+ *                     fp4_quantize's outputs are), else FP4_UNSUPPORTED.
+ */
+FP4_API fp4_status fp4_gemm_nv_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_scales, int64_t ld_as,
+                        const float* a_ts, int64_t a_rows_per_group, const uint8_t* b_codes, int64_t ldb,
+                        const uint8_t* b_scales, int64_t ld_bs, const float* b_ts, int64_t m, int64_t n, int64_t k,
+                        void* c, int c_dtype, int64_t ldc, const float* residual, void* stream);
 
 /*
  * fp4_gemm_panel -- fp4_gemm for MXFP4 operands in the panel layout (same

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 105
+    assert fq.fp4_abi_version() == 106
 
 
 def test_status_strings(lib):
@@ -246,3 +246,42 @@ def test_gemm_panel_euler_reward_rejects(lib, kw):
                                 dict(rows_per_cand=64)])
 def test_gemm_panel_euler_reward_unsupported(lib, kw):
     assert ger(**kw) == fq.binding.UNSUPPORTED
+
+
+def qg(**kw):
+    a = dict(x=P, x_dtype=0, rows=8, k=64, ldx=64, rpg=4, codes=P2, ld_codes=32, scales=P3, ld_scales=4, ts=P,
+             flags=0, stream=None)
+    a.update(kw)
+    return fq.fp4_quantize_nv_grouped(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(ts=None), dict(ts=P + 2), dict(rpg=0), dict(rpg=3), dict(rpg=16), dict(k=24),
+    dict(flags=0x400), dict(ld_scales=3), dict(x_dtype=4),
+])
+def test_quantize_nv_grouped_rejects(lib, kw):
+    assert qg(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(flags=0x200), dict(flags=0x1)])
+def test_quantize_nv_grouped_unsupported(lib, kw):
+    """The panel layout and the prologues are MX-only, as for fp4_quantize."""
+    assert qg(**kw) == fq.binding.UNSUPPORTED
+
+
+def gng(**kw):
+    a = dict(a=P, lda=32, a_s=P3, ld_as=4, a_ts=P, rpg=4, b=P2, ldb=32, b_s=P3, ld_bs=4, b_ts=P2, m=8, n=8, k=64,
+             c=P, c_dtype=0, ldc=8, residual=None, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_nv_grouped(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(a=None), dict(a_ts=None), dict(b_ts=None), dict(rpg=0), dict(rpg=3), dict(m=0), dict(k=8), dict(ldc=6),
+])
+def test_gemm_nv_grouped_rejects(lib, kw):
+    assert gng(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def test_gemm_nv_grouped_unaligned_scale_rows_unsupported(lib):
+    assert gng(ld_as=5) == fq.binding.UNSUPPORTED
