@@ -12,8 +12,9 @@ Sources (the method's pages):
   * aitrends.kr summary of the same paper, paragraphs on Stage 1 / Stage 2:
     6 FP4 solver steps, top K/2 and bottom K/2 seeds, weights re-quantized to
     FP4 after every update.
-  * VeRL-Omni "DiffusionNFT" docs, section "Algorithm", first equation: the
-    clipped reward normalisation r = 1/2 + 1/2 clip((r_raw - E r_raw)/Z, -1, 1).
+  * VeRL-Omni "DiffusionNFT" docs, section "Algorithm": the clipped reward
+    normalisation r = 1/2 + 1/2 clip((r_raw - E r_raw)/Z, -1, 1), and the
+    implicit positive / negative branch loss of the policy update.
 
 The pages do not define the FP4 block formats; the two formats implemented
 here (MXFP4: E2M1 + E8M0 per 32; NVFP4-style: E2M1 + E4M3 per 16 + fp32 tensor
@@ -40,7 +41,10 @@ Parity status per function:
   lora.merge .................. pinned (exact rationals on small non-square
                                 shapes, all-ones and rank-one closed forms,
                                 s = 0 and B = 0 identities)
+  nft.noise / loss_terms ...... pinned (exact rationals, beta = 0 and equal-
+                                velocity identities, r = 0 / 1 branch
+                                selection, noising end points and slope)
   rollout (composite) ......... parity unpinned beyond the pinned pieces it
                                 composes (statistical comparison only)
 """
-from . import e2m1, mxfp4, nvfp4, gemm, euler, reward, rollout, lora  # noqa: F401
+from . import e2m1, mxfp4, nvfp4, gemm, euler, reward, rollout, lora, nft  # noqa: F401
