@@ -58,11 +58,11 @@ def test_beta_zero_is_plain_regression():
 
 
 def test_r_selects_the_branch():
-    vo, vt, x0, eps, _ = rand(4)
+    vo, vt, x0, eps, _ = (a.astype(np.float64) for a in rand(4))
     beta = 0.5
-    v = eps.astype(np.float64) - x0
-    pos = (((1 - beta) * vo + beta * vt.astype(np.float64) - v) ** 2).sum(axis=1)
-    neg = (((1 + beta) * vo - beta * vt.astype(np.float64) - v) ** 2).sum(axis=1)
+    v = eps - x0
+    pos = (((1 - beta) * vo + beta * vt - v) ** 2).sum(axis=1)
+    neg = (((1 + beta) * vo - beta * vt - v) ** 2).sum(axis=1)
     np.testing.assert_allclose(nft.loss_terms(vo, vt, x0, eps, np.ones(3), beta), pos, rtol=1e-14)
     np.testing.assert_allclose(nft.loss_terms(vo, vt, x0, eps, np.zeros(3), beta), neg, rtol=1e-14)
 
