@@ -93,24 +93,30 @@ def make_inputs(cfg, device):
     return noise_d, w1, w2, u
 
 
-def bf16_rollout(noise, w1, w2, u, steps, tokens, chunk):
-    """Same rollout with bf16 linears (torch), for rank agreement only."""
+def bf16_velocity(x, w1, w2):
+    """The velocity network with bf16 linears (torch): fp32 [rows, dim] in and out."""
     import torch
     import torch.nn.functional as F
+    h = x.clone()
+    for a, b in zip(w1, w2):
+        y = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + 1e-6)
+        z = F.gelu(F.linear(y.bfloat16(), a).float())
+        h = h + F.linear(z.bfloat16(), b).float()
+    return h
+
+
+def bf16_rollout(noise, w1, w2, u, steps, tokens, chunk, return_x=False):
+    """Same rollout with bf16 linears (torch): rank agreement, the step
+    ablation's reference and the Stage-2 regeneration."""
     n_cand, _, dim = noise.shape
     x = noise.reshape(-1, dim).clone()
     t = [1.0 - i / steps for i in range(steps + 1)]
     for i in range(steps):
         for c0 in range(0, n_cand, chunk):
             xs = x[c0 * tokens:(c0 + chunk) * tokens]
-            h = xs.clone()
-            for a, b in zip(w1, w2):
-                y = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + 1e-6)
-                z = F.gelu(F.linear(y.bfloat16(), a).float())
-                h = h + F.linear(z.bfloat16(), b).float()
-            xs.add_(h, alpha=(t[i + 1] - t[i]))
+            xs.add_(bf16_velocity(xs, w1, w2), alpha=(t[i + 1] - t[i]))
     r = (x.view(n_cand, tokens, dim).mean(1) @ u)
-    return r
+    return (r, x.view(n_cand, tokens, dim)) if return_x else r
 
 
 def rank_stats(a, b, k):
@@ -163,16 +169,72 @@ def step_ablation(noise, w1, w2, u, cfg, chunk, fp4_steps=(2, 3, 4, 6, 8, 10), r
         (r, top, bottom, _), t_s = timed(lambda: ro.run(noise, work))
         out["fp4"][str(s)] = {"seconds": round(t_s, 3), **rank_stats(r.cpu().numpy(), r_ref, k_top)}
         if s == cfg["steps"]:
-            sel, t_explore = torch.cat([top, bottom]).long(), t_s
+            sel, t_explore, r_fp4 = torch.cat([top, bottom]).long(), t_s, r.cpu().numpy()
     if sel is not None:
         seeds = noise.index_select(0, sel).contiguous()
-        _, t_regen = timed(lambda: bf16_rollout(seeds, w1, w2, u, ref_steps, tokens, bchunk))
+        (r_regen, x_regen), t_regen = timed(lambda: bf16_rollout(seeds, w1, w2, u, ref_steps, tokens, bchunk,
+                                                                 return_x=True))
         out["stage2_regeneration"] = {"seeds": int(sel.numel()), "bf16_steps": ref_steps,
                                       "seconds": round(t_regen, 3),
                                       "fp4_exploration_seconds": round(t_explore, 3),
                                       "fp4_exploration": f"{noise.shape[0]} seeds x {cfg['steps']} steps",
                                       "regeneration_over_exploration": round(t_regen / t_explore, 3)}
+        out["nft_loss_forward"] = nft_forward(x_regen, r_regen, w1, w2, tokens, bchunk)
+        out["evt_diagnostic"] = evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, bchunk)
     return out
+
+
+def nft_forward(x0, r_raw, w1, w2, tokens, chunk, beta=0.1, seed=3):
+    """DiffusionNFT loss forward on the regenerated samples (VeRL-Omni
+    DiffusionNFT docs, "Algorithm"): r = the normalized rewards
+    (select_topk_bottomk's r_norm), x_t = (1 - t) x0 + t eps at a random t
+    per sample (fp4_nft_noise), v_old from the network, v_theta from the
+    network with a small weight perturbation standing in for the trained
+    adapter, then fp4_nft_loss; the two kernels are timed against HBM."""
+    import torch
+    import fp4_quantized_diffusion_amd as fq
+    n, _, dim = x0.shape
+    g = torch.Generator(device=x0.device).manual_seed(seed)
+    eps = torch.randn(x0.shape, generator=g, device=x0.device)
+    t = torch.rand(n, generator=g, device=x0.device)
+    _, _, rn = fq.select(r_raw.float().contiguous(), 1, 1)
+    xt = fq.nft_noise(x0.contiguous(), eps, t)
+    w1p = [w + (0.01 * w.float().std() * torch.randn(w.shape, generator=g, device=w.device)).bfloat16() for w in w1]
+    v_old = torch.empty_like(xt)
+    v_theta = torch.empty_like(xt)
+    flat = xt.view(-1, dim)
+    for c0 in range(0, n, chunk):
+        rows = slice(c0 * tokens, (c0 + chunk) * tokens)
+        v_old.view(-1, dim)[rows] = bf16_velocity(flat[rows], w1, w2)
+        v_theta.view(-1, dim)[rows] = bf16_velocity(flat[rows], w1p, w2)
+    loss, terms = fq.nft_loss(v_old, v_theta, x0.contiguous(), eps, rn, beta)
+    x0c = x0.contiguous()
+    t_noise = time_launches([lambda: fq.nft_noise(x0c, eps, t, out=xt)], reps=20)
+    t_loss = time_launches([lambda: fq.nft_loss(v_old, v_theta, x0c, eps, rn, beta)], reps=20)
+    elems = x0.numel()
+    return {"samples": n, "beta": beta, "loss": round(float(loss.item()), 6),
+            "noise_us": round(t_noise[0], 1), "noise_tbps": round(elems * 12 / t_noise[0] / 1e6, 3),
+            "loss_us": round(t_loss[0], 1), "loss_tbps": round(elems * 16 / t_loss[0] / 1e6, 3)}
+
+
+def evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, bchunk):
+    """The extreme-value statement of the aitrends summary: the expected
+    reward range of the FP4-selected extremes is at least
+    2 sigma sqrt(2 log N) - 4 Delta, with sigma the reward spread and Delta
+    the largest FP4-vs-BF16 reward perturbation. One draw of N candidates:
+    W = BF16 reward of the FP4 top-1 seed minus that of the FP4 bottom-1
+    seed, both rollouts with the same step count."""
+    import math
+    s = cfg["steps"]
+    r4 = np.asarray(r_fp4, dtype=np.float64)
+    rb = bf16_rollout(noise, w1, w2, u, s, cfg["tokens"], bchunk).cpu().numpy().astype(np.float64)
+    n = len(r4)
+    sigma = float(rb.std())
+    delta = float(np.abs(r4 - rb).max())
+    w = float(rb[int(np.argmax(r4))] - rb[int(np.argmin(r4))])
+    bound = 2 * sigma * math.sqrt(2 * math.log(n)) - 4 * delta
+    return {"n": n, "steps": s, "sigma_bf16": round(sigma, 6), "delta_max": round(delta, 6),
+            "range_of_fp4_extremes_in_bf16": round(w, 6), "bound": round(bound, 6), "holds": bool(w >= bound)}
 
 
 def cpu_baseline(cfg, tokens_sample=128, w_rows_sample=1024):

@@ -46,6 +46,8 @@ _SIGS = {
     "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
     "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
     "select_topk_bottomk": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+    "fp4_nft_noise": [_p, _p, _p, _i64, _i64, _p, _p],
+    "fp4_nft_loss": [_p, _p, _p, _p, _p, _f32, _i64, _i64, _p, _p, _p, _p],
 }
 EXPORTS = tuple(_SIGS) + ("fp4_status_str", "fp4_abi_version")
 
@@ -147,6 +149,14 @@ def fp4_proxy_reward(x, n_cand, rows_per_cand, dim, ldx, u, rewards, stream):
 
 def select_topk_bottomk(rewards, n, k_top, k_bottom, top_idx, bottom_idx, r_norm, stream):
     return load_library().select_topk_bottomk(rewards, n, k_top, k_bottom, top_idx, bottom_idx, r_norm, stream)
+
+
+def fp4_nft_noise(x0, eps, t, n, d, x_t, stream):
+    return load_library().fp4_nft_noise(x0, eps, t, n, d, x_t, stream)
+
+
+def fp4_nft_loss(v_old, v_theta, x0, eps, r, beta, n, d, partials, terms, loss, stream):
+    return load_library().fp4_nft_loss(v_old, v_theta, x0, eps, r, beta, n, d, partials, terms, loss, stream)
 
 
 def fp4_abi_version():
@@ -448,3 +458,37 @@ def select(rewards, k_top, k_bottom, normalize=True):
                              _stream())
     _check(st, "select_topk_bottomk")
     return top, bottom, rn
+
+
+def _samples(*ts):
+    n = ts[0].shape[0]
+    for t in ts:
+        if not t.is_contiguous() or t.shape[0] != n or t.numel() != ts[0].numel():
+            raise ValueError("arrays must be contiguous with one shape [n, ...]")
+    return n, ts[0].numel() // n
+
+
+def nft_noise(x0, eps, t, out=None):
+    """x_t = (1 - t) x0 + t eps per sample (fp4_nft_noise); x0, eps fp32
+    [n, ...] contiguous, t fp32 [n]."""
+    torch = _torch()
+    n, d = _samples(x0, eps)
+    if out is None:
+        out = torch.empty_like(x0)
+    _check(fp4_nft_noise(x0.data_ptr(), eps.data_ptr(), t.data_ptr(), n, d, out.data_ptr(), _stream()),
+           "fp4_nft_noise")
+    return out
+
+
+def nft_loss(v_old, v_theta, x0, eps, r, beta):
+    """DiffusionNFT loss (fp4_nft_loss): returns (loss [1], terms [n]) as fp32
+    tensors; all inputs fp32 contiguous [n, ...], r fp32 [n]."""
+    torch = _torch()
+    n, d = _samples(v_old, v_theta, x0, eps)
+    partials = torch.empty(n * 128, dtype=torch.float32, device=x0.device)
+    terms = torch.empty(n, dtype=torch.float32, device=x0.device)
+    loss = torch.empty(1, dtype=torch.float32, device=x0.device)
+    _check(fp4_nft_loss(v_old.data_ptr(), v_theta.data_ptr(), x0.data_ptr(), eps.data_ptr(), r.data_ptr(),
+                        float(beta), n, d, partials.data_ptr(), terms.data_ptr(), loss.data_ptr(), _stream()),
+           "fp4_nft_loss")
+    return loss, terms

@@ -30,6 +30,7 @@ HIP_COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-fvisibil
 HIP_SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "lora.hip": ["-ffp-contract=off"],
+    "nft.hip": ["-ffp-contract=off"],
     "gemm_mx.hip": [],
     "gemm_nv.hip": [],
     "euler.hip": [],

@@ -364,6 +364,34 @@ FP4_API fp4_status fp4_gemm_nv_grouped(const uint8_t* a_codes, int64_t lda, cons
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 106; }
+FP4_API fp4_status fp4_nft_noise(const float* x0, const float* eps, const float* t, int64_t n, int64_t d, float* x_t,
+                                 void* stream) {
+  try {
+    if (!x0 || !eps || !t || !x_t) return FP4_INVALID_ARGUMENT;
+    if (n < 1 || n > 65535 || d < 4 || d % 4 != 0 || d >= ((int64_t)1 << 40)) return FP4_INVALID_ARGUMENT;
+    if (!aligned(x0, 16) || !aligned(eps, 16) || !aligned(x_t, 16) || !aligned(t, 4)) return FP4_INVALID_ARGUMENT;
+    return from_hip(fp4r::launch_nft_noise(x0, eps, t, n, d, x_t, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const float* x0, const float* eps,
+                                const float* r, float beta, int64_t n, int64_t d, float* partials, float* terms,
+                                float* loss, void* stream) {
+  try {
+    if (!v_old || !v_theta || !x0 || !eps || !r || !partials || !terms || !loss) return FP4_INVALID_ARGUMENT;
+    if (n < 1 || n > 65535 || d < 4 || d % 4 != 0 || d >= ((int64_t)1 << 40)) return FP4_INVALID_ARGUMENT;
+    if (!aligned(v_old, 16) || !aligned(v_theta, 16) || !aligned(x0, 16) || !aligned(eps, 16)) return FP4_INVALID_ARGUMENT;
+    if (!aligned(r, 4) || !aligned(partials, 4) || !aligned(terms, 4) || !aligned(loss, 4)) return FP4_INVALID_ARGUMENT;
+    if (!(beta - beta == 0.0f)) return FP4_INVALID_ARGUMENT;  // NaN or infinite
+    return from_hip(fp4r::launch_nft_loss(v_old, v_theta, x0, eps, r, beta, n, d, partials, terms, loss,
+                                          static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API int fp4_abi_version(void) { return 107; }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ hipError_t launch_euler(float* x_out, const float* x, const void* v, int v_bf16,
                         float t_cur, float t_next, hipStream_t st);
 hipError_t launch_proxy_reward(const float* x, int64_t n_cand, int64_t rows_per_cand, int64_t dim,
                                int64_t ldx, const float* u, float* rewards, hipStream_t st);
+hipError_t launch_nft_noise(const float* x0, const float* eps, const float* t, int64_t n, int64_t d, float* xt,
+                            hipStream_t st);
+hipError_t launch_nft_loss(const float* v_old, const float* v_theta, const float* x0, const float* eps,
+                           const float* r, float beta, int64_t n, int64_t d, float* partials, float* terms,
+                           float* loss, hipStream_t st);
 hipError_t launch_select(const float* r, int64_t n, int64_t k_top, int64_t k_bottom,
                          int32_t* top, int32_t* bottom, float* r_norm, hipStream_t st);
 

@@ -364,6 +364,37 @@ FP4_API fp4_status select_topk_bottomk(const float* rewards, int64_t n, int64_t 
                                int32_t* top_idx, int32_t* bottom_idx, float* r_norm, void* stream);
 
 /* Human-readable name of a status code (static string). */
+/*
+ * fp4_nft_noise / fp4_nft_loss -- the DiffusionNFT policy update's forward
+ * pieces on the regenerated samples (VeRL-Omni DiffusionNFT docs,
+ * "Algorithm"; the K seeds the FP4 rollout selects are regenerated in BF16
+ * and trained on with DiffusionNFT -- aitrends summary, Stage-2 paragraph).
+ * Sample i is a row of d fp32 values of each array (n samples; contiguous).
+ *
+ * fp4_nft_noise: the forward process on the rectified-flow path of the
+ * rollout's sampler, x_t[i] = (1 - t[i]) x0[i] + t[i] eps[i], evaluated as
+ * fmaf(t, eps, fl(1 - t) x0). Its velocity, the training target, is
+ * v = eps - x0.
+ *
+ * fp4_nft_loss: with v+ = (1 - beta) v_old + beta v_theta and
+ * v- = (1 + beta) v_old - beta v_theta (the implicit positive and negative
+ * branches; v_old from the rollout policy, v_theta from the trained one, both
+ * at x_t), per sample
+ *   terms[i] = r[i] ||v+ - v||^2 + (1 - r[i]) ||v- - v||^2   (squared norm over d),
+ * and *loss = mean of terms. r is the optimality probability (the r_norm of
+ * select_topk_bottomk). Sums are fp32 in a fixed order (deterministic).
+ *   v_old, v_theta, x0, eps  fp32 [n, d], 16-byte aligned; d a multiple of 4.
+ *   r                 fp32 [n]; beta finite.
+ *   n                 1 .. 65535.
+ *   partials          caller workspace, fp32 [n * 128], 4-byte aligned.
+ *   terms, loss       out: fp32 [n] and fp32 [1].
+ */
+FP4_API fp4_status fp4_nft_noise(const float* x0, const float* eps, const float* t, int64_t n, int64_t d,
+                        float* x_t, void* stream);
+FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const float* x0, const float* eps,
+                        const float* r, float beta, int64_t n, int64_t d, float* partials, float* terms,
+                        float* loss, void* stream);
+
 FP4_API const char* fp4_status_str(fp4_status s);
 
 /* Version of this ABI (major * 100 + minor). */

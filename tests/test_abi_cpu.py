@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 106
+    assert fq.fp4_abi_version() == 107
 
 
 def test_status_strings(lib):
@@ -285,3 +285,26 @@ def test_gemm_nv_grouped_rejects(lib, kw):
 
 def test_gemm_nv_grouped_unaligned_scale_rows_unsupported(lib):
     assert gng(ld_as=5) == fq.binding.UNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
+    (None, P, P2, 2, 8, P3, None), (P, P, P2, 0, 8, P3, None), (P, P, P2, 70000, 8, P3, None),
+    (P, P, P2, 2, 6, P3, None), (P + 4, P, P2, 2, 8, P3, None), (P, P, P2 + 2, 2, 8, P3, None),
+    (P, P, P2, 2, 8, None, None),
+])
+def test_nft_noise_rejects(lib, args):
+    assert fq.fp4_nft_noise(*args) == fq.binding.INVALID_ARGUMENT
+
+
+def nl(**kw):
+    a = dict(vo=P, vt=P, x0=P2, eps=P3, r=P, beta=0.5, n=2, d=8, partials=P2, terms=P3, loss=P, stream=None)
+    a.update(kw)
+    return fq.fp4_nft_loss(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(vo=None), dict(r=None), dict(partials=None), dict(loss=None), dict(n=0), dict(n=65536), dict(d=2),
+    dict(d=10), dict(vt=P + 8), dict(r=P + 2), dict(beta=float("nan")), dict(beta=float("inf")),
+])
+def test_nft_loss_rejects(lib, kw):
+    assert nl(**kw) == fq.binding.INVALID_ARGUMENT
