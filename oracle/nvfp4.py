@@ -45,9 +45,11 @@ def e4m3_decode(code):
 def e4m3_encode(s):
     """Nearest finite E4M3 code of non-negative s, ties to the even code.
 
-    Picking the nearest of the finite codes saturates at 448 by itself (the
-    IEEE rule would overflow only at >= 464, and there is no code above 448)."""
-    s = np.asarray(s, dtype=np.float64)
+    Picking the nearest of the finite codes saturates at 448 (the IEEE rule
+    would overflow only at >= 464, and there is no code above 448). s is
+    clamped to 448 first: for s far above it (or infinite) the distances
+    s - value all round to the same float64, and the nearest would be lost."""
+    s = np.minimum(np.asarray(s, dtype=np.float64), 448.0)
     dist = np.abs(s[..., None] - _E4M3)
     dmin = dist.min(axis=-1, keepdims=True)
     at_min = dist == dmin

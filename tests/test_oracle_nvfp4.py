@@ -45,6 +45,9 @@ def test_e4m3_values_from_bit_fields_and_saturation():
     assert v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
     assert np.all(np.diff(v) > 0)
     assert nvfp4.e4m3_encode(np.array([463.9, 470.0, 1e9])).tolist() == [0x7E] * 3
+    # far above 448, where s - 448 rounds back to s in float64, and +inf
+    # (a block amax over a tiny given tensor scale): still the largest code
+    assert nvfp4.e4m3_encode(np.array([1e20, 5e21, 3e38, np.inf])).tolist() == [0x7E] * 4
     assert nvfp4.e4m3_encode(np.array([2.0 ** -10])).tolist() == [0]       # tie to even zero
     assert nvfp4.e4m3_encode(np.array([1.5 * 2.0 ** -9])).tolist() == [2]  # tie to even code 2
 
