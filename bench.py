@@ -328,7 +328,7 @@ def class_benchmarks(dev, n_sets=4):
             qb = [fq.quantize(w, "mx", layout="panel") for _, w in draws]
             c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             flop = 2.0 * m * n * k
-            key = f"{name}_{'qkv_or_up' if which == 1 else 'down'}_{m}x{k}x{n}"
+            key = f"{name}_{inputs.class_gemm(name, which)[0]}_{m}x{k}x{n}"
             f_us = time_launches([lambda i=i: fq.gemm(qa[i], qb[i], "bf16", out=c) for i in range(n_sets)])
             b_us = time_launches([lambda i=i: F.linear(draws[i][0], draws[i][1]) for i in range(n_sets)])
             g = {"m": m, "k": k, "n": n,
@@ -377,6 +377,44 @@ def class_benchmarks(dev, n_sets=4):
     return gemms, mem
 
 
+def rollout_step_kernels(x, v, u, cfg):
+    """The unfused Euler update (a7), proxy reward (a8) and selection (a9) at
+    the rollout's size, each timed on its own (the rollout fuses the first
+    two into its last GEMMs). x and v are [n_cand * tokens, dim] fp32 of
+    4.83 GB each, far beyond the Infinity Cache, so no rotation is needed;
+    the Euler update runs in place on x."""
+    import torch
+    import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd import binding as fb
+
+    n, tokens, dim = cfg["n_cand"], cfg["tokens"], cfg["dim"]
+    numel = x.numel()
+    out = {}
+    e_us = time_launches([lambda: fq.euler(x, v, 1.0, 5.0 / 6.0, out=x)])
+    out[f"euler_step_{n}x{tokens}x{dim}_f32"] = {
+        "us": [round(a, 1) for a in e_us], "tbps": round(12.0 * numel / e_us[0] / 1e6, 3),
+        "frac_of_hbm": round(12.0 * numel / e_us[0] / 1e-6 / PEAK_HBM, 4)}
+    r = torch.empty(n, dtype=torch.float32, device=x.device)
+    r_us = time_launches([lambda: fq.proxy_reward(x, n, tokens, u, out=r)])
+    out[f"proxy_reward_{n}x{tokens}x{dim}"] = {
+        "us": [round(a, 1) for a in r_us], "tbps": round(4.0 * numel / r_us[0] / 1e6, 3),
+        "frac_of_hbm": round(4.0 * numel / r_us[0] / 1e-6 / PEAK_HBM, 4)}
+    kt, kb = cfg["k_top"], cfg["k_bottom"]
+    top = torch.empty(kt, dtype=torch.int32, device=x.device)
+    bottom = torch.empty(kb, dtype=torch.int32, device=x.device)
+    rn = torch.empty(n, dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def sel():
+        st = fb.select_topk_bottomk(r.data_ptr(), n, kt, kb, top.data_ptr(), bottom.data_ptr(), rn.data_ptr(),
+                                    stream)
+        assert st == 0, fb.status_str(st)
+    s_us = time_launches([sel])
+    # latency-bound: one workgroup, event pair around the two kernels of the call
+    out[f"select_{n}_top{kt}_bottom{kb}"] = {"us": [round(a, 1) for a in s_us]}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +425,8 @@ def main():
     ap.add_argument("--no-rank-agreement", action="store_true")
     ap.add_argument("--no-class-gemms", action="store_true",
                     help="skip the FLUX/SANA/SD3.5-class GEMM, bf16 baseline and quantizer timings")
+    ap.add_argument("--no-step-kernels", action="store_true",
+                    help="skip the standalone Euler / proxy reward / selection timings at the rollout's size")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
@@ -491,6 +531,12 @@ def main():
         t0 = time.time()
         out["class_gemms"], out["memory_kernels"] = class_benchmarks(dev)
         log(f"class benchmarks: {time.time() - t0:.1f}s")
+    if not args.no_step_kernels:
+        # after the rollout's outputs are read: the Euler timing overwrites `work`
+        t0 = time.time()
+        out["rollout_step_kernels"] = rollout_step_kernels(work.view(-1, cfg["dim"]), noise.view(-1, cfg["dim"]),
+                                                           u, cfg)
+        log(f"standalone step kernels: {time.time() - t0:.1f}s")
     if not args.no_rank_agreement:
         try:
             t0 = time.time()

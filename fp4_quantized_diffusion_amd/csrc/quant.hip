@@ -65,13 +65,45 @@ struct GeluLds<1, PRO_GELU> {
 // loads per lane in flight.
 constexpr int kUnroll = 4;
 
+// n / d for a workgroup-uniform step index n and a divisor fixed per launch,
+// without a 64-bit division in the loop: one high multiply, an add and two
+// shifts (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, the unsigned N = 32 case: l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, q = (t + ((n - t) >> min(l, 1))) >>
+// max(l - 1, 0) with t the high word of m n), exact for every n < 2^32.
+// Larger n (or d) take the plain division.
+struct UDiv {
+  int64_t d, lim;  // lim: 2^32 when d < 2^32, else 0 (fast path off)
+  uint32_t m, s1, s2;
+};
+
+UDiv make_udiv(int64_t d) {  // d >= 1
+  UDiv f{d, 0, 0u, 0u, 0u};
+  if (d >= ((int64_t)1 << 32)) return f;
+  int l = 0;
+  while (((int64_t)1 << l) < d) ++l;
+  f.lim = (int64_t)1 << 32;
+  f.m = (uint32_t)(((((uint64_t)1 << l) - (uint64_t)d) << 32) / (uint64_t)d + 1u);
+  f.s1 = l < 1 ? (uint32_t)l : 1u;
+  f.s2 = l > 1 ? (uint32_t)(l - 1) : 0u;
+  return f;
+}
+
+__device__ __forceinline__ int64_t udiv(int64_t n, const UDiv& f) {
+  if (n < f.lim) {
+    const uint32_t x = (uint32_t)n, t = __umulhi(x, f.m);
+    return (int64_t)((t + ((x - t) >> f.s1)) >> f.s2);
+  }
+  return n / f.d;
+}
+
 // Row-major layout, elementwise prologues. Work comes in steps of 256
 // consecutive octets of one row (segs steps per row); a step's row and
 // segment are workgroup-uniform, so the index arithmetic is scalar.
 template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
     const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps) {
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, UDiv segs, int64_t steps) {
   const float* tab = GeluLds<BF16, PRO>().get();
   const int64_t G = gridDim.x;
   for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
@@ -80,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t st = st0 + u * G;
-      row[u] = st / segs;
-      oct[u] = (st - row[u] * segs) * kThreads + threadIdx.x;
+      row[u] = udiv(st, segs);
+      oct[u] = (st - row[u] * segs.d) * kThreads + threadIdx.x;
       // unconditional loads (an idle lane reads the first octet), so that
       // all of them are in flight before the first is waited for
       const bool ok = st < steps && oct[u] < opr;
@@ -109,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
 template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
     const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t nc, int64_t steps) {
+    uint8_t* __restrict__ scales, UDiv nc, int64_t steps) {
   const float* tab = GeluLds<BF16, PRO>().get();
   const int64_t G = gridDim.x;
   for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
@@ -119,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t st = st0 + u * G;
       const int64_t blk = st >> 4;
-      const int64_t pnl = blk / nc, ch = blk - pnl * nc;
+      const int64_t pnl = udiv(blk, nc), ch = blk - pnl * nc.d;
       const int64_t row = pnl * 256 + (int)((st & 15) << 4) + (int)(threadIdx.x >> 4);
       const int64_t e0 = ch * 128 + (int)(threadIdx.x & 15) * 8;
       // a 32-block's 4 octets share row and validity (k is a multiple of 32)
@@ -340,7 +372,7 @@ __global__ void nv_zero_kernel(float* ts) { *reinterpret_cast<uint32_t*>(ts) = 0
 // and segment), kUnroll steps per pass with all loads issued first.
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restrict__ x, int64_t ldx, int64_t opr,
-                                                           int64_t segs, int64_t steps, float* ts) {
+                                                           UDiv segs, int64_t steps, float* ts) {
   __shared__ uint32_t sh[kThreads / 64];
   const int64_t G = gridDim.x;
   uint32_t m = 0;
@@ -350,8 +382,8 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restric
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t st = st0 + u * G;
-      const int64_t row = st / segs;
-      const int64_t oct = (st - row * segs) * kThreads + threadIdx.x;
+      const int64_t row = udiv(st, segs);
+      const int64_t oct = (st - row * segs.d) * kThreads + threadIdx.x;
       ok[u] = st < steps && oct < opr;
       load8<BF16>(x, ok[u] ? row * ldx + oct * 8 : 0, v[u]);
     }
@@ -442,12 +474,12 @@ __global__ void nv_finalize_groups_kernel(float* ts, int64_t n) {
 
 // Codes and E4M3 block scales, in the row-major kernels' steps (a 16-block is
 // two adjacent lanes of one step), kUnroll steps per pass. GROUPED: the
-// tensor scale of row r is ts[r / rpg] (rows, rpg < 2^31).
+// tensor scale of row r is ts[r / rpg].
 template <int BF16, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
     const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, int64_t segs, int64_t steps,
-    const float* __restrict__ ts, int64_t rpg) {
+    uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, UDiv segs, int64_t steps,
+    const float* __restrict__ ts, UDiv rpg) {
   const float sg0 = GROUPED ? 0.0f : *ts;
   const float tau0 = 6.0f * sg0;
   const int64_t G = gridDim.x;
@@ -457,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t st = st0 + u * G;
-      rows[u] = st / segs;
-      octs[u] = (st - rows[u] * segs) * kThreads + threadIdx.x;
+      rows[u] = udiv(st, segs);
+      octs[u] = (st - rows[u] * segs.d) * kThreads + threadIdx.x;
       const bool ok = st < steps && octs[u] < opr;
       load8<BF16>(x, ok ? rows[u] * ldx + octs[u] * 8 : 0, vv[u]);
     }
@@ -467,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
     // whole 16-blocks drop out: opr is even
     if (st0 + u * G >= steps || octs[u] >= opr) continue;
     const int64_t row = rows[u], oct = octs[u];
-    const float sg = GROUPED ? ts[(uint32_t)row / (uint32_t)rpg] : sg0;  // row is uniform over the workgroup
+    const float sg = GROUPED ? ts[udiv(row, rpg)] : sg0;  // row is uniform over the workgroup
     const float tau = GROUPED ? 6.0f * sg : tau0;
     float* v = vv[u];
     uint32_t am = amax_bits8(v);
@@ -480,11 +512,35 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) w |= ((__float_as_uint(v[j]) >> 28) & 8u) << (4 * j);
     } else {
-      // fl(x / d) (correctly rounded division), then its E2M1 code through
-      // the same scaled convert as the MX path, with scale 1
+      // fl(x / d), correctly rounded, then its E2M1 code through the same
+      // scaled convert as the MX path, with scale 1. For d in [2^-100, 2^100]
+      // and |x| / d <= 2^64 (every block whose tensor scale comes from the
+      // data: there |x| / d is at most about 6.4) the quotient takes no
+      // division per element: y = fl(1 / d) once per block, q = fl(x y), then
+      // twice q <- fl(q + fl(x - d q) y) with fmas. The first correction
+      // leaves q within one ulp of x / d (faithful); with y correctly rounded
+      // and q faithful, x - d q is exact and the second correction gives the
+      // correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990;
+      // Muller et al., Handbook of Floating-Point Arithmetic, "Newton-Raphson
+      // based division with an FMA"). The range keeps every intermediate
+      // normal and finite where a code can be non-zero: |x / d| < 2^-3 codes
+      // to a signed zero whatever its last bits. The quotient takes the sign
+      // of x (d > 0) explicitly: for x = -0 the corrections would add +0 to
+      // -0 and return +0. Other blocks (a caller-supplied tensor scale far
+      // from the data, NaN or infinite input) divide.
       float q[8];
+      const float y = 1.0f / d;
+      if (d >= 0x1p-100f && d <= 0x1p100f && __uint_as_float(am) * y <= 0x1p64f) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = v[j] / d;
+        for (int j = 0; j < 8; ++j) {
+          float t = v[j] * y;
+          t = fmaf(fmaf(-d, t, v[j]), y, t);
+          q[j] = __builtin_copysignf(fmaf(fmaf(-d, t, v[j]), y, t), v[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = v[j] / d;
+      }
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
@@ -542,7 +598,7 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
   const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
 #define FP4R_LAUNCH(B, P, TAB)                                                                             \
   quant_mx_kernel<B, P><<<elementwise_grid(quant_mx_kernel<B, P>, steps, TAB), kThreads, 0, st>>>(         \
-      x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps)
+      x, ldx, codes, ld_codes, scales, ld_scales, opr, make_udiv(segs), steps)
   if (prologue == PRO_GELU) {
     if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
     else FP4R_LAUNCH(0, PRO_GELU, false);
@@ -570,7 +626,7 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
   const int64_t steps = panels * nc * 16;  // 256 octets per step, 16 steps per (panel, chunk) block
 #define FP4R_LAUNCH(B, P, TAB)                                                                             \
   quant_mx_panel_kernel<B, P><<<elementwise_grid(quant_mx_panel_kernel<B, P>, steps, TAB), kThreads, 0, st>>>( \
-      x, rows, k, ldx, codes, scales, nc, steps)
+      x, rows, k, ldx, codes, scales, make_udiv(nc), steps)
   if (prologue == PRO_GELU) {
     if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
     else FP4R_LAUNCH(0, PRO_GELU, false);
@@ -592,17 +648,17 @@ hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, i
     // a resident-sized grid: each workgroup issues one atomic at its end
     const unsigned ga = g < 2048 ? g : 2048;
     if (x_bf16)
-      nv_amax_kernel<1><<<ga, kThreads, 0, st>>>(x, ldx, opr, segs, steps, tensor_scale);
+      nv_amax_kernel<1><<<ga, kThreads, 0, st>>>(x, ldx, opr, make_udiv(segs), steps, tensor_scale);
     else
-      nv_amax_kernel<0><<<ga, kThreads, 0, st>>>(x, ldx, opr, segs, steps, tensor_scale);
+      nv_amax_kernel<0><<<ga, kThreads, 0, st>>>(x, ldx, opr, make_udiv(segs), steps, tensor_scale);
     nv_finalize_kernel<<<1, 1, 0, st>>>(tensor_scale);
   }
   if (x_bf16)
-    quant_nv_kernel<1, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                       tensor_scale, rows);
+    quant_nv_kernel<1, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr,
+                                                       make_udiv(segs), steps, tensor_scale, make_udiv(1));
   else
-    quant_nv_kernel<0, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                       tensor_scale, rows);
+    quant_nv_kernel<0, false><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr,
+                                                       make_udiv(segs), steps, tensor_scale, make_udiv(1));
   return hipGetLastError();
 }
 
@@ -629,11 +685,11 @@ hipError_t launch_quant_nv_grouped(const void* x, int x_bf16, int64_t rows, int6
     nv_finalize_groups_kernel<<<gz, 256, 0, st>>>(tensor_scales, groups);
   }
   if (x_bf16)
-    quant_nv_kernel<1, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                      tensor_scales, rpg);
+    quant_nv_kernel<1, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr,
+                                                      make_udiv(segs), steps, tensor_scales, make_udiv(rpg));
   else
-    quant_nv_kernel<0, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr, segs, steps,
-                                                      tensor_scales, rpg);
+    quant_nv_kernel<0, true><<<g, kThreads, 0, st>>>(x, ldx, codes, ld_codes, scales, ld_scales, opr,
+                                                      make_udiv(segs), steps, tensor_scales, make_udiv(rpg));
   return hipGetLastError();
 }
 

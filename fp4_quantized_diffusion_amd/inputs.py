@@ -25,12 +25,23 @@ Recipe:
 """
 import numpy as np
 
-# workload shapes: (M, hidden, mlp); M = candidates x tokens per candidate
+# workload shapes: M = candidates x tokens per candidate, and the two linears
+# timed per class as (name, K, N): SANA-class its attention QKV projection
+# (hidden -> 3 hidden) and MLP down projection, FLUX.1- and SD3.5-L-class
+# their MLP up and down projections
 CLASS_SHAPES = {
-    "sana": dict(m=96 * 1024, hidden=2240, mlp=5600, seed=1, act="normal"),
-    "flux": dict(m=8 * 4608, hidden=3072, mlp=12288, seed=2, act="normal"),
-    "sd35": dict(m=8 * 4352, hidden=2432, mlp=9728, seed=3, act="student_t"),
+    "sana": dict(m=96 * 1024, hidden=2240, mlp=5600, seed=1, act="normal",
+                 gemms=(("qkv", 2240, 6720), ("down", 5600, 2240))),
+    "flux": dict(m=8 * 4608, hidden=3072, mlp=12288, seed=2, act="normal",
+                 gemms=(("up", 3072, 12288), ("down", 12288, 3072))),
+    "sd35": dict(m=8 * 4352, hidden=2432, mlp=9728, seed=3, act="student_t",
+                 gemms=(("up", 2432, 9728), ("down", 9728, 2432))),
 }
+
+
+def class_gemm(name, which):
+    """(label, K, N) of linear `which` (1 or 2) of a workload class."""
+    return CLASS_SHAPES[name]["gemms"][which - 1]
 
 ROLLOUT = dict(n_cand=96, tokens=4096, dim=3072, hidden=12288, blocks=4, steps=6,
                k_top=12, k_bottom=12, seed=4)
@@ -81,11 +92,11 @@ def tiny(seed=0):
 
 
 def class_linear(name, which, rows=None):
-    """Activation [M, K] and weight [N, K] for GEMM `which` (1: hidden->mlp,
-    2: mlp->hidden) of a workload class. `rows` limits M (the draw of the
+    """Activation [M, K] and weight [N, K] for linear `which` (1 or 2, see
+    CLASS_SHAPES) of a workload class. `rows` limits M (the draw of the
     first rows is the same for any limit)."""
     cfg = CLASS_SHAPES[name]
-    k, n = (cfg["hidden"], cfg["mlp"]) if which == 1 else (cfg["mlp"], cfg["hidden"])
+    _, k, n = class_gemm(name, which)
     m = cfg["m"] if rows is None else rows
     rng_w = np.random.default_rng([cfg["seed"], which, 1])
     w = weights(rng_w, n, k)
@@ -100,7 +111,7 @@ def class_linear_device(name, which, device, draw=0, chunk_rows=8192):
     weight [N, K]."""
     import torch
     cfg = CLASS_SHAPES[name]
-    k, n = (cfg["hidden"], cfg["mlp"]) if which == 1 else (cfg["mlp"], cfg["hidden"])
+    _, k, n = class_gemm(name, which)
     m = cfg["m"]
     g = torch.Generator(device=device)
     g.manual_seed(cfg["seed"] * 1000003 + which * 1009 + draw)

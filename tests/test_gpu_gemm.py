@@ -172,7 +172,7 @@ def test_determinism(gpu_lib):
         np.testing.assert_array_equal(to_np(gpu_lib.gemm(qa, qb, "f32")), c0)
 
 
-@pytest.mark.parametrize("cls,which", [("flux", 1), ("flux", 2), ("sana", 2), ("sd35", 1)])
+@pytest.mark.parametrize("cls,which", [("flux", 1), ("flux", 2), ("sana", 1), ("sana", 2), ("sd35", 1)])
 def test_full_size_sampled(gpu_lib, cls, which):
     """Workload-class GEMMs at full size, in the launch configuration the
     benchmark uses (bf16 activations, bf16 output): quantized codes of sampled

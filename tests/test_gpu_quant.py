@@ -137,6 +137,64 @@ def test_element_rounding_sweep_nv(gpu_lib, block_amax):
     np.testing.assert_array_equal(to_np(q.codes)[:, :32], oc)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_nv_quotients_near_decisions_many_divisors(gpu_lib, seed):
+    """The NVFP4-style code of x is decided by the rounded quotient fl(x / d)
+    (d = E4M3 scale times tensor scale). Rows of 16 blocks, groups of 4 rows
+    with their own random given tensor scale (the grouped quantizer), and
+    blocks with random amax give thousands of distinct divisors; each block's
+    other 15 values are fl(q d) for q within 8 ulps of an E2M1 decision point
+    or grid value, or a neighbour of that product. Codes and scales equal the
+    oracle's (per group) bit for bit."""
+    rng = np.random.default_rng(100 + seed)
+    rows, rpg = 1024, 4
+    groups = rows // rpg
+    sg = (rng.uniform(0.5, 2.0, groups) * 2.0 ** rng.integers(-20, 20, groups)).astype(np.float32)
+    sg_blk = np.repeat(sg, rpg * 16)
+    nblk = rows * 16
+    amax = (np.exp(rng.uniform(np.log(0.05), np.log(400.0), nblk)) * sg_blk * 6).astype(np.float32)
+    d = np.empty(nblk, np.float32)
+    for gi in range(groups):
+        sl = slice(gi * rpg * 16, (gi + 1) * rpg * 16)
+        probe = np.zeros((rpg * 16, 16), np.float32)
+        probe[:, 0] = amax[sl]
+        _, s_blk, _ = nvfp4.quantize(probe, s_g=sg[gi])
+        d[sl] = (nvfp4.e4m3_decode(s_blk[:, 0]).astype(np.float32) * sg[gi]).astype(np.float32)
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0], np.float32)
+    qb = pts.view(np.uint32)[rng.integers(0, pts.size, (nblk, 15))].astype(np.int64)
+    q = (qb + rng.integers(-8, 9, (nblk, 15))).astype(np.uint32).view(np.float32)
+    x = (q * d[:, None]).astype(np.float32)
+    step = rng.integers(-1, 2, (nblk, 15))
+    x = np.where(step < 0, np.nextafter(x, np.float32(0)), np.where(step > 0, np.nextafter(x, np.float32(np.inf)), x))
+    x = np.where(np.abs(x) < amax[:, None], x, np.float32(0))
+    blocks = np.concatenate([amax[:, None], x], axis=1)
+    blocks *= np.where(rng.random((nblk, 16)) < 0.5, np.float32(-1), np.float32(1))
+    xr = np.ascontiguousarray(blocks.reshape(rows, 256))
+    assert np.unique(d).size > 2000
+    g = gpu_lib.quantize_nv_grouped(torch.from_numpy(xr).to(DEV), rpg, tensor_scales=torch.from_numpy(sg).to(DEV))
+    gc, gs = to_np(g.codes)[:, :128], to_np(g.scales)
+    for gi in range(groups):
+        r = slice(gi * rpg, (gi + 1) * rpg)
+        oc, os_, _ = nvfp4.quantize(xr[r], s_g=sg[gi])
+        np.testing.assert_array_equal(gs[r], os_)
+        np.testing.assert_array_equal(gc[r], oc)
+
+
+@pytest.mark.parametrize("sg", [1e-35, 1e-3, 1e35])
+def test_nv_given_scale_far_from_data(gpu_lib, sg):
+    """A caller-supplied tensor scale far from the data: E4M3 scales
+    saturate at 448 (quotients far above 6 saturate to code 7) or divisors
+    leave the range where the kernel replaces the division by its reciprocal
+    form; either way the codes are those of the correctly rounded quotient."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-30, 30, (64, 1)))).astype(np.float32)
+    sg = np.float32(sg)
+    g = gpu_lib.quantize(torch.from_numpy(x).to(DEV), "nv", tensor_scale=torch.tensor([sg], device=DEV))
+    oc, os_, _ = nvfp4.quantize(x, s_g=sg)
+    np.testing.assert_array_equal(to_np(g.scales), os_)
+    np.testing.assert_array_equal(to_np(g.codes)[:, :128], oc)
+
+
 def test_element_rounding_sweep_mx(gpu_lib):
     """fp32 values with exponent in [2^-3, 2^3): every 5th mantissa of each
     binade plus every value within 256 ulps of each E2M1 decision point and
