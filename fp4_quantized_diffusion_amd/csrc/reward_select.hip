@@ -21,10 +21,13 @@ constexpr int kRankChunk = 4096;
 // dim % 4 == 0 and dim / 4 <= 1024 (the rollout's 3072 dims are 768 groups),
 // thread t owns column group t for every row -- its weights u stay in
 // registers, there is no index division, and each thread keeps kRows
-// 16-byte loads in flight. Other shapes take the flat loop. u == NULL gives
-// the plain mean. The sum runs in a fixed order (per thread, then a fixed
-// shuffle tree and a fixed LDS order), so it is bitwise repeatable.
-constexpr int kRows = 8;
+// 16-byte loads in flight (256 KiB per workgroup: one workgroup per
+// candidate leaves most CUs idle at 96 candidates, so each must keep many
+// bytes in flight). Other shapes take the flat loop. u == NULL gives the
+// plain mean. The sum runs in a fixed order (per thread over the rows in
+// order, then a fixed shuffle tree and a fixed LDS order), so it is bitwise
+// repeatable and independent of kRows.
+constexpr int kRows = 16;
 
 __device__ __forceinline__ float dot4(float4 a, float4 w) { return a.x * w.x + a.y * w.y + a.z * w.z + a.w * w.w; }
 
