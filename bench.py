@@ -368,6 +368,16 @@ def class_benchmarks(dev, n_sets=4):
                     "us": [round(v, 1) for v in lq_us], "tbps": round(lbytes / lq_us[0] / 1e6, 3),
                     "fp32_tflops": round((2 * r + 2) * n * k / lq_us[0] / 1e6, 2),
                     "vs_plain_requantize": round(lq_us[0] / wq_us[0], 2)}
+                # NVFP4-style: a tensor-amax pass over the merged weight, then the
+                # merge again and the codes (2 + 0.5 + 1/16 B/elem written and read)
+                qn_w = [fq.quantize(draws[i][1], "nv") for i in range(n_sets)]
+                ln_us = time_launches([lambda i=i: fq.quantize_lora(draws[i][1], lb[i], la[i], 2.0, fmt="nv",
+                                                                    out=qn_w[i]) for i in range(n_sets)])
+                nbytes = 2 * (n * k * 2 + (n + k) * r * 4) + n * k * (0.5 + 1 / 16)
+                mem[f"nv_quantize_lora_r{r}_weight_{name}_{n}x{k}"] = {
+                    "us": [round(v, 1) for v in ln_us], "tbps": round(nbytes / ln_us[0] / 1e6, 3),
+                    "fp32_tflops": round(2 * (2 * r + 2) * n * k / ln_us[0] / 1e6, 2), "passes": 2}
+                del qn_w
                 del qn_a, qn_b, lb, la
             gemms[key] = g
             log(f"class {key}: mxfp4 {f_us[0]:.0f} us ({g['mxfp4_tflops']} TF/s), bf16 {b_us[0]:.0f} us "

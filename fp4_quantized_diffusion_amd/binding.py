@@ -32,7 +32,7 @@ _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_
 _SIGS = {
     "fp4_quantize": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
     "fp4_quantize_lora": [_i32, _p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _i32, _i64, _f32, _p, _i64, _p, _i64,
-                          _i32, _p],
+                          _p, _i32, _p],
     "fp4_quantize_nv_grouped": [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i32, _p],
     "fp4_panel_bytes": [_i64, _i64, _p, _p],
     "fp4_gemm": [_i32, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
@@ -88,9 +88,10 @@ def fp4_quantize(fmt, x, x_dtype, rows, k, ldx, codes, ld_codes, scales, ld_scal
 
 
 def fp4_quantize_lora(fmt, w, w_dtype, rows, k, ldw, lora_b, ld_b, lora_a, ld_a, ab_dtype, rank, scale, codes,
-                      ld_codes, scales, ld_scales, flags, stream):
+                      ld_codes, scales, ld_scales, tensor_scale, flags, stream):
     return load_library().fp4_quantize_lora(fmt, w, w_dtype, rows, k, ldw, lora_b, ld_b, lora_a, ld_a, ab_dtype,
-                                            rank, scale, codes, ld_codes, scales, ld_scales, flags, stream)
+                                            rank, scale, codes, ld_codes, scales, ld_scales, tensor_scale, flags,
+                                            stream)
 
 
 def fp4_gemm(fmt, a_codes, lda, a_scales, ld_as, a_ts, b_codes, ldb, b_scales, ld_bs, b_ts, m, n, k, c, c_dtype,
@@ -273,31 +274,38 @@ def quantize(x, fmt="mx", prologue=None, tensor_scale=None, out=None, layout="ro
     return out
 
 
-def quantize_lora(w, lora_b, lora_a, scale, out=None, layout="row"):
-    """MXFP4 QTensor of W + scale * (B A) -- a LoRA adapter merged into the
-    weight in fp32 and re-quantized in one pass (fp4_quantize_lora).
+def quantize_lora(w, lora_b, lora_a, scale, out=None, layout="row", fmt="mx", tensor_scale=None):
+    """QTensor of W + scale * (B A) -- a LoRA adapter merged into the weight in
+    fp32 and re-quantized (fp4_quantize_lora), the merged weight never written.
     w: [rows, k] fp32 or bf16; lora_b: [rows, rank] and lora_a: [rank, k] of
-    one dtype (fp32 or bf16); all 2-D with unit inner stride. layout: "row" or
-    "panel"; out: a QTensor to write into (its layout wins)."""
+    one dtype (fp32 or bf16); all 2-D with unit inner stride. fmt: "mx" or
+    "nv"; layout: "row" or "panel" (MX only); tensor_scale: a 1-element fp32
+    tensor used as s_g (NV only); out: a QTensor to write into (its layout
+    wins)."""
     for t in (w, lora_b, lora_a):
         if not _row_view_ok(t):
             raise ValueError("w, lora_b and lora_a must be 2-D with unit inner stride")
     if lora_b.dtype != lora_a.dtype:
         raise ValueError("lora_b and lora_a must have one dtype")
+    f = {"mx": FMT_MX, "nv": FMT_NV}[fmt]
     rows, k = w.shape
     rank = lora_b.shape[1]
     if lora_b.shape[0] != rows or tuple(lora_a.shape) != (rank, k):
         raise ValueError("shapes do not chain: w [rows, k], lora_b [rows, rank], lora_a [rank, k]")
     if out is None:
-        out = _alloc_panel(rows, k, w.device) if layout == "panel" else _alloc_rows(rows, k, w.device, FMT_MX)
-    if out.rows not in (0, rows) or out.k != k or out.fmt != FMT_MX:
+        out = _alloc_panel(rows, k, w.device) if layout == "panel" else _alloc_rows(rows, k, w.device, f)
+    if out.rows not in (0, rows) or out.k != k or out.fmt != f:
         raise ValueError("out was allocated for another shape or format")
     panel = out.layout == "panel"
-    st = fp4_quantize_lora(FMT_MX, w.data_ptr(), _dtype_code(w), rows, k, w.stride(0), lora_b.data_ptr(),
+    flags = LAYOUT_PANEL if panel else 0
+    ts = out.tensor_scale
+    if f == FMT_NV and tensor_scale is not None:
+        ts.copy_(tensor_scale.reshape(1))
+        flags |= TENSOR_SCALE_GIVEN
+    st = fp4_quantize_lora(f, w.data_ptr(), _dtype_code(w), rows, k, w.stride(0), lora_b.data_ptr(),
                            lora_b.stride(0), lora_a.data_ptr(), lora_a.stride(0), _dtype_code(lora_a), rank,
                            float(scale), out.codes.data_ptr(), 0 if panel else out.codes.stride(0),
-                           out.scales.data_ptr(), 0 if panel else out.scales.stride(0),
-                           LAYOUT_PANEL if panel else 0, _stream())
+                           out.scales.data_ptr(), 0 if panel else out.scales.stride(0), _ptr(ts), flags, _stream())
     _check(st, "fp4_quantize_lora")
     return out
 

@@ -107,7 +107,7 @@ fp4_status check_gemm_panel(int fmt, const uint8_t* a, const uint8_t* as, const 
 fp4_status check_quantize_lora(int fmt, const void* w, int w_dtype, int64_t rows, int64_t k, int64_t ldw,
                                const void* lora_b, int64_t ld_b, const void* lora_a, int64_t ld_a, int ab_dtype,
                                int64_t rank, float scale, const uint8_t* codes, int64_t ld_codes,
-                               const uint8_t* scales, int64_t ld_scales, int flags) {
+                               const uint8_t* scales, int64_t ld_scales, const float* tensor_scale, int flags) {
   if (fmt != FP4_FMT_MX && fmt != FP4_FMT_NV) return FP4_INVALID_ARGUMENT;
   if (!lora_b || !lora_a) return FP4_INVALID_ARGUMENT;
   if (ab_dtype != FP4_DT_F32 && ab_dtype != FP4_DT_BF16) return FP4_INVALID_ARGUMENT;
@@ -116,13 +116,12 @@ fp4_status check_quantize_lora(int fmt, const void* w, int w_dtype, int64_t rows
   const uintptr_t ab_size = ab_dtype == FP4_DT_F32 ? 4 : 2;
   if (!aligned(lora_b, ab_size) || !aligned(lora_a, ab_size)) return FP4_INVALID_ARGUMENT;
   if (!(scale - scale == 0.0f)) return FP4_INVALID_ARGUMENT;  // NaN or infinite
-  if (flags & ~FP4_LAYOUT_PANEL) return FP4_INVALID_ARGUMENT;
-  // the weight and the outputs as for fp4_quantize (no prologue, no tensor scale)
-  const fp4_status s = check_quantize(FP4_FMT_MX, w, w_dtype, rows, k, ldw, codes, ld_codes, scales, ld_scales,
-                                      nullptr, flags);
-  if (s != FP4_OK) return s;
-  if (fmt == FP4_FMT_NV) return FP4_UNSUPPORTED;
-  return FP4_OK;
+  // no prologues: MX takes only the panel layout flag, NV only a given tensor
+  // scale (NV with the panel layout is refused by check_quantize)
+  if (fmt == FP4_FMT_MX && (flags & ~FP4_LAYOUT_PANEL)) return FP4_INVALID_ARGUMENT;
+  if (fmt == FP4_FMT_NV && (flags & ~(FP4_TENSOR_SCALE_GIVEN | FP4_LAYOUT_PANEL))) return FP4_INVALID_ARGUMENT;
+  // the weight, the outputs and the tensor scale as for fp4_quantize
+  return check_quantize(fmt, w, w_dtype, rows, k, ldw, codes, ld_codes, scales, ld_scales, tensor_scale, flags);
 }
 
 }  // namespace
@@ -313,11 +312,16 @@ FP4_API const char* fp4_status_str(fp4_status s) {
 FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_t rows, int64_t k, int64_t ldw,
                                      const void* lora_b, int64_t ld_b, const void* lora_a, int64_t ld_a, int ab_dtype,
                                      int64_t rank, float scale, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
-                                     int64_t ld_scales, int flags, void* stream) {
+                                     int64_t ld_scales, float* tensor_scale, int flags, void* stream) {
   try {
     const fp4_status s = check_quantize_lora(fmt, w, w_dtype, rows, k, ldw, lora_b, ld_b, lora_a, ld_a, ab_dtype, rank,
-                                             scale, codes, ld_codes, scales, ld_scales, flags);
+                                             scale, codes, ld_codes, scales, ld_scales, tensor_scale, flags);
     if (s != FP4_OK) return s;
+    if (fmt == FP4_FMT_NV)
+      return from_hip(fp4r::launch_quant_nv_lora(w, w_dtype == FP4_DT_BF16, rows, k, ldw, lora_b, ld_b, lora_a, ld_a,
+                                                 ab_dtype == FP4_DT_BF16, (int)rank, scale, codes, ld_codes, scales,
+                                                 ld_scales, tensor_scale, (flags & FP4_TENSOR_SCALE_GIVEN) ? 1 : 0,
+                                                 static_cast<hipStream_t>(stream)));
     return from_hip(fp4r::launch_quant_mx_lora(w, w_dtype == FP4_DT_BF16, rows, k, ldw, lora_b, ld_b, lora_a, ld_a,
                                                ab_dtype == FP4_DT_BF16, (int)rank, scale, codes, ld_codes, scales,
                                                ld_scales, (flags & FP4_LAYOUT_PANEL) ? 1 : 0,
@@ -392,6 +396,6 @@ FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const 
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 107; }
+FP4_API int fp4_abi_version(void) { return 108; }
 
 }  // extern "C"

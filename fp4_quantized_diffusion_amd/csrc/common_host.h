@@ -17,6 +17,15 @@ hipError_t launch_quant_mx_lora(const void* w, int w_bf16, int64_t rows, int64_t
                                 int64_t ldb, const void* la, int64_t lda, int ab_bf16, int rank, float scale,
                                 uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, int panel,
                                 hipStream_t st);
+hipError_t launch_quant_nv_lora(const void* w, int w_bf16, int64_t rows, int64_t k, int64_t ldw, const void* lb,
+                                int64_t ldb, const void* la, int64_t lda, int ab_bf16, int rank, float scale,
+                                uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, float* ts,
+                                int scale_given, hipStream_t st);
+// The NVFP4-style tensor-scale word: zero it before an amax pass (integer
+// atomicMax on the float bits), then turn the amax into s_g = fl(amax / 2688),
+// 1 where that is 0.
+hipError_t launch_nv_scale_reset(float* ts, hipStream_t st);
+hipError_t launch_nv_scale_finalize(float* ts, hipStream_t st);
 hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, int64_t ldx,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            float* tensor_scale, int scale_given, hipStream_t st);

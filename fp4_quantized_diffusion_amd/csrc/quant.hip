@@ -410,26 +410,6 @@ __global__ void nv_finalize_kernel(float* ts) {
   *ts = (sg == 0.0f) ? 1.0f : sg;
 }
 
-// E4M3 (bias 7, max 448) code of a non-negative finite fp32 value, round to
-// nearest even, saturating at 448 (code 0x7E).
-__device__ __forceinline__ uint32_t e4m3_rne(float s) {
-  const uint32_t b = __float_as_uint(s);
-  const int e = (int)(b >> 23) - 127;
-  if (e < -6) {
-    // below the smallest normal 2^-6: steps of 2^-9; s * 512 is exact
-    return (uint32_t)rintf(s * 512.0f);  // 0..8 (8 is the smallest normal, code 0x08)
-  }
-  // round the 23-bit mantissa to 3 bits (nearest even), carry into the exponent
-  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
-  const uint32_t code = r - (120u << 3);  // exponent bias 127 -> 7
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t S) {
-  const uint32_t e = S >> 3, m = S & 7u;
-  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
-}
-
 // Per-group tensor amax (GROUPED quantization: one tensor scale per group of
 // rpg rows, e.g. per candidate): workgroup (g, s) takes slice s of group g's
 // rows, one integer atomicMax at its end, as nv_amax_kernel.
@@ -501,51 +481,8 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
     const int64_t row = rows[u], oct = octs[u];
     const float sg = GROUPED ? ts[udiv(row, rpg)] : sg0;  // row is uniform over the workgroup
     const float tau = GROUPED ? 6.0f * sg : tau0;
-    float* v = vv[u];
-    uint32_t am = amax_bits8(v);
-    am = max(am, (uint32_t)__shfl_xor((int)am, 1));  // the 2 octets of a 16-block
-    const float sf = __uint_as_float(am) / tau;
-    const uint32_t S = e4m3_rne(sf);
-    const float d = e4m3_value(S) * sg;
-    uint32_t w = 0;
-    if (d == 0.0f) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w |= ((__float_as_uint(v[j]) >> 28) & 8u) << (4 * j);
-    } else {
-      // fl(x / d), correctly rounded, then its E2M1 code through the same
-      // scaled convert as the MX path, with scale 1. For d in [2^-100, 2^100]
-      // and |x| / d <= 2^64 (every block whose tensor scale comes from the
-      // data: there |x| / d is at most about 6.4) the quotient takes no
-      // division per element: y = fl(1 / d) once per block, q = fl(x y), then
-      // twice q <- fl(q + fl(x - d q) y) with fmas. The first correction
-      // leaves q within one ulp of x / d (faithful); with y correctly rounded
-      // and q faithful, x - d q is exact and the second correction gives the
-      // correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990;
-      // Muller et al., Handbook of Floating-Point Arithmetic, "Newton-Raphson
-      // based division with an FMA"). The range keeps every intermediate
-      // normal and finite where a code can be non-zero: |x / d| < 2^-3 codes
-      // to a signed zero whatever its last bits. The quotient takes the sign
-      // of x (d > 0) explicitly: for x = -0 the corrections would add +0 to
-      // -0 and return +0. Other blocks (a caller-supplied tensor scale far
-      // from the data, NaN or infinite input) divide.
-      float q[8];
-      const float y = 1.0f / d;
-      if (d >= 0x1p-100f && d <= 0x1p100f && __uint_as_float(am) * y <= 0x1p64f) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float t = v[j] * y;
-          t = fmaf(fmaf(-d, t, v[j]), y, t);
-          q[j] = __builtin_copysignf(fmaf(fmaf(-d, t, v[j]), y, t), v[j]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) q[j] = v[j] / d;
-      }
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
-    }
+    uint32_t S;
+    const uint32_t w = nv_block(vv[u], sg, tau, S);
     st_out<true>(reinterpret_cast<uint32_t*>(codes + row * ld_codes + oct * 4), w);
     if ((oct & 1) == 0) st_out<true>(scales + row * ld_scales + (oct >> 1), (uint8_t)S);
     }
@@ -635,6 +572,16 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
     else FP4R_LAUNCH(0, PRO_NONE, false);
   }
 #undef FP4R_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_scale_reset(float* ts, hipStream_t st) {
+  nv_zero_kernel<<<1, 1, 0, st>>>(ts);
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_scale_finalize(float* ts, hipStream_t st) {
+  nv_finalize_kernel<<<1, 1, 0, st>>>(ts);
   return hipGetLastError();
 }
 

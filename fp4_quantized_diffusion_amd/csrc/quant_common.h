@@ -1,5 +1,7 @@
 // Device helpers shared by the elementwise quantizers (quant.hip) and the
-// LoRA-merge quantizer (lora.hip): the octet load and the 4-lane MX block.
+// LoRA-merge quantizer (lora.hip): the octet load, the 4-lane MX block and
+// the 2-lane NVFP4-style block. Both users must produce the same bits for
+// the same input, so these are the only copies.
 #pragma once
 #include "mx_common.h"
 
@@ -33,6 +35,84 @@ __device__ __forceinline__ uint32_t mx_block(const float v[8], uint32_t& S) {
   am = max(am, (uint32_t)__shfl_xor((int)am, 2));
   S = mx_scale(am);
   return mx_pack8(v, S);
+}
+
+
+// E4M3 (bias 7, max 448) code of a non-negative finite fp32 value, round to
+// nearest even, saturating at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float s) {
+#pragma clang fp contract(off)
+  const uint32_t b = __float_as_uint(s);
+  const int e = (int)(b >> 23) - 127;
+  if (e < -6) {
+    // below the smallest normal 2^-6: steps of 2^-9; s * 512 is exact
+    return (uint32_t)rintf(s * 512.0f);  // 0..8 (8 is the smallest normal, code 0x08)
+  }
+  // round the 23-bit mantissa to 3 bits (nearest even), carry into the exponent
+  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+  const uint32_t code = r - (120u << 3);  // exponent bias 127 -> 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t S) {
+#pragma clang fp contract(off)
+  const uint32_t e = S >> 3, m = S & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// NVFP4-style block rule for one octet of a 16-block (the block's other
+// octet in the adjacent lane, lane ^ 1; both lanes must call this together):
+// block amax, s_f = fl(amax / tau) with tau = fl(6 sg), S = E4M3 code of s_f
+// (nearest even, saturating at 448), d = fl(dec(S) sg), and the packed E2M1
+// codes of fl(x / d) -- signed zeros for a block whose d is 0. sg is the
+// tensor scale (positive).
+//
+// fl(x / d) is correctly rounded. For d in [2^-100, 2^100] and amax / d <=
+// 2^64 (every block whose tensor scale comes from the data: there amax / d
+// is at most about 6.4) it takes no division per element: y = fl(1 / d) once
+// per block, q = fl(x y), then twice q <- fl(q + fl(x - d q) y) with fmas.
+// The first correction leaves q within one ulp of x / d (faithful); with y
+// correctly rounded and q faithful, x - d q is exact and the second
+// correction gives the correctly rounded quotient (Markstein, IBM J. Res.
+// Dev. 34(1), 1990; Muller et al., Handbook of Floating-Point Arithmetic,
+// "Newton-Raphson based division with an FMA"). The range keeps every
+// intermediate normal and finite where a code can be non-zero: |x / d| <
+// 2^-3 codes to a signed zero whatever its last bits. The quotient takes the
+// sign of x (d > 0) explicitly: for x = -0 the corrections would add +0 to
+// -0 and return +0. Other blocks (a caller-supplied tensor scale far from
+// the data, NaN or infinite input) divide. The codes come from the same
+// scaled convert as the MX path, with scale 1.
+__device__ __forceinline__ uint32_t nv_block(const float v[8], float sg, float tau, uint32_t& S) {
+#pragma clang fp contract(off)
+  uint32_t am = amax_bits8(v);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1));  // the 2 octets of a 16-block
+  const float sf = __uint_as_float(am) / tau;
+  S = e4m3_rne(sf);
+  const float d = e4m3_value(S) * sg;
+  uint32_t w = 0;
+  if (d == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= ((__float_as_uint(v[j]) >> 28) & 8u) << (4 * j);
+    return w;
+  }
+  float q[8];
+  const float y = 1.0f / d;
+  if (d >= 0x1p-100f && d <= 0x1p100f && __uint_as_float(am) * y <= 0x1p64f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float t = v[j] * y;
+      t = fmaf(fmaf(-d, t, v[j]), y, t);
+      q[j] = __builtin_copysignf(fmaf(fmaf(-d, t, v[j]), y, t), v[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = v[j] / d;
+  }
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+  return w;
 }
 
 }  // namespace fp4r

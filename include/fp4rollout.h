@@ -122,7 +122,7 @@ FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t row
 
 /*
  * fp4_quantize_lora -- merge a LoRA adapter into a weight and re-quantize the
- * result to MXFP4, in one pass: the merged weight is never written.
+ * result (MXFP4 or NVFP4-style); the merged weight is never written.
  *
  * The policy is trained with LoRA adapters (rank 32 on the aitrends summary)
  * and after each update the adapted weights are re-quantized at run time for
@@ -131,9 +131,12 @@ FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t row
  * standard LoRA form W' = W + scale * (B A), evaluated in fp32 as
  *     acc = sum over j = 0 .. rank-1, in order, of fmaf(B[n, j], A[j, k], acc)
  *     W'[n, k] = fmaf(scale, acc, W[n, k])
- * and W' is then quantized exactly as fp4_quantize(FP4_FMT_MX, W', ...) would.
+ * and W' is then quantized exactly as fp4_quantize(fmt, W', ...) would.
+ * NV without FP4_TENSOR_SCALE_GIVEN takes two passes over W (and the
+ * adapter): the first finds max |W'| for the tensor scale, the second
+ * recomputes W' bit for bit and quantizes it.
  *
- *   fmt          FP4_FMT_MX (FP4_FMT_NV: FP4_UNSUPPORTED).
+ *   fmt          FP4_FMT_MX or FP4_FMT_NV.
  *   w            [rows, ldw] weight (nn.Linear layout: rows = output features,
  *                k = input features) of type w_dtype, with the alignment and
  *                size rules of fp4_quantize's x.
@@ -144,15 +147,21 @@ FP4_API fp4_status fp4_quantize(int fmt, const void* x, int x_dtype, int64_t row
  *   rank         1 .. 64.
  *   scale        the adapter's scale (alpha / rank in the usual
  *                parametrisation); finite.
- *   codes, ld_codes, scales, ld_scales
- *                as for fp4_quantize with FP4_FMT_MX (row-major, or the panel
- *                layout with FP4_LAYOUT_PANEL and ld_codes = ld_scales = 0).
- *   flags        0 or FP4_LAYOUT_PANEL.
+ *   codes, ld_codes, scales, ld_scales, tensor_scale
+ *                as for fp4_quantize with the same fmt (MX: row-major, or the
+ *                panel layout with FP4_LAYOUT_PANEL and ld_codes = ld_scales =
+ *                0, tensor_scale NULL; NV: row-major, tensor_scale receives
+ *                s_g = fl(max|W'| / 2688), or supplies it with
+ *                FP4_TENSOR_SCALE_GIVEN).
+ *   flags        MX: 0 or FP4_LAYOUT_PANEL. NV: 0 or FP4_TENSOR_SCALE_GIVEN
+ *                (FP4_LAYOUT_PANEL: FP4_UNSUPPORTED).
+ *   Errors as for fp4_quantize; rank outside 1 .. 64, a non-finite scale or
+ *   misaligned adapters: FP4_INVALID_ARGUMENT.
  */
 FP4_API fp4_status fp4_quantize_lora(int fmt, const void* w, int w_dtype, int64_t rows, int64_t k, int64_t ldw,
                         const void* lora_b, int64_t ld_b, const void* lora_a, int64_t ld_a, int ab_dtype,
                         int64_t rank, float scale, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
-                        int64_t ld_scales, int flags, void* stream);
+                        int64_t ld_scales, float* tensor_scale, int flags, void* stream);
 
 /*
  * fp4_quantize_nv_grouped -- fp4_quantize(FP4_FMT_NV, ...) with one tensor

@@ -1,7 +1,7 @@
 """Comparison helpers for the GPU parity tests (no GPU needed to import)."""
 import numpy as np
 
-from oracle import e2m1, mxfp4
+from oracle import e2m1, mxfp4, nvfp4
 
 
 def to_np(t):
@@ -63,6 +63,54 @@ def mx_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, rel=2e-6, band=None)
         adjacent = np.abs((gn & 7).astype(int) - (on & 7).astype(int)) == 1
         okay_mag = (slack < 0) & adjacent & ((gn & 8) == (on & 8))
         # the sign (decision point 0) may differ only for a value within the band of zero
+        okay_sign = (band > 0) & (np.abs(x_ref) <= band) & ((gn & 7) == 0) & ((on & 7) == 0)
+        okay = dc & (okay_mag | okay_sign)
+        bad += int((dc & ~okay).sum())
+        flips += int(okay.sum())
+    return bad, flips
+
+
+def nv_codes_near_boundary_ok(x_ref, gpu_codes, gpu_scales, sg, rel=2e-6, band=None):
+    """The NVFP4-style counterpart of mx_codes_near_boundary_ok, for tensor
+    scale sg: every E4M3 scale and code must equal the oracle's for the
+    float64 reference input x_ref, except where x_ref sits within `rel`
+    (relative) plus `band` (absolute, per element) of a decision point -- an
+    E4M3 rounding midpoint for the block amax over fl(6 sg), or an E2M1
+    threshold for x over the block's divisor; there either neighbour is a
+    valid result. Returns (n_mismatch_outside_tolerance, n_boundary_flips)."""
+    x_ref = np.asarray(x_ref, dtype=np.float64)
+    rows, k = x_ref.shape
+    sg = np.float32(sg)
+    oc, os_, _ = nvfp4.quantize(x_ref.astype(np.float32), s_g=sg)
+    gn = e2m1.unpack(gpu_codes[:, : k // 2])
+    on = e2m1.unpack(oc)
+    gs = np.asarray(gpu_scales[:, : k // 16]).astype(np.int64)
+    osc = os_.astype(np.int64)
+    band = np.zeros_like(x_ref) if band is None else np.broadcast_to(np.asarray(band, dtype=np.float64), x_ref.shape)
+    amax = np.abs(x_ref.reshape(rows, k // 16, 16)).max(-1)
+    bmax = band.reshape(rows, k // 16, 16).max(-1)
+    tau = float(np.float32(np.float32(6.0) * sg))
+    vals = nvfp4.e4m3_values()
+    bad = flips = 0
+    ds = gs != osc
+    if ds.any():
+        lo = np.clip(np.minimum(gs, osc), 0, 125)
+        mid = (vals[lo] + vals[lo + 1]) / 2
+        near = np.abs(amax / tau - mid) * tau <= bmax + rel * amax
+        okay = ds & (np.abs(gs - osc) == 1) & near
+        bad += int((ds & ~okay).sum())
+        flips += int(okay.sum())
+    same = np.repeat(gs == osc, 16, axis=1)
+    dc = (gn != on) & same
+    if dc.any():
+        d = np.repeat((vals[osc].astype(np.float32) * sg).astype(np.float32).astype(np.float64), 16, axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            y = np.where(d > 0, np.abs(x_ref) / d, 0.0)
+            yb = np.where(d > 0, band / d, 0.0)
+        thr = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        slack = np.min(np.abs(y[..., None] - thr) - rel * thr - yb[..., None], axis=-1)
+        adjacent = np.abs((gn & 7).astype(int) - (on & 7).astype(int)) == 1
+        okay_mag = (slack < 0) & adjacent & ((gn & 8) == (on & 8))
         okay_sign = (band > 0) & (np.abs(x_ref) <= band) & ((gn & 7) == 0) & ((on & 7) == 0)
         okay = dc & (okay_mag | okay_sign)
         bad += int((dc & ~okay).sum())

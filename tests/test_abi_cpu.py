@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 107
+    assert fq.fp4_abi_version() == 108
 
 
 def test_status_strings(lib):
@@ -195,7 +195,7 @@ def test_gemm_panel_gelu_unsupported(lib, kw):
 
 def ql(**kw):
     a = dict(fmt=0, w=P, w_dtype=0, rows=4, k=64, ldw=64, b=P2, ld_b=8, a=P3, ld_a=64, ab_dtype=0, rank=8, scale=0.25,
-             codes=P2, ld_codes=32, scales=P3, ld_scales=2, flags=0, stream=None)
+             codes=P2, ld_codes=32, scales=P3, ld_scales=2, ts=None, flags=0, stream=None)
     a.update(kw)
     return fq.fp4_quantize_lora(*a.values())
 
@@ -205,14 +205,26 @@ def ql(**kw):
     dict(ab_dtype=3), dict(rank=0), dict(rank=65), dict(ld_b=7), dict(ld_a=32), dict(rows=0), dict(k=48),
     dict(ldw=32), dict(w=P + 4), dict(b=P2 + 2), dict(ab_dtype=1, a=P3 + 1), dict(scale=float("nan")),
     dict(scale=float("inf")), dict(flags=0x1), dict(flags=0x2), dict(flags=0x100), dict(ld_codes=16),
-    dict(flags=0x200), dict(rows=1 << 31),
+    dict(flags=0x200), dict(rows=1 << 31), dict(ts=P),
 ])
 def test_quantize_lora_rejects(lib, kw):
     assert ql(**kw) == fq.binding.INVALID_ARGUMENT
 
 
-def test_quantize_lora_nv_unsupported(lib):
-    assert ql(fmt=1) == fq.binding.UNSUPPORTED
+@pytest.mark.parametrize("kw", [
+    dict(ts=None), dict(ts=P + 2), dict(flags=0x1), dict(flags=0x2), dict(k=40, ldw=40, ld_a=40),
+    dict(ld_scales=3), dict(ld_codes=30),
+])
+def test_quantize_lora_nv_rejects(lib, kw):
+    """NVFP4-style: a tensor-scale word is required (4-byte aligned), blocks of
+    16 along k, no prologue, scale rows of at least k / 16 bytes."""
+    a = dict(fmt=1, ld_scales=4, ts=P)
+    a.update(kw)
+    assert ql(**a) == fq.binding.INVALID_ARGUMENT
+
+
+def test_quantize_lora_nv_panel_unsupported(lib):
+    assert ql(fmt=1, ts=P, ld_codes=0, ld_scales=0, flags=0x200) == fq.binding.UNSUPPORTED
 
 
 def test_rollout_lora_entries_per_block():
