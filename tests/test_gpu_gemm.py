@@ -196,6 +196,38 @@ def test_full_size_sampled(gpu_lib, cls, which):
     assert ok, worst
 
 
+@pytest.mark.parametrize("cls,which", [("flux", 1), ("flux", 2), ("sd35", 1)])
+def test_full_size_sampled_nv(gpu_lib, cls, which):
+    """The NVFP4-style pair at full workload size (bf16 activations and
+    weights, bf16 output): the tensor scales equal the oracle's over the whole
+    operands, the codes and E4M3 scales of sampled rows are bit-exact, and
+    sampled outputs are within the GEMM tolerance of the exact dequantized
+    product."""
+    from oracle import nvfp4
+    a, w = inputs.class_linear(cls, which)
+    qa, qb = quantize_both(gpu_lib, a, w, "nv", torch.bfloat16)
+    c = gpu_lib.gemm(qa, qb, "bf16")
+    torch.cuda.synchronize()
+    sg_a, sg_b = nvfp4.tensor_scale(a), nvfp4.tensor_scale(w)
+    assert to_np(qa.tensor_scale)[0] == sg_a and to_np(qb.tensor_scale)[0] == sg_b
+    rng = np.random.default_rng(35)
+    rows = np.sort(rng.choice(a.shape[0], 48, replace=False))
+    rows[-1] = a.shape[0] - 1
+    cols = np.sort(rng.choice(w.shape[0], 64, replace=False))
+    cols[-1] = w.shape[0] - 1
+    k = a.shape[1]
+    oc, os_, _ = nvfp4.quantize(a[rows], s_g=sg_a)
+    np.testing.assert_array_equal(to_np(qa.codes[rows])[:, : k // 2], oc)
+    np.testing.assert_array_equal(to_np(qa.scales[rows])[:, : k // 16], os_)
+    oc, os_, _ = nvfp4.quantize(w[cols], s_g=sg_b)
+    np.testing.assert_array_equal(to_np(qb.codes[cols])[:, : k // 2], oc)
+    np.testing.assert_array_equal(to_np(qb.scales[cols])[:, : k // 16], os_)
+    c_exact, s_abs = oracle_c(qa, qb, "nv", rows, cols)
+    c_s = to_np(c.float())[np.ix_(rows, cols)]
+    ok, worst = gemm_within_tol(c_s, c_exact, s_abs, bf16_out=True)
+    assert ok, worst
+
+
 def nv_operand(codes, scales, ts, k, code_garbage=None, scale_ld=None, scale_fill=0x7F):
     """An NVFP4-style QTensor from host codes [rows, k/2] and E4M3 scale
     bytes [rows, k/16]. Code rows are padded to a multiple of 16 bytes with
@@ -275,19 +307,3 @@ def test_nv_unaligned_scale_rows(gpu_lib, k):
     assert ok, worst
 
 
-def test_nv_full_size_flux_sampled(gpu_lib):
-    """FLUX-class 36864 x 3072 -> 12288 with NVFP4-style operands quantized on
-    the GPU, bf16 output, in the benchmark's launch configuration: sampled
-    outputs within tolerance of the oracle product of the same codes."""
-    a, w = inputs.class_linear("flux", 1)
-    qa, qb = quantize_both(gpu_lib, a, w, "nv", torch.bfloat16)
-    c = gpu_lib.gemm(qa, qb, "bf16")
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(36)
-    rows = np.sort(rng.choice(a.shape[0], 48, replace=False))
-    rows[-1] = a.shape[0] - 1
-    cols = np.sort(rng.choice(w.shape[0], 64, replace=False))
-    cols[-1] = w.shape[0] - 1
-    c_exact, s_abs = oracle_c(qa, qb, "nv", rows, cols)
-    ok, worst = gemm_within_tol(to_np(c.float())[np.ix_(rows, cols)], c_exact, s_abs, bf16_out=True)
-    assert ok, worst
