@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void amax_nv_lora_kernel(
   if (threadIdx.x == 0) {
     uint32_t t = 0;
     for (int wv = 0; wv < kThreads / 64; ++wv) t = max(t, sh[wv]);
-    atomicMax(reinterpret_cast<unsigned int*>(ts), t);
+    amax_raise(ts, t);
   }
 }
 

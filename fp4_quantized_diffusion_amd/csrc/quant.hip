@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restric
   if (threadIdx.x == 0) {
     uint32_t t = 0;
     for (int w = 0; w < kThreads / 64; ++w) t = max(t, sh[w]);
-    atomicMax(reinterpret_cast<unsigned int*>(ts), t);
+    amax_raise(ts, t);
   }
 }
 
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_group_kernel(const void* __r
   if (threadIdx.x == 0) {
     uint32_t t = 0;
     for (int w = 0; w < kThreads / 64; ++w) t = max(t, sh[w]);
-    atomicMax(reinterpret_cast<unsigned int*>(ts + g), t);
+    amax_raise(ts + g, t);
   }
 }
 

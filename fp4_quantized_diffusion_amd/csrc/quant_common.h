@@ -60,6 +60,18 @@ __device__ __forceinline__ float e4m3_value(uint32_t S) {
   return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
 }
 
+// Raise an NVFP4-style amax word (the float bits of a non-negative value,
+// ordered like integers) to at least t with an integer atomicMax. Most
+// workgroups finish below the running maximum, so the word is read first and
+// the atomic skipped then; the word only grows, so a stale read can only
+// cost an atomic that was not needed. Without the check the same-address
+// atomics of a few thousand workgroups serialize (2048 workgroups over a
+// 36864 x 3072 bf16 activation: 129 -> 123 us for the whole quantization).
+__device__ __forceinline__ void amax_raise(float* word, uint32_t t) {
+  unsigned int* w = reinterpret_cast<unsigned int*>(word);
+  if (t > __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(w, t);
+}
+
 // NVFP4-style block rule for one octet of a 16-block (the block's other
 // octet in the adjacent lane, lane ^ 1; both lanes must call this together):
 // block amax, s_f = fl(amax / tau) with tau = fl(6 sg), S = E4M3 code of s_f
