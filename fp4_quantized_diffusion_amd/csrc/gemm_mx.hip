@@ -1010,16 +1010,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
 }
 
 
+// CUs of the device current at the first call (thread-safe static
+// initialization; the library runs on one kind of GPU): the persistent grid.
 int cu_count() {
-  static int n = 0;
-  if (n == 0) {
+  static const int n = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
                                                  hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
+      return v;
+    return 256;
+  }();
   return n;
 }
 

@@ -511,17 +511,18 @@ template <class Kernel>
 unsigned elementwise_grid(Kernel kernel, int64_t steps, bool table) {
   unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
   if (!table) return g;
-  static int resident = 0;  // per kernel instantiation
-  if (resident == 0) {
+  // per kernel instantiation, queried once (thread-safe static
+  // initialization) on the device current at the first call; the library
+  // runs on one kind of GPU
+  static const int resident = [kernel] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
-      resident = 1024;
-    else
-      resident = cus * per_cu;
-  }
+      return 1024;
+    return cus * per_cu;
+  }();
   return g < (unsigned)resident ? g : (unsigned)resident;
 }
 
