@@ -64,6 +64,9 @@ struct GeluLds<1, PRO_GELU> {
 // are all issued before the first is used, so each wave keeps four 16-byte
 // loads per lane in flight.
 constexpr int kUnroll = 4;
+// The NVFP4-style passes keep two steps in flight: with four they took 2-3%
+// longer (the code pass carries more registers per step), with eight 5-8%.
+constexpr int kUnrollNv = 2;
 
 // n / d for a workgroup-uniform step index n and a divisor fixed per launch,
 // without a 64-bit division in the loop: one high multiply, an add and two
@@ -376,18 +379,18 @@ __global__ void nv_zero_kernel(float* ts) { *reinterpret_cast<uint32_t*>(ts) = 0
 // Tensor amax: |x| bit patterns order like the values, so an integer max is
 // exact and order-independent (deterministic). Work comes in the row-major
 // kernels' steps (256 consecutive octets of one row, workgroup-uniform row
-// and segment), kUnroll steps per pass with all loads issued first.
+// and segment), kUnrollNv steps per pass with all loads issued first.
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restrict__ x, int64_t ldx, int64_t opr,
                                                            UDiv segs, int64_t steps, float* ts) {
   __shared__ uint32_t sh[kThreads / 64];
   const int64_t G = gridDim.x;
   uint32_t m = 0;
-  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
-    float v[kUnroll][8];
-    bool ok[kUnroll];
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnrollNv * G) {
+    float v[kUnrollNv][8];
+    bool ok[kUnrollNv];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollNv; ++u) {
       const int64_t st = st0 + u * G;
       const int64_t row = udiv(st, segs);
       const int64_t oct = (st - row * segs.d) * kThreads + threadIdx.x;
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const void* __restric
       load8<BF16>(x, ok[u] ? row * ldx + oct * 8 : 0, v[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kUnrollNv; ++u)
       if (ok[u]) m = max(m, amax_bits8(v[u]));
   }
 #pragma unroll
@@ -460,7 +463,7 @@ __global__ void nv_finalize_groups_kernel(float* ts, int64_t n) {
 }
 
 // Codes and E4M3 block scales, in the row-major kernels' steps (a 16-block is
-// two adjacent lanes of one step), kUnroll steps per pass. GROUPED: the
+// two adjacent lanes of one step), kUnrollNv steps per pass. GROUPED: the
 // tensor scale of row r is ts[r / rpg].
 template <int BF16, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
@@ -470,11 +473,11 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
   const float sg0 = GROUPED ? 0.0f : *ts;
   const float tau0 = 6.0f * sg0;
   const int64_t G = gridDim.x;
-  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
-    float vv[kUnroll][8];
-    int64_t rows[kUnroll], octs[kUnroll];
+  for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnrollNv * G) {
+    float vv[kUnrollNv][8];
+    int64_t rows[kUnrollNv], octs[kUnrollNv];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollNv; ++u) {
       const int64_t st = st0 + u * G;
       rows[u] = udiv(st, segs);
       octs[u] = (st - rows[u] * segs.d) * kThreads + threadIdx.x;
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void quant_nv_kernel(
       load8<BF16>(x, ok ? rows[u] * ldx + octs[u] * 8 : 0, vv[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollNv; ++u) {
     // whole 16-blocks drop out: opr is even
     if (st0 + u * G >= steps || octs[u] >= opr) continue;
     const int64_t row = rows[u], oct = octs[u];
@@ -597,7 +600,7 @@ hipError_t launch_quant_nv(const void* x, int x_bf16, int64_t rows, int64_t k, i
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            float* tensor_scale, int scale_given, hipStream_t st) {
   const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
-  const unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
+  const unsigned g = grid_for((steps + kUnrollNv - 1) / kUnrollNv * kThreads);
   if (!scale_given) {
     nv_zero_kernel<<<1, 1, 0, st>>>(tensor_scale);
     // a resident-sized grid: each workgroup issues one atomic at its end
@@ -622,7 +625,7 @@ hipError_t launch_quant_nv_grouped(const void* x, int x_bf16, int64_t rows, int6
                                    float* tensor_scales, int scale_given, hipStream_t st) {
   const int64_t opr = k >> 3, segs = (opr + kThreads - 1) / kThreads, steps = rows * segs;
   const int64_t groups = rows / rpg;
-  const unsigned g = grid_for((steps + kUnroll - 1) / kUnroll * kThreads);
+  const unsigned g = grid_for((steps + kUnrollNv - 1) / kUnrollNv * kThreads);
   if (!scale_given) {
     const unsigned gz = (unsigned)((groups + 255) / 256);
     nv_zero_groups_kernel<<<gz, 256, 0, st>>>(tensor_scales, groups);
