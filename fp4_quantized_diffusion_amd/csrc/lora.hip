@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileRows = 32;
+constexpr int kRowsPerThread = kTileRows / (kThreads / 32);  // rows rg + 8 i of a thread
 constexpr int kTileCols = 256;
 
 template <int BF16>
@@ -45,8 +46,8 @@ __device__ __forceinline__ float load1(const void* p, int64_t i) {
 template <int WBF16, int ABBF16>
 __device__ __forceinline__ void lora_merge(const void* __restrict__ w, int64_t rows, int64_t k, int64_t ldw,
                                            const void* __restrict__ lb, int64_t ldb, const void* __restrict__ la,
-                                           int64_t lda, int rank, float scale, float* lds, float out[4][8],
-                                           bool valid[4]) {
+                                           int64_t lda, int rank, float scale, float* lds, float out[kRowsPerThread][8],
+                                           bool valid[kRowsPerThread]) {
   float* sa = lds;                        // [rank][kTileCols]
   float* sb = lds + rank * kTileCols;     // [kTileRows][rank]
   const int64_t r0 = (int64_t)blockIdx.y * kTileRows;
@@ -55,9 +56,9 @@ __device__ __forceinline__ void lora_merge(const void* __restrict__ w, int64_t r
   const int64_t og = (c0 >> 3) + o;            // global octet index along K
   const bool col_ok = og * 8 < k;              // shared by a block's octets (k % 16 == 0)
 
-  float wv[4][8];
+  float wv[kRowsPerThread][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kRowsPerThread; ++i) {
     const int64_t row = r0 + rg + 8 * i;
     valid[i] = row < rows && col_ok;
     if (valid[i]) {
@@ -77,9 +78,9 @@ __device__ __forceinline__ void lora_merge(const void* __restrict__ w, int64_t r
   }
   __syncthreads();
 
-  float acc[4][8];
+  float acc[kRowsPerThread][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kRowsPerThread; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   for (int j = 0; j < rank; ++j) {
@@ -87,14 +88,14 @@ __device__ __forceinline__ void lora_merge(const void* __restrict__ w, int64_t r
     const float4 a1 = *reinterpret_cast<const float4*>(sa + j * kTileCols + 8 * o + 4);
     const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kRowsPerThread; ++i) {
       const float bv = sb[(rg + 8 * i) * rank + j];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(bv, av[e], acc[i][e]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kRowsPerThread; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[i][e] = valid[i] ? fmaf(scale, acc[i][e], wv[i][e]) : 0.f;
 }
@@ -108,14 +109,14 @@ __global__ __launch_bounds__(kThreads) void quant_mx_lora_kernel(
     const void* __restrict__ la, int64_t lda, int rank, float scale, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, int64_t nrows, int64_t nc) {
   extern __shared__ float lds[];
-  float v[4][8];
-  bool valid[4];
+  float v[kRowsPerThread][8];
+  bool valid[kRowsPerThread];
   lora_merge<WBF16, ABBF16>(w, rows, k, ldw, lb, ldb, la, lda, rank, scale, lds, v, valid);
   const int64_t r0 = (int64_t)blockIdx.y * kTileRows;
   const int o = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int64_t og = ((int64_t)blockIdx.x * kTileCols >> 3) + o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kRowsPerThread; ++i) {
     const int64_t row = r0 + rg + 8 * i;  // the same for a 32-block's 4 lanes
     if (row >= nrows) continue;
     uint32_t S;
@@ -142,12 +143,12 @@ __global__ __launch_bounds__(kThreads) void amax_nv_lora_kernel(
     const void* __restrict__ la, int64_t lda, int rank, float scale, float* ts) {
   extern __shared__ float lds[];
   __shared__ uint32_t sh[kThreads / 64];
-  float v[4][8];
-  bool valid[4];
+  float v[kRowsPerThread][8];
+  bool valid[kRowsPerThread];
   lora_merge<WBF16, ABBF16>(w, rows, k, ldw, lb, ldb, la, lda, rank, scale, lds, v, valid);
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, amax_bits8(v[i]));  // outside elements are 0
+  for (int i = 0; i < kRowsPerThread; ++i) m = max(m, amax_bits8(v[i]));  // outside elements are 0
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
@@ -167,15 +168,15 @@ __global__ __launch_bounds__(kThreads) void quant_nv_lora_kernel(
     const void* __restrict__ la, int64_t lda, int rank, float scale, const float* __restrict__ ts,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
   extern __shared__ float lds[];
-  float v[4][8];
-  bool valid[4];
+  float v[kRowsPerThread][8];
+  bool valid[kRowsPerThread];
   lora_merge<WBF16, ABBF16>(w, rows, k, ldw, lb, ldb, la, lda, rank, scale, lds, v, valid);
   const float sg = *ts, tau = 6.0f * sg;
   const int64_t r0 = (int64_t)blockIdx.y * kTileRows;
   const int o = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int64_t og = ((int64_t)blockIdx.x * kTileCols >> 3) + o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kRowsPerThread; ++i) {
     if (!valid[i]) continue;  // the same for a 16-block's 2 lanes
     const int64_t row = r0 + rg + 8 * i;
     uint32_t S;
