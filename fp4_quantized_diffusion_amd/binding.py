@@ -342,10 +342,20 @@ def gemm(a, b, out_dtype="bf16", residual=None, out=None):
     if a.fmt != b.fmt or a.k != b.k or a.layout != b.layout:
         raise ValueError("operands differ in format, layout or k")
     m, n, k = a.n_rows, b.n_rows, a.k
+    if out_dtype not in ("bf16", "f32"):
+        raise ValueError(f"out_dtype must be 'bf16' or 'f32', not {out_dtype!r}")
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     if out is None:
         ldc = ((n + 3) // 4) * 4
         out = torch.empty((m, ldc), dtype=dt, device=a.codes.device)[:, :n]
+    if out.dim() != 2 or tuple(out.shape) != (m, n) or out.stride(1) != 1 or out.dtype != dt:
+        raise ValueError(f"out must be a [{m}, {n}] {dt} matrix with unit inner stride")
+    if residual is not None:
+        if out_dtype != "f32":
+            raise ValueError("a residual needs fp32 output")
+        if (residual.dim() != 2 or tuple(residual.shape) != (m, n) or residual.dtype != torch.float32
+                or residual.stride(1) != 1 or residual.stride(0) != out.stride(0)):
+            raise ValueError(f"residual must be a [{m}, {n}] fp32 matrix with out's row stride ({out.stride(0)})")
     if a.layout == "panel":
         st = fp4_gemm_panel(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
                             m, n, k, out.data_ptr(), _dtype_code(out), out.stride(0), _ptr(residual), _stream())
@@ -438,6 +448,11 @@ def euler(x, v, t_cur, t_next, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
+    if x.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("x and out must be fp32")
+    for t in (x, v, out):
+        if not t.is_contiguous() or t.numel() != x.numel():
+            raise ValueError("x, v and out must be contiguous with one element count")
     st = euler_step(out.data_ptr(), x.data_ptr(), v.data_ptr(), _dtype_code(v), x.numel(), float(t_cur),
                     float(t_next), _stream())
     _check(st, "euler_step")
@@ -447,8 +462,16 @@ def euler(x, v, t_cur, t_next, out=None):
 def proxy_reward(x, n_cand, rows_per_cand, u=None, out=None):
     """x: [n_cand * rows_per_cand, dim] fp32 (unit inner stride)."""
     torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.float32:
+        raise ValueError("x must be a 2-D fp32 matrix with unit inner stride")
+    if x.shape[0] != n_cand * rows_per_cand:
+        raise ValueError(f"x has {x.shape[0]} rows, not n_cand * rows_per_cand = {n_cand * rows_per_cand}")
+    if u is not None and (u.dtype != torch.float32 or not u.is_contiguous() or u.numel() != x.shape[1]):
+        raise ValueError("u must be a contiguous fp32 vector of one entry per column of x")
     if out is None:
         out = torch.empty(n_cand, dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n_cand:
+        raise ValueError("out must be a contiguous fp32 vector of n_cand entries")
     st = fp4_proxy_reward(x.data_ptr(), n_cand, rows_per_cand, x.shape[1], x.stride(0), _ptr(u), out.data_ptr(),
                           _stream())
     _check(st, "fp4_proxy_reward")

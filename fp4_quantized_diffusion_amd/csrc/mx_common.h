@@ -129,11 +129,15 @@ __device__ __forceinline__ uint32_t mx_pack8_alu(const float v[8], uint32_t S) {
 // Same codes through gfx950's V_CVT_SCALEF32_PK_FP4_F32, which converts
 // x / scale to E2M1 with round-to-nearest-even, saturation at 6 and the sign
 // kept -- checked against the oracle over millions of fp32 inputs and four
-// power-of-two scales, and by the element-rounding sweep test. Byte j of the
-// result takes elements 2j (low nibble) and 2j + 1. S = 0 would need a
-// subnormal scale, so that (rare) block takes the ALU path.
+// power-of-two scales, and by the exhaustive element-rounding sweep test.
+// Byte j of the result takes elements 2j (low nibble) and 2j + 1. Blocks with
+// S <= 2 take the ALU path: S = 0 would need a subnormal scale, and for
+// S = 1, 2 the block can hold fp32 subnormals that must round to non-zero
+// codes (|x| in (2^(S - 129), 2^-126)), which the ALU path's exact
+// power-of-two product handles by construction. Such blocks (amax below
+// 2^-122) do not occur in practice, so the branch costs one compare.
 __device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
-  if (S == 0) return mx_pack8_alu(v, S);
+  if (S <= 2) return mx_pack8_alu(v, S);
   const float sc = __uint_as_float(S << 23);  // 2^(S - 127)
   uint32_t w = 0;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], sc, 0);

@@ -4,6 +4,7 @@
 // the same input, so these are the only copies.
 #pragma once
 #include "mx_common.h"
+#include "nv_div.h"
 
 namespace fp4r {
 
@@ -79,21 +80,12 @@ __device__ __forceinline__ void amax_raise(float* word, uint32_t t) {
 // codes of fl(x / d) -- signed zeros for a block whose d is 0. sg is the
 // tensor scale (positive).
 //
-// fl(x / d) is correctly rounded. For d in [2^-100, 2^100] and amax / d <=
-// 2^64 (every block whose tensor scale comes from the data: there amax / d
-// is at most about 6.4) it takes no division per element: y = fl(1 / d) once
-// per block, q = fl(x y), then twice q <- fl(q + fl(x - d q) y) with fmas.
-// The first correction leaves q within one ulp of x / d (faithful); with y
-// correctly rounded and q faithful, x - d q is exact and the second
-// correction gives the correctly rounded quotient (Markstein, IBM J. Res.
-// Dev. 34(1), 1990; Muller et al., Handbook of Floating-Point Arithmetic,
-// "Newton-Raphson based division with an FMA"). The range keeps every
-// intermediate normal and finite where a code can be non-zero: |x / d| <
-// 2^-3 codes to a signed zero whatever its last bits. The quotient takes the
-// sign of x (d > 0) explicitly: for x = -0 the corrections would add +0 to
-// -0 and return +0. Other blocks (a caller-supplied tensor scale far from
-// the data, NaN or infinite input) divide. The codes come from the same
-// scaled convert as the MX path, with scale 1.
+// fl(x / d) is correctly rounded: nv_div (reciprocal once per block, two fma
+// corrections) wherever nv_div_applies -- every block whose tensor scale
+// comes from the data, where amax / d is at most about 6.4 -- and a plain
+// division for other blocks (a caller-supplied tensor scale far from the
+// data, NaN or infinite input). The codes come from the same scaled convert
+// as the MX path, with scale 1.
 __device__ __forceinline__ uint32_t nv_block(const float v[8], float sg, float tau, uint32_t& S) {
 #pragma clang fp contract(off)
   uint32_t am = amax_bits8(v);
@@ -109,13 +101,9 @@ __device__ __forceinline__ uint32_t nv_block(const float v[8], float sg, float t
   }
   float q[8];
   const float y = 1.0f / d;
-  if (d >= 0x1p-100f && d <= 0x1p100f && __uint_as_float(am) * y <= 0x1p64f) {
+  if (nv_div_applies(d, __uint_as_float(am), y)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float t = v[j] * y;
-      t = fmaf(fmaf(-d, t, v[j]), y, t);
-      q[j] = __builtin_copysignf(fmaf(fmaf(-d, t, v[j]), y, t), v[j]);
-    }
+    for (int j = 0; j < 8; ++j) q[j] = nv_div(v[j], d, y);
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = v[j] / d;

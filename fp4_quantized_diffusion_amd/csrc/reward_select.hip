@@ -76,23 +76,33 @@ __global__ __launch_bounds__(kRewardThreads) void proxy_reward_kernel(
 
 // Position of each candidate in the total order (reward descending, ties by
 // ascending index), by counting; positions < k_top go to top, positions
-// >= n - k_bottom go to bottom (lowest first).
+// >= n - k_bottom go to bottom (lowest first). Rewards are compared through
+// an integer key that orders every float: finite values and infinities by
+// value (-0 and +0 equal), every NaN below -inf. The positions then form a
+// permutation of 0..n-1 whatever the rewards hold, so every requested slot of
+// top and bottom is written exactly once.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v != v) return 0u;                                         // NaN: below everything
+  const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);        // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);             // -inf -> 0x007FFFFF
+}
+
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(const float* __restrict__ r, int n, int k_top,
                                                             int k_bottom, int32_t* __restrict__ top,
                                                             int32_t* __restrict__ bottom) {
-  __shared__ float sr[kRankChunk];
+  __shared__ uint32_t sr[kRankChunk];
   const int i = blockIdx.x * kRankThreads + threadIdx.x;
-  const float ri = i < n ? r[i] : 0.f;
+  const uint32_t ki = i < n ? order_key(r[i]) : 0u;
   int pos = 0;
   for (int base = 0; base < n; base += kRankChunk) {
     const int len = min(kRankChunk, n - base);
     __syncthreads();
-    for (int j = threadIdx.x; j < len; j += kRankThreads) sr[j] = r[base + j];
+    for (int j = threadIdx.x; j < len; j += kRankThreads) sr[j] = order_key(r[base + j]);
     __syncthreads();
     if (i < n) {
       for (int j = 0; j < len; ++j) {
-        const float rj = sr[j];
-        pos += (rj > ri) || (rj == ri && base + j < i);
+        const uint32_t kj = sr[j];
+        pos += (kj > ki) || (kj == ki && base + j < i);
       }
     }
   }

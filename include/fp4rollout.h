@@ -364,6 +364,11 @@ FP4_API fp4_status fp4_proxy_reward(const float* x, int64_t n_cand, int64_t rows
  * by ascending index. top_idx[i] is the i-th entry of that order (i < k_top);
  * bottom_idx[i] is the i-th entry from its end (i < k_bottom), i.e. lowest
  * reward first. With k_top + k_bottom <= n the two lists are disjoint.
+ * Non-finite rewards are ranked too (the one exception to the finite-input
+ * rule above): infinities by value, -0 equal to +0, and every NaN below -inf,
+ * NaNs among themselves by ascending index. Every requested slot of top_idx
+ * and bottom_idx therefore receives a valid index in 0..n-1; r_norm is NaN
+ * everywhere when any reward is NaN.
  *   rewards     fp32 [n], 1 <= n <= 65536.
  *   top_idx     out int32 [k_top] (may be NULL when k_top == 0).
  *   bottom_idx  out int32 [k_bottom] (may be NULL when k_bottom == 0).

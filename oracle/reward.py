@@ -40,9 +40,12 @@ def normalize(r):
 
 
 def order(r):
-    """The total order: reward descending, ties by ascending index."""
+    """The total order: reward descending, ties by ascending index. Every NaN
+    ranks below -inf (NaNs among themselves by index); -0 equals +0. The
+    pages assume finite rewards; this convention only makes the order total,
+    so that a selection always names valid candidates."""
     r = [float(v) for v in np.asarray(r, dtype=np.float64)]
-    return sorted(range(len(r)), key=lambda i: (-r[i], i))
+    return sorted(range(len(r)), key=lambda i: (1, 0.0, i) if r[i] != r[i] else (0, -r[i], i))
 
 
 def select(r, k_top, k_bottom):

@@ -18,6 +18,9 @@ P3 = 0x30000
 
 @pytest.fixture(scope="module")
 def lib():
+    alt = os.environ.get("FP4_ABI_TEST_LIB")  # the sanitizer build of the ABI layer (test_abi_sanitized.py)
+    if alt:
+        return fq.load_library(alt)
     if not os.path.exists(fq.LIB_PATH):
         fbuild.build()
     return fq.load_library()

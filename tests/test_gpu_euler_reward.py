@@ -113,3 +113,27 @@ def test_tiny_config_end_to_end(gpu_lib, fmt):
         gt, gb = oreward.select(to_np(r), 2, 2)
         np.testing.assert_array_equal(to_np(top), gt)
         np.testing.assert_array_equal(to_np(bottom), gb)
+
+
+@pytest.mark.parametrize("n,kt,kb", [(8, 3, 4), (96, 12, 12), (300, 40, 50)])
+def test_select_non_finite_rewards(gpu_lib, n, kt, kb):
+    """NaN and infinite rewards still give a permutation: every requested slot
+    holds a valid index, equal to the oracle's total order (NaN below -inf,
+    -0 equal to +0). The output buffers start as sentinels, so an unwritten
+    slot would show."""
+    import torch
+    rng = np.random.default_rng(n)
+    r = rng.standard_normal(n).astype(np.float32)
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, np.nan, 1.0, -np.inf], np.float32)
+    pos = rng.choice(n, size=min(n, len(special)), replace=False)
+    r[pos] = special[:len(pos)]
+    top = torch.full((kt,), -7, dtype=torch.int32, device=DEV)
+    bottom = torch.full((kb,), -7, dtype=torch.int32, device=DEV)
+    from fp4_quantized_diffusion_amd import binding as fb
+    rd = dev(r)
+    st = fb.select_topk_bottomk(rd.data_ptr(), n, kt, kb, top.data_ptr(), bottom.data_ptr(), None,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    ot, ob = oreward.select(r, kt, kb)
+    np.testing.assert_array_equal(to_np(top), ot)
+    np.testing.assert_array_equal(to_np(bottom), ob)

@@ -105,3 +105,22 @@ def test_pack_unpack_low_nibble_first():
     packed = e2m1.pack(nib)
     assert packed.tolist() == [[0x91, 0x53]]
     np.testing.assert_array_equal(e2m1.unpack(packed), nib)
+
+
+def test_encode_is_monotone_in_magnitude():
+    """For a fixed sign the magnitude index never decreases as |x| grows
+    (the property the exhaustive GPU sweeps rely on to check whole runs of
+    patterns from their ends): every fp32 pattern within 2^14 ulps of each
+    decision point and of each grid value, plus a stride through all finite
+    patterns, in increasing order."""
+    pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 8.0]
+    parts = [np.arange(0, 0x7F800000, 4099, dtype=np.int64)]
+    for v in pts:
+        b = int(np.array(v, np.float32).view(np.uint32))
+        parts.append(np.arange(b - (1 << 14), b + (1 << 14), dtype=np.int64))
+    p = np.unique(np.concatenate(parts)).astype(np.uint32)
+    x = p.view(np.float32).astype(np.float64)
+    for sign in (1.0, -1.0):
+        nib = e2m1.encode(sign * x)
+        assert np.all(np.diff((nib & 7).astype(np.int64)) >= 0)
+        assert np.all((nib >> 3) == (1 if sign < 0 else 0))

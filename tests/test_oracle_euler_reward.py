@@ -141,3 +141,13 @@ def test_rollout_small_is_deterministic_and_ranks_agree():
     ra, rc = np.argsort(np.argsort(a[1])), np.argsort(np.argsort(c[1]))
     rho = np.corrcoef(ra, rc)[0, 1]
     assert rho > 0.8
+
+
+def test_selection_order_with_non_finite_rewards():
+    """The order is total for any float: +inf first, then finite values by
+    value (-0 ties with +0, by index), -inf, and every NaN last by index.
+    Hand-worked: r = [nan, 1, -inf, inf, nan, -0.0, 0.0, -2]."""
+    r = np.array([np.nan, 1.0, -np.inf, np.inf, np.nan, -0.0, 0.0, -2.0])
+    assert reward.order(r) == [3, 1, 5, 6, 7, 2, 0, 4]
+    top, bottom = reward.select(r, 3, 4)
+    assert top.tolist() == [3, 1, 5] and bottom.tolist() == [4, 0, 2, 7]
