@@ -101,7 +101,7 @@ def test_gemm_panel_vs_oracle_and_row_major(gpu_lib, m, n, k, out):
     res = None
     if out == "f32+res":
         ldc = ((n + 3) // 4) * 4
-        res = dev(act(m, ldc, 5))
+        res = dev(act(m, ldc, 5))[:, :n]  # an [m, n] view with the output's row stride
     dt = "bf16" if out == "bf16" else "f32"
     cp = gpu_lib.gemm(qa_p, qb_p, dt, residual=res)
     cr = gpu_lib.gemm(qa_r, qb_r, dt, residual=res)
