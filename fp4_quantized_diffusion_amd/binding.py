@@ -4,10 +4,12 @@ Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
   * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_quantize_nv_grouped,
     fp4_panel_bytes, fp4_gemm_nv_grouped,
-    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, fp4_gemm_panel_euler_reward, euler_step, fp4_proxy_reward,
+    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, fp4_gemm_panel_euler_reward,
+    fp4_gemm_panel_euler_reward_noalloc, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
-  * torch-tensor helpers (quantize, quantize_lora, quantize_nv_grouped, gemm, gemm_gelu, gemm_euler, gemm_euler_reward, euler,
+  * torch-tensor helpers (quantize, quantize_lora, quantize_nv_grouped, gemm, gemm_gelu, gemm_euler, gemm_euler_reward,
+    gemm_euler_reward_noalloc, euler,
     proxy_reward, select) that
     allocate outputs with torch, pass data_ptr()s and the current HIP stream,
     and raise Fp4Error on a non-zero status.
@@ -43,6 +45,8 @@ _SIGS = {
     "fp4_gemm_panel_euler": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p],
     "fp4_gemm_panel_euler_reward": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p, _i64,
                                     _p, _p, _p],
+    "fp4_gemm_panel_euler_reward_noalloc": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p,
+                                            _i64, _p, _p],
     "euler_step": [_p, _p, _p, _i32, _i64, _f32, _f32, _p],
     "fp4_proxy_reward": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
     "select_topk_bottomk": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
@@ -138,6 +142,13 @@ def fp4_gemm_panel_euler_reward(fmt, a_codes, a_scales, b_codes, b_scales, m, n,
     return load_library().fp4_gemm_panel_euler_reward(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual,
                                                       x, x_out, ldx, t_cur, t_next, u, rows_per_cand, partials,
                                                       rewards, stream)
+
+
+def fp4_gemm_panel_euler_reward_noalloc(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x, x_out, ldx,
+                                        t_cur, t_next, u, rows_per_cand, rewards, stream):
+    return load_library().fp4_gemm_panel_euler_reward_noalloc(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k,
+                                                              residual, x, x_out, ldx, t_cur, t_next, u,
+                                                              rows_per_cand, rewards, stream)
 
 
 def euler_step(x_out, x, v, v_dtype, numel, t_cur, t_next, stream):
@@ -440,6 +451,26 @@ def gemm_euler_reward(a, b, residual, x, t_cur, t_next, u, rows_per_cand, out=No
                                      x.stride(0), float(t_cur), float(t_next), u.data_ptr(), rows_per_cand,
                                      partials.data_ptr(), rewards.data_ptr(), _stream())
     _check(st, "fp4_gemm_panel_euler_reward")
+    return out, rewards
+
+
+def gemm_euler_reward_noalloc(a, b, residual, x, t_cur, t_next, u, rows_per_cand, out, rewards):
+    """gemm_euler_reward into caller-supplied out and rewards, with the
+    partial sums in the library's own device array (no workspace, and
+    nothing allocated by this call: for use under graph capture)."""
+    if a.layout != "panel" or b.layout != "panel" or a.k != b.k:
+        raise ValueError("gemm_euler_reward_noalloc takes panel-layout operands of one k")
+    m, n, k = a.n_rows, b.n_rows, a.k
+    for t in (residual, x, out):
+        if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) != x.stride(0) or tuple(t.shape) != (m, n):
+            raise ValueError("residual, x and out must be [m, n] with one row stride")
+    if rows_per_cand < 1 or m % rows_per_cand or rewards.numel() != m // rows_per_cand:
+        raise ValueError("rows_per_cand must divide m, and rewards hold one value per candidate")
+    st = fp4_gemm_panel_euler_reward_noalloc(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                             b.scales.data_ptr(), m, n, k, residual.data_ptr(), x.data_ptr(),
+                                             out.data_ptr(), x.stride(0), float(t_cur), float(t_next), u.data_ptr(),
+                                             rows_per_cand, rewards.data_ptr(), _stream())
+    _check(st, "fp4_gemm_panel_euler_reward_noalloc")
     return out, rewards
 
 

@@ -255,6 +255,32 @@ FP4_API fp4_status fp4_gemm_panel_euler_reward(int fmt, const uint8_t* a_codes, 
   }
 }
 
+FP4_API fp4_status fp4_gemm_panel_euler_reward_noalloc(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                                                       int64_t n, int64_t k, const float* residual, const float* x,
+                                                       float* x_out, int64_t ldx, float t_cur, float t_next,
+                                                       const float* u, int64_t rows_per_cand, float* rewards,
+                                                       void* stream) {
+  try {
+    if (!residual || !x || !aligned(x, 16)) return FP4_INVALID_ARGUMENT;
+    if (!u || !aligned(u, 16) || !rewards || !aligned(rewards, 4)) return FP4_INVALID_ARGUMENT;
+    if (rows_per_cand < 1 || rows_per_cand >= kMaxDim) return FP4_INVALID_ARGUMENT;
+    const fp4_status s =
+        check_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, x_out, FP4_DT_F32, ldx, residual);
+    if (s != FP4_OK) return s;
+    if (m % rows_per_cand != 0) return FP4_INVALID_ARGUMENT;
+    if (m % 256 != 0 || n % 256 != 0 || rows_per_cand % 128 != 0) return FP4_UNSUPPORTED;
+    // the library-owned partial sums: one float per wave tile
+    if ((m / 256) * (n / 256) * 4 > fp4r::kNoAllocPartials) return FP4_INVALID_ARGUMENT;
+    const float dt = t_next - t_cur;  // fp32 subtraction, as euler_step
+    return from_hip(fp4r::launch_gemm_mx_panel_euler_reward_noalloc(a_codes, a_scales, b_codes, b_scales, m, n, k,
+                                                                    residual, x, x_out, ldx, dt, u, rows_per_cand,
+                                                                    rewards, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
 FP4_API fp4_status euler_step(float* x_out, const float* x, const void* v, int v_dtype, int64_t numel, float t_cur,
                               float t_next, void* stream) {
   try {
@@ -396,6 +422,6 @@ FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const 
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 108; }
+FP4_API int fp4_abi_version(void) { return 109; }
 
 }  // extern "C"

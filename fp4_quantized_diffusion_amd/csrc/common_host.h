@@ -46,6 +46,15 @@ hipError_t launch_gemm_mx_panel_euler_reward(const uint8_t* a, const uint8_t* as
                                              int64_t m, int64_t n, int64_t k, const float* residual, const float* x,
                                              float* x_out, int64_t ldx, float dt, const float* u, int64_t rows_per_cand,
                                              float* partials, float* rewards, hipStream_t st);
+// The no-allocation variant of launch_gemm_mx_panel_euler_reward: the partial
+// sums live in a library-owned device array of kNoAllocPartials floats per GPU.
+constexpr int64_t kNoAllocPartials = (int64_t)1 << 18;
+constexpr int kMaxDevices = 64;
+hipError_t launch_gemm_mx_panel_euler_reward_noalloc(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                                     const uint8_t* bs, int64_t m, int64_t n, int64_t k,
+                                                     const float* residual, const float* x, float* x_out, int64_t ldx,
+                                                     float dt, const float* u, int64_t rows_per_cand, float* rewards,
+                                                     hipStream_t st);
 hipError_t launch_gemm_nv(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const float* a_ts,
                           const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs, const float* b_ts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,

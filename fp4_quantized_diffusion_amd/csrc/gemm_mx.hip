@@ -41,6 +41,8 @@
 //    tile map gives each XCD a contiguous band of tiles, walked in groups of
 //    kGroupM tile-rows, so tiles that run together on an XCD share A and B
 //    panels in its L2.
+#include <mutex>
+
 #include "gemm_common.h"
 #include "mx_common.h"
 
@@ -1154,6 +1156,47 @@ hipError_t launch_gemm_mx_panel_euler_reward(const uint8_t* a, const uint8_t* as
   reward_partials_kernel<<<(unsigned)(m / rows_per_cand), 256, 0, st>>>(partials, p.tiles_n, (int)rows_per_cand,
                                                                         rewards);
   return hipGetLastError();
+}
+
+// Scratch for fp4_gemm_panel_euler_reward_noalloc: the per-wave partial sums
+// of the Euler + reward epilogue, for callers that cannot allocate (graph
+// capture, serving loops). One copy per GPU, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not the device array: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[kNoAllocPartials];
+
+hipError_t noalloc_partials(float** ptr) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+// launch_gemm_mx_panel_euler_reward with the partial sums in `scratch`; the
+// caller has checked (m / 256) (n / 256) 4 <= kNoAllocPartials. Every partial
+// is written by the GEMM before the reward kernel reads it, so nothing needs
+// clearing between calls.
+hipError_t launch_gemm_mx_panel_euler_reward_noalloc(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                                     const uint8_t* bs, int64_t m, int64_t n, int64_t k,
+                                                     const float* residual, const float* x, float* x_out, int64_t ldx,
+                                                     float dt, const float* u, int64_t rows_per_cand, float* rewards,
+                                                     hipStream_t st) {
+  float* part = nullptr;
+  const hipError_t e = noalloc_partials(&part);
+  if (e != hipSuccess) return e;
+  return launch_gemm_mx_panel_euler_reward(a, as, b, bs, m, n, k, residual, x, x_out, ldx, dt, u, rows_per_cand, part,
+                                           rewards, st);
 }
 
 // The first solver linear with GELU and MXFP4 quantization of its output in

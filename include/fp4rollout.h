@@ -326,6 +326,29 @@ FP4_API fp4_status fp4_gemm_panel_euler_reward(int fmt, const uint8_t* a_codes, 
                                 float* partials, float* rewards, void* stream);
 
 /*
+ * fp4_gemm_panel_euler_reward_noalloc -- fp4_gemm_panel_euler_reward without
+ * the `partials` workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The per-wave partial sums go to a library-owned device array
+ * of 2^18 floats (1 MiB) per GPU, held until the process ends; the call
+ * itself allocates nothing (the first call on a device looks up the array's
+ * address once). Arguments, layouts and results are those of
+ * fp4_gemm_panel_euler_reward, bit for bit.
+ *   Limit: (m / 256) * (n / 256) * 4 <= 262144 (e.g. m = 393216 rows at
+ *   n = 3072 uses 73728); larger calls return FP4_INVALID_ARGUMENT.
+ *   Every call on one GPU shares that GPU's array, so calls that overlap in
+ *   time on one GPU (other streams, other host threads) race; calls ordered
+ *   on one stream do not. Nothing in the array needs clearing: each call
+ *   writes every partial it reads.
+ */
+FP4_API fp4_status fp4_gemm_panel_euler_reward_noalloc(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                                               int64_t n, int64_t k, const float* residual, const float* x,
+                                               float* x_out, int64_t ldx, float t_cur, float t_next,
+                                               const float* u, int64_t rows_per_cand, float* rewards,
+                                               void* stream);
+
+/*
  * euler_step -- one explicit Euler step of the sampler's ODE,
  *   x_out = x + (t_next - t_cur) * v,
  * with dt = fl32(t_next - t_cur) and an fp32 multiply-add per element. The

@@ -42,6 +42,10 @@ CASES = [
      "launch_gemm_mx_panel_euler"),
     ("fp4_gemm_panel_euler_reward", (0, P, P3, P2, P3, 256, 256, 64, P2, P3, P, 256, 1.0, 0.5, P2, 128, P3, P,
                                      STREAM), "launch_gemm_mx_panel_euler_reward"),
+    ("fp4_gemm_panel_euler_reward_noalloc", (0, P, P3, P2, P3, 256, 256, 64, P2, P3, P, 256, 1.0, 0.5, P2, 128, P,
+                                             STREAM), "launch_gemm_mx_panel_euler_reward_noalloc"),
+    ("fp4_gemm_panel_euler_reward_noalloc", (0, P, P3, P2, P3, 256 * 512, 256 * 128, 64, P2, P3, P, 256 * 128, 1.0,
+                                             0.5, P2, 128, P, STREAM), "launch_gemm_mx_panel_euler_reward_noalloc"),
     ("euler_step", (P, P2, P3, 0, 100, 1.0, 0.5, STREAM), "launch_euler"),
     ("fp4_proxy_reward", (P, 2, 3, 8, 8, None, P2, STREAM), "launch_proxy_reward"),
     ("select_topk_bottomk", (P, 8, 2, 2, P2, P3, None, STREAM), "launch_select"),

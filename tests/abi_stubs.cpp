@@ -53,6 +53,11 @@ hipError_t launch_gemm_mx_panel_euler_reward(const uint8_t*, const uint8_t*, con
                                              const float*, int64_t, float*, float*, hipStream_t) {
   return hit("launch_gemm_mx_panel_euler_reward");
 }
+hipError_t launch_gemm_mx_panel_euler_reward_noalloc(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*,
+                                                     int64_t, int64_t, int64_t, const float*, const float*, float*,
+                                                     int64_t, float, const float*, int64_t, float*, hipStream_t) {
+  return hit("launch_gemm_mx_panel_euler_reward_noalloc");
+}
 hipError_t launch_gemm_nv(const uint8_t*, int64_t, const uint8_t*, int64_t, const float*, const uint8_t*, int64_t,
                           const uint8_t*, int64_t, const float*, int64_t, int64_t, int64_t, void*, int, int64_t,
                           const float*, hipStream_t) { return hit("launch_gemm_nv"); }

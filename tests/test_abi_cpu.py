@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 108
+    assert fq.fp4_abi_version() == 109
 
 
 def test_status_strings(lib):
@@ -323,3 +323,27 @@ def nl(**kw):
 ])
 def test_nft_loss_rejects(lib, kw):
     assert nl(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+def gern(**kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=256, n=256, k=64, residual=P2, x=P3, x_out=P, ldx=256,
+             t_cur=1.0, t_next=5.0 / 6.0, u=P2, rows_per_cand=128, rewards=P, stream=None)
+    a.update(kw)
+    return fq.fp4_gemm_panel_euler_reward_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=3), dict(a=None), dict(residual=None), dict(x=None), dict(x_out=None), dict(u=None), dict(u=P2 + 4),
+    dict(rewards=None), dict(rewards=P + 1), dict(rows_per_cand=0), dict(rows_per_cand=96), dict(m=0), dict(k=48),
+    dict(ldx=250), dict(x=P3 + 4),
+    # the library-owned partial sums hold (m / 256) (n / 256) 4 <= 2^18 floats
+    dict(m=256 * 512, n=256 * 129, ldx=256 * 129), dict(m=256 * 65537, n=256, ldx=256),
+])
+def test_gemm_panel_euler_reward_noalloc_rejects(lib, kw):
+    assert gern(**kw) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=384, rows_per_cand=128), dict(n=128, ldx=128),
+                                dict(rows_per_cand=64)])
+def test_gemm_panel_euler_reward_noalloc_unsupported(lib, kw):
+    assert gern(**kw) == fq.binding.UNSUPPORTED
