@@ -8,10 +8,13 @@ inputs are resident in HBM before timing starts.
 
 Prints one JSON line: candidates/s, the FP4 GEMM's achieved TFLOP/s against
 the MXFP4 peak (HIP events around every GEMM launch of the timed steps), the
-CPU oracle timed on a bounded sample, and rank agreement against the same
-rollout with bf16 linears (torch, outside the timed region).
+CPU oracle timed on bounded samples, rank agreement against the same rollout
+with bf16 linears, and the Stage-2 block -- the BF16 regeneration of the
+selected seeds and the FP4 step-count ablation -- all outside the timed
+region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--chunk C] [--no-cpu-baseline] [--no-rank-agreement]
+                    [--no-stage2] [--ablation]
 """
 import argparse
 import json
@@ -93,95 +96,21 @@ def make_inputs(cfg, device):
     return noise_d, w1, w2, u
 
 
-def bf16_velocity(x, w1, w2):
-    """The velocity network with bf16 linears (torch): fp32 [rows, dim] in and out."""
-    import torch
-    import torch.nn.functional as F
-    h = x.clone()
-    for a, b in zip(w1, w2):
-        y = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + 1e-6)
-        z = F.gelu(F.linear(y.bfloat16(), a).float())
-        h = h + F.linear(z.bfloat16(), b).float()
-    return h
+def bf16_rewards(noise, w1, w2, u, steps, chunk):
+    """Proxy rewards of every candidate under the same rollout with BF16
+    linears (stage2.Bf16Regenerator), for the rank agreement."""
+    from fp4_quantized_diffusion_amd import stage2
+    return stage2.Bf16Regenerator(w1, w2, u, chunk=chunk).run(noise, steps)[1]
 
 
-def bf16_rollout(noise, w1, w2, u, steps, tokens, chunk, return_x=False):
-    """Same rollout with bf16 linears (torch): rank agreement, the step
-    ablation's reference and the Stage-2 regeneration."""
-    n_cand, _, dim = noise.shape
-    x = noise.reshape(-1, dim).clone()
-    t = [1.0 - i / steps for i in range(steps + 1)]
-    for i in range(steps):
-        for c0 in range(0, n_cand, chunk):
-            xs = x[c0 * tokens:(c0 + chunk) * tokens]
-            xs.add_(bf16_velocity(xs, w1, w2), alpha=(t[i + 1] - t[i]))
-    r = (x.view(n_cand, tokens, dim).mean(1) @ u)
-    return (r, x.view(n_cand, tokens, dim)) if return_x else r
-
-
-def rank_stats(a, b, k):
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ra, rb = np.argsort(np.argsort(a)), np.argsort(np.argsort(b))
-    rho = float(np.corrcoef(ra, rb)[0, 1])
-    n = len(a)
-    conc = 0
-    for i in range(n):
-        for j in range(i + 1, n):
-            conc += np.sign(a[i] - a[j]) * np.sign(b[i] - b[j])
-    tau = float(conc / (n * (n - 1) / 2))
-    ta, tb = set(np.argsort(-a)[:k]), set(np.argsort(-b)[:k])
-    ba, bb = set(np.argsort(a)[:k]), set(np.argsort(b)[:k])
-    return {"spearman": round(rho, 4), "kendall_tau": round(tau, 4), "top_overlap": len(ta & tb),
-            "bottom_overlap": len(ba & bb), "k": k}
-
-
-def step_ablation(noise, w1, w2, u, cfg, chunk, fp4_steps=(2, 3, 4, 6, 8, 10), ref_steps=20):
-    """The step-count ablation and the Stage-2 regeneration cost (project
-    page, "Two-Stage Pipeline": FP4 rollouts rank the seeds, the selected K
-    are regenerated in BF16 with the full step budget; aitrends summary: 6 FP4
-    steps). The reference ranking is a BF16 rollout of all candidates with
-    ref_steps steps; each FP4 rollout with S steps is compared with it
-    (Spearman, Kendall, top/bottom-K overlap). Then the BF16 regeneration of
-    the K selected seeds of the 6-step FP4 rollout is timed against that FP4
-    exploration of all candidates. Synthetic weights: the numbers describe
-    this network, not a trained DiT."""
-    import torch
-    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
-    k_top, k_bottom, tokens = cfg["k_top"], cfg["k_bottom"], cfg["tokens"]
-    bchunk = min(chunk, 8)
-
-    def timed(fn):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        res = fn()
-        torch.cuda.synchronize()
-        return res, time.perf_counter() - t0
-
-    r_ref, t_ref = timed(lambda: bf16_rollout(noise, w1, w2, u, ref_steps, tokens, bchunk))
-    r_ref = r_ref.cpu().numpy()
-    out = {"reference": {"kind": "bf16 linears (torch)", "steps": ref_steps, "seconds": round(t_ref, 3)},
-           "fp4": {}}
-    work = torch.empty_like(noise)
-    sel = None
-    for s in fp4_steps:
-        ro = Fp4Rollout(w1, w2, u, steps=s, k_top=k_top, k_bottom=k_bottom, chunk=chunk)
-        ro.run(noise, work)  # warm (buffers, weights)
-        (r, top, bottom, _), t_s = timed(lambda: ro.run(noise, work))
-        out["fp4"][str(s)] = {"seconds": round(t_s, 3), **rank_stats(r.cpu().numpy(), r_ref, k_top)}
-        if s == cfg["steps"]:
-            sel, t_explore, r_fp4 = torch.cat([top, bottom]).long(), t_s, r.cpu().numpy()
-    if sel is not None:
-        seeds = noise.index_select(0, sel).contiguous()
-        (r_regen, x_regen), t_regen = timed(lambda: bf16_rollout(seeds, w1, w2, u, ref_steps, tokens, bchunk,
-                                                                 return_x=True))
-        out["stage2_regeneration"] = {"seeds": int(sel.numel()), "bf16_steps": ref_steps,
-                                      "seconds": round(t_regen, 3),
-                                      "fp4_exploration_seconds": round(t_explore, 3),
-                                      "fp4_exploration": f"{noise.shape[0]} seeds x {cfg['steps']} steps",
-                                      "regeneration_over_exploration": round(t_regen / t_explore, 3)}
-        out["nft_loss_forward"] = nft_forward(x_regen, r_regen, w1, w2, tokens, bchunk)
-        out["evt_diagnostic"] = evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, bchunk)
-    return out
+def ablation_extras(noise, w1, w2, u, cfg, chunk, r_fp4, sel):
+    """--ablation only: the DiffusionNFT loss forward on the BF16-regenerated
+    selected seeds and the extreme-value diagnostic."""
+    from fp4_quantized_diffusion_amd import stage2
+    regen = stage2.Bf16Regenerator(w1, w2, u, chunk=min(chunk, 8))
+    x_regen, r_regen = regen.regenerate(noise, sel, 20)
+    return {"nft_loss_forward": nft_forward(x_regen, r_regen, w1, w2, cfg["tokens"], min(chunk, 8)),
+            "evt_diagnostic": evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, min(chunk, 8))}
 
 
 def nft_forward(x0, r_raw, w1, w2, tokens, chunk, beta=0.1, seed=3):
@@ -193,6 +122,7 @@ def nft_forward(x0, r_raw, w1, w2, tokens, chunk, beta=0.1, seed=3):
     adapter, then fp4_nft_loss; the two kernels are timed against HBM."""
     import torch
     import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd import stage2
     n, _, dim = x0.shape
     g = torch.Generator(device=x0.device).manual_seed(seed)
     eps = torch.randn(x0.shape, generator=g, device=x0.device)
@@ -205,8 +135,8 @@ def nft_forward(x0, r_raw, w1, w2, tokens, chunk, beta=0.1, seed=3):
     flat = xt.view(-1, dim)
     for c0 in range(0, n, chunk):
         rows = slice(c0 * tokens, (c0 + chunk) * tokens)
-        v_old.view(-1, dim)[rows] = bf16_velocity(flat[rows], w1, w2)
-        v_theta.view(-1, dim)[rows] = bf16_velocity(flat[rows], w1p, w2)
+        v_old.view(-1, dim)[rows] = stage2.bf16_velocity(flat[rows], w1, w2)
+        v_theta.view(-1, dim)[rows] = stage2.bf16_velocity(flat[rows], w1p, w2)
     loss, terms = fq.nft_loss(v_old, v_theta, x0.contiguous(), eps, rn, beta)
     x0c = x0.contiguous()
     t_noise = time_launches([lambda: fq.nft_noise(x0c, eps, t, out=xt)], reps=20)
@@ -227,7 +157,7 @@ def evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, bchunk):
     import math
     s = cfg["steps"]
     r4 = np.asarray(r_fp4, dtype=np.float64)
-    rb = bf16_rollout(noise, w1, w2, u, s, cfg["tokens"], bchunk).cpu().numpy().astype(np.float64)
+    rb = bf16_rewards(noise, w1, w2, u, s, bchunk).cpu().numpy().astype(np.float64)
     n = len(r4)
     sigma = float(rb.std())
     delta = float(np.abs(r4 - rb).max())
@@ -237,22 +167,50 @@ def evt_diagnostic(r_fp4, noise, w1, w2, u, cfg, bchunk):
             "range_of_fp4_extremes_in_bf16": round(w, 6), "bound": round(bound, 6), "holds": bool(w >= bound)}
 
 
-def cpu_baseline(cfg, tokens_sample=128, w_rows_sample=1024):
-    """The CPU oracle on a bounded sample of the rollout, scaled to candidates/s:
-    (a) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one W1,
-        scaled by element count to all 8 weights (once per rollout);
-    (b) the oracle's rollout of 1 candidate x tokens_sample tokens through 6
-        steps of the 4-block network (weights in quantized form), scaled by
-        4096 / tokens_sample tokens per candidate."""
+def blas_env():
+    """BLAS library, its thread count and the thread variables, for the CPU figures."""
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS") if k in os.environ}
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [{"api": p.get("internal_api"), "threads": p.get("num_threads"), "version": p.get("version")}
+                 for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception as e:  # reported, never fatal
+        pools = [{"error": repr(e)}]
+    return {"blas": pools, "env": env, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(cfg, tokens_sample=512, w_rows_sample=1024, gemm_rows=512):
+    """The CPU oracle on bounded samples of the workload (numpy float64,
+    the host's BLAS threads), scaled to candidates/s:
+    (a) the tiny configuration in full (128 x 256 x 512: quantize both
+        operands, GEMM, 8 rewards, top-2 / bottom-2), reported as is;
+    (b) the oracle's MXFP4 quantization of a w_rows_sample-row slice of one
+        W1, scaled by element count to all 8 weights (once per rollout);
+    (c) the oracle rollout of 1 candidate x tokens_sample tokens through the
+        6 steps of the 4-block network (weights in quantized form), scaled by
+        4096 / tokens_sample tokens per candidate and by the 96 candidates;
+    (d) a gemm_rows-row slice of the FLUX.1-class up projection (36864 x 3072
+        x 12288): the oracle's activation quantization and exact GEMM,
+        reported in TFLOP/s and scaled to the whole GEMM.
+    value = 96 / ((b) + 96 (c))."""
     from fp4_quantized_diffusion_amd import inputs
-    from oracle import mxfp4, rollout as orollout
+    from oracle import gemm as ogemm, mxfp4, reward as oreward, rollout as orollout
     dim, hidden, blocks = cfg["dim"], cfg["hidden"], cfg["blocks"]
     rng = np.random.default_rng(0)
+    # (a) tiny configuration
+    t0 = time.perf_counter()
+    x, b = inputs.tiny(0)
+    ca, sa = mxfp4.quantize(x)
+    cb, sb = mxfp4.quantize(b)
+    c, _ = ogemm.gemm_mx(ca, sa, cb, sb)
+    oreward.select(oreward.proxy_reward(c, 16), 2, 2)
+    t_tiny = time.perf_counter() - t0
+    # (b) weight re-quantization
     w_slice = inputs.weights(rng, w_rows_sample, dim)
     t0 = time.perf_counter()
     mxfp4.quantize(w_slice)
     t_wq = (time.perf_counter() - t0) * (2 * blocks * hidden * dim) / w_slice.size
-    # quantized weights for the timing sample: random codes / scales of the right shapes
+    # (c) rollout slice; quantized weights for the timing sample: random codes / scales of the right shapes
     q1 = [orollout.QuantLinear.from_quantized("mx", rng.integers(0, 256, (hidden, dim // 2), dtype=np.uint8),
                                               rng.integers(118, 124, (hidden, dim // 32), dtype=np.uint8))
           for _ in range(blocks)]
@@ -264,15 +222,30 @@ def cpu_baseline(cfg, tokens_sample=128, w_rows_sample=1024):
     t0 = time.perf_counter()
     orollout.rollout(noise, q1, q2, u, n_steps=cfg["steps"], k_top=1, k_bottom=0)
     t_cand = (time.perf_counter() - t0) * cfg["tokens"] / tokens_sample
+    # (d) FLUX-class GEMM slice (the weight quantization is outside the timing: once per iteration)
+    m_full, k, n = 36864, 3072, 12288
+    act = inputs.activations(rng, gemm_rows, k)
+    wq = q1[0].w_hat if (k, n) == (dim, hidden) else None
+    t0 = time.perf_counter()
+    a_hat = mxfp4.dequant(*mxfp4.quantize(act))
+    ogemm.gemm_dense(a_hat, wq)
+    t_gemm = time.perf_counter() - t0
+    flop = 2.0 * gemm_rows * k * n
     total = t_wq + cfg["n_cand"] * t_cand
-    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    return {"value": round(cfg["n_cand"] / total, 6), "unit": "candidates/s", "cores": int(threads),
+    env = blas_env()
+    threads = env["blas"][0].get("threads") if env["blas"] and "threads" in env["blas"][0] else None
+    return {"value": round(cfg["n_cand"] / total, 6), "unit": "candidates/s",
+            "cores": int(threads or os.environ.get("OMP_NUM_THREADS") or os.cpu_count()),
             "kind": "oracle",
             "sample": (f"oracle MXFP4 quantization of a {w_rows_sample}x{dim} weight slice (scaled by elements to "
                        f"all {2 * blocks} weights: {t_wq:.1f}s) + oracle rollout of 1 candidate x {tokens_sample} "
                        f"tokens, {cfg['steps']} steps x {blocks} blocks (scaled x{cfg['tokens'] // tokens_sample} "
-                       f"tokens, x{cfg['n_cand']} candidates: {cfg['n_cand'] * t_cand:.1f}s); numpy float64, "
-                       f"os.cpu_count()={os.cpu_count()}")}
+                       f"tokens, x{cfg['n_cand']} candidates: {cfg['n_cand'] * t_cand:.1f}s); numpy float64"),
+            "tiny_config_seconds": round(t_tiny, 4),
+            "flux_up_gemm_slice": {"rows": gemm_rows, "of": [m_full, k, n], "seconds": round(t_gemm, 3),
+                                   "tflops": round(flop / t_gemm / 1e12, 4),
+                                   "full_gemm_seconds_scaled": round(t_gemm * m_full / gemm_rows, 1)},
+            "host": env}
 
 
 def time_launches(fns, reps=50, warm_ms=100.0):
@@ -440,9 +413,11 @@ def main():
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
+    ap.add_argument("--no-stage2", action="store_true",
+                    help="skip the Stage-2 block (BF16 regeneration of the selected seeds, FP4 step-count ablation)")
     ap.add_argument("--ablation", action="store_true",
-                    help="also run the FP4 step-count ablation (2..10 steps against a 20-step BF16 rollout) and "
-                         "time the BF16 regeneration of the selected seeds")
+                    help="a finer step-count ablation (2, 3, 4, 6, 8, 10 FP4 steps), plus the DiffusionNFT loss "
+                         "forward on the regenerated seeds and the extreme-value diagnostic")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
@@ -548,17 +523,30 @@ def main():
                                                            u, cfg)
         log(f"standalone step kernels: {time.time() - t0:.1f}s")
     if not args.no_rank_agreement:
+        from fp4_quantized_diffusion_amd import stage2
         try:
             t0 = time.time()
-            r_bf16 = bf16_rollout(noise, w1, w2, u, cfg["steps"], cfg["tokens"], min(chunk, 8))
-            out["rank_agreement_vs_bf16"] = rank_stats(rewards.cpu().numpy(), r_bf16.cpu().numpy(), cfg["k_top"])
+            r_bf16 = bf16_rewards(noise, w1, w2, u, cfg["steps"], min(chunk, 8))
+            out["rank_agreement_vs_bf16"] = stage2.rank_stats(rewards.cpu().numpy(), r_bf16.cpu().numpy(),
+                                                              cfg["k_top"])
             log(f"bf16 rollout for rank agreement: {time.time() - t0:.1f}s")
         except Exception as e:  # reported, never fatal
             out["rank_agreement_vs_bf16"] = {"error": repr(e)}
-    if args.ablation:
+    if not args.no_stage2:
+        # Stage 2 and the step-count ablation, outside the timed region: FP4
+        # explorations with 2..10 steps ranked against a 20-step BF16 rollout of
+        # every candidate, and the BF16 regeneration of the 24 seeds the 6-step
+        # exploration keeps
+        from fp4_quantized_diffusion_amd import stage2
         t0 = time.time()
-        out["step_ablation"] = step_ablation(noise, w1, w2, u, cfg, chunk)
-        log(f"step ablation: {time.time() - t0:.1f}s")
+        steps_list = (2, 3, 4, 6, 8, 10) if args.ablation else (2, 4, 6, 10)
+        out["stage2"] = stage2.step_ablation(noise, w1, w2, u, cfg["k_top"], cfg["k_bottom"], fp4_steps=steps_list,
+                                             ref_steps=20, explore_steps=cfg["steps"], chunk=chunk,
+                                             bf16_chunk=min(chunk, 8))
+        log(f"stage 2 and step ablation: {time.time() - t0:.1f}s")
+        if args.ablation:
+            sel = torch.cat([top, bottom])
+            out["stage2"].update(ablation_extras(noise, w1, w2, u, cfg, chunk, rewards.cpu().numpy(), sel))
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -27,6 +27,11 @@ def ranks(v):
 # times (GELU + MXFP4 in the first GEMM's epilogue, the Euler step and the
 # proxy reward in the last GEMM's).
 ROLLOUT_CASES = [("panel", 64, 3, 8), ("row", 64, 3, 8), ("panel", 256, 4, 16)]
+# Observed on MI355X: final-latent relative L2 4.20e-2 (all three cases),
+# Spearman rho 1.000 / 1.000 / 0.988, top-2 and bottom-2 overlap 4 of 4. The
+# distance is dominated by the bf16 rounding of the hidden activation before
+# GELU (the oracle keeps it exact), which moves values across quantization
+# decision points; the gates sit above the observed values.
 
 
 @pytest.mark.parametrize("layout,tokens,chunk,n_cand", ROLLOUT_CASES)
@@ -53,7 +58,8 @@ def test_reduced_rollout_against_oracle(gpu_lib, layout, tokens, chunk, n_cand):
     print(f"rollout {layout} tokens={tokens} chunk={chunk}: rel L2 {rel:.3e}  reward rel {rrel:.3e}  "
           f"spearman {rho:.4f}  top/bottom overlap {ov}/4")
     assert rel < 0.05
-    assert rho > 0.9
+    assert rho > 0.95
+    assert ov >= 3
     # the GPU's selection is the exact selection of its own rewards
     from oracle import reward as oreward
     gt, gb = oreward.select(to_np(r), 2, 2)
