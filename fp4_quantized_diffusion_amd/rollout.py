@@ -55,7 +55,7 @@ from . import binding as fb
 
 class Fp4Rollout:
     def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None,
-                 layout="panel", overlap=False, lora=None, fuse_reward=True):
+                 layout="panel", overlap=False, lora=None, fuse_reward=True, hidden="bf16"):
         """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
         lora: optional (lora1, lora2), one entry per block each, None or a
         LoRA adapter (B, A, scale) of that weight; the per-iteration
@@ -70,7 +70,13 @@ class Fp4Rollout:
         overlap: two-stream schedule over two halves of the candidates (needs
         at least 2 candidates).
         timer: optional callable(name, fn) wrapping each launch (for timing);
-        it is called with the launch's stream current."""
+        it is called with the launch's stream current.
+        hidden: "bf16" (default) rounds the first linear's output to bf16
+        before GELU -- in the fused epilogue, or stored as bf16 between the
+        kernels; "f32" keeps it fp32 (GEMM with fp32 output, then the GELU
+        quantizer evaluates erfc on the fp32 values), which is the float64
+        oracle's reading of the hidden activation, at the cost of the unfused
+        path's traffic."""
         if fmt != "mx":
             raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
         self.w1, self.w2, self.u = list(w1), list(w2), u
@@ -80,6 +86,11 @@ class Fp4Rollout:
         self.fmt, self.chunk, self.layout = fmt, chunk, layout
         self.overlap = overlap
         self.fuse_reward = fuse_reward
+        if hidden not in ("bf16", "f32"):
+            raise ValueError(f"unknown hidden dtype {hidden!r}")
+        if hidden == "f32" and overlap:
+            raise ValueError("the two-stream schedule stores the hidden activation as bf16")
+        self.hidden = hidden
         self._side = None
         self.timer = timer
         self.q1 = self.q2 = None
@@ -134,8 +145,9 @@ class Fp4Rollout:
         hidden = self.w1[0].shape[0]
         # the first linear quantizes GELU of its own output (fp4_gemm_panel_gelu)
         # when the shapes allow; otherwise z goes through HBM as bf16
-        fused = self.layout == "panel" and rows % 256 == 0 and hidden % 256 == 0
-        z = None if fused else self._buf("z", (rows, hidden), torch.bfloat16, x.device)
+        fused = self.layout == "panel" and rows % 256 == 0 and hidden % 256 == 0 and self.hidden == "bf16"
+        zdt = torch.bfloat16 if self.hidden == "bf16" else torch.float32
+        z = None if fused else self._buf("z", (rows, hidden), zdt, x.device)
         src = x
         last = len(self.w1) - 1
         for b in range(len(self.w1)):
@@ -145,7 +157,7 @@ class Fp4Rollout:
                 a2 = self._call("gemm", lambda: fb.gemm_gelu(a1, self.q1[b], out=self._qbuf("a2", rows, hidden,
                                                                                           x.device)))
             else:
-                self._gemm(a1, self.q1[b], "bf16", out=z)
+                self._gemm(a1, self.q1[b], self.hidden, out=z)
                 a2 = self._call("quant_gelu", lambda: fb.quantize(
                     z, self.fmt, prologue="gelu", out=self._qbuf("a2", rows, hidden, x.device)))
             if b == last and step is not None:

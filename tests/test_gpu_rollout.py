@@ -199,3 +199,30 @@ def test_lora_rollout_equals_rollout_on_merged_weights(gpu_lib, layout):
         outs.append((to_np(xd), to_np(r), to_np(top), to_np(bottom), to_np(rn)))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_rollout_with_fp32_hidden_activation_against_oracle(gpu_lib):
+    """hidden="f32": the first linear's output stays fp32 into the GELU
+    quantizer (the oracle's reading of the hidden activation), so the GPU
+    differs from the float64 oracle only by fp32 accumulation and evaluation
+    -- a far smaller distance than the bf16-hidden default (4.2e-2 above).
+    Observed on MI355X: see the printed value; the gate sits above it."""
+    seed, n_cand, tokens, dim, hidden = 4, 8, 64, 256, 1024
+    noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
+    ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
+    w1 = [w[0] for w in ws]
+    w2 = [w[1] for w in ws]
+    u = inputs.reward_vector(seed, dim)
+    x_or, r_or, t_or, b_or = orollout.rollout(noise, w1, w2, u, fmt="mx", k_top=2, k_bottom=2)
+    ro = Fp4Rollout([torch.from_numpy(w).to(DEV).bfloat16() for w in w1],
+                    [torch.from_numpy(w).to(DEV).bfloat16() for w in w2],
+                    torch.from_numpy(u).to(DEV), k_top=2, k_bottom=2, chunk=4, hidden="f32")
+    xd = torch.from_numpy(noise).to(DEV)
+    r, top, bottom, rn = ro.run(xd)
+    torch.cuda.synchronize()
+    x_gpu = to_np(xd).astype(np.float64)
+    rel = np.linalg.norm(x_gpu - x_or) / np.linalg.norm(x_or)
+    rho = np.corrcoef(ranks(to_np(r)), ranks(r_or))[0, 1]
+    print(f"rollout hidden=f32: rel L2 {rel:.3e}  spearman {rho:.4f}")
+    assert rel < 2e-2
+    assert rho > 0.95
