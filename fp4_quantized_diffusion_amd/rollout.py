@@ -41,8 +41,9 @@ beside the GEMM's one workgroup per CU (its waves leave VGPRs for one more
 wave per SIMD), so they overlap it. Every kernel computes rows independently
 of how the rows are chunked, so the result is bit-identical to the
 one-stream schedule. Both streams run at the default priority. On MI355X
-this schedule measured slower than the one-stream one for the 96 x 4096 x
-3072 rollout (534 vs 523 ms per step): the GEMM runs at the card's power
+this schedule measured slower than the one-stream schedule of the same
+(unfused) kernels for the 96 x 4096 x 3072 rollout (534 vs 523 ms per step;
+the fused default path takes 370-381 ms): the GEMM runs at the card's power
 limit, and the overlapped quantizers lower the clock and slow the GEMM by
 more than they hide; it is kept as an option.
 

@@ -400,7 +400,6 @@ FP4_API fp4_status fp4_proxy_reward(const float* x, int64_t n_cand, int64_t rows
 FP4_API fp4_status select_topk_bottomk(const float* rewards, int64_t n, int64_t k_top, int64_t k_bottom,
                                int32_t* top_idx, int32_t* bottom_idx, float* r_norm, void* stream);
 
-/* Human-readable name of a status code (static string). */
 /*
  * fp4_nft_noise / fp4_nft_loss -- the DiffusionNFT policy update's forward
  * pieces on the regenerated samples (VeRL-Omni DiffusionNFT docs,
@@ -432,6 +431,7 @@ FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const 
                         const float* r, float beta, int64_t n, int64_t d, float* partials, float* terms,
                         float* loss, void* stream);
 
+/* Human-readable name of a status code (static string). */
 FP4_API const char* fp4_status_str(fp4_status s);
 
 /* Version of this ABI (major * 100 + minor). */

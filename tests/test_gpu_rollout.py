@@ -206,7 +206,8 @@ def test_rollout_with_fp32_hidden_activation_against_oracle(gpu_lib):
     quantizer (the oracle's reading of the hidden activation), so the GPU
     differs from the float64 oracle only by fp32 accumulation and evaluation
     -- a far smaller distance than the bf16-hidden default (4.2e-2 above).
-    Observed on MI355X: see the printed value; the gate sits above it."""
+    Observed on MI355X: relative L2 1.88e-3, Spearman rho 1.000; the gate
+    leaves about twice that."""
     seed, n_cand, tokens, dim, hidden = 4, 8, 64, 256, 1024
     noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
     ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
@@ -224,5 +225,5 @@ def test_rollout_with_fp32_hidden_activation_against_oracle(gpu_lib):
     rel = np.linalg.norm(x_gpu - x_or) / np.linalg.norm(x_or)
     rho = np.corrcoef(ranks(to_np(r)), ranks(r_or))[0, 1]
     print(f"rollout hidden=f32: rel L2 {rel:.3e}  spearman {rho:.4f}")
-    assert rel < 2e-2
+    assert rel < 4e-3
     assert rho > 0.95
