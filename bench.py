@@ -398,6 +398,23 @@ def rollout_step_kernels(x, v, u, cfg):
     return out
 
 
+def gelu_epilogue_variants(x, w1, cfg):
+    """The first linear's fused GELU + MXFP4 epilogue at the rollout's size,
+    two ways: GELU of bf16(C) from the LDS table (the default) and GELU of the
+    fp32 sums (fp4_gemm_panel_gelu_f32, the oracle's reading), each timed
+    alone. x: fp32 [rows, dim]; w1: the first block's bf16 weight."""
+    import fp4_quantized_diffusion_amd as fq
+    a1 = fq.quantize(x, "mx", prologue="rmsnorm", layout="panel")
+    wq = fq.quantize(w1, "mx", layout="panel")
+    out = fq.gemm_gelu(a1, wq)
+    t_tab = time_launches([lambda: fq.gemm_gelu(a1, wq, out=out)], reps=10)
+    t_f32 = time_launches([lambda: fq.gemm_gelu(a1, wq, out=out, exact=True)], reps=10)
+    flop = 2.0 * x.shape[0] * cfg["dim"] * cfg["hidden"]
+    return {"shape": [x.shape[0], cfg["dim"], cfg["hidden"]],
+            "bf16_table_us": [round(a, 1) for a in t_tab], "f32_erfc_us": [round(a, 1) for a in t_f32],
+            "bf16_table_tflops": round(flop / t_tab[0] / 1e6, 1), "f32_erfc_tflops": round(flop / t_f32[0] / 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +538,7 @@ def main():
         t0 = time.time()
         out["rollout_step_kernels"] = rollout_step_kernels(work.view(-1, cfg["dim"]), noise.view(-1, cfg["dim"]),
                                                            u, cfg)
+        out["rollout_step_kernels"]["gelu_epilogue"] = gelu_epilogue_variants(noise.view(-1, cfg["dim"]), w1[0], cfg)
         log(f"standalone step kernels: {time.time() - t0:.1f}s")
     if not args.no_rank_agreement:
         from fp4_quantized_diffusion_amd import stage2

@@ -14,7 +14,7 @@ _BINDING_NAMES = {
     "fp4_gemm_panel_euler", "gemm_euler", "fp4_gemm_panel_gelu", "gemm_gelu", "fp4_quantize_lora", "quantize_lora",
     "fp4_gemm_panel_euler_reward", "gemm_euler_reward", "fp4_quantize_nv_grouped", "quantize_nv_grouped",
     "fp4_gemm_nv_grouped", "fp4_nft_noise", "fp4_nft_loss", "nft_noise", "nft_loss",
-    "fp4_gemm_panel_euler_reward_noalloc", "gemm_euler_reward_noalloc",
+    "fp4_gemm_panel_euler_reward_noalloc", "gemm_euler_reward_noalloc", "fp4_gemm_panel_gelu_f32",
 }
 
 

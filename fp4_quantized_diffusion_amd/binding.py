@@ -4,7 +4,8 @@ Two layers, argument marshalling only -- every step of the path runs in the
 library's HIP kernels:
   * the raw entry points under their C names (fp4_quantize, fp4_quantize_lora, fp4_quantize_nv_grouped,
     fp4_panel_bytes, fp4_gemm_nv_grouped,
-    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_euler, fp4_gemm_panel_euler_reward,
+    fp4_gemm, fp4_gemm_panel, fp4_gemm_panel_gelu, fp4_gemm_panel_gelu_f32, fp4_gemm_panel_euler,
+    fp4_gemm_panel_euler_reward,
     fp4_gemm_panel_euler_reward_noalloc, euler_step, fp4_proxy_reward,
     select_topk_bottomk), taking integers and device addresses and returning
     the status code;
@@ -42,6 +43,7 @@ _SIGS = {
                             _p, _p],
     "fp4_gemm_panel": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p],
     "fp4_gemm_panel_gelu": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p],
+    "fp4_gemm_panel_gelu_f32": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p],
     "fp4_gemm_panel_euler": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p],
     "fp4_gemm_panel_euler_reward": [_i32, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _f32, _f32, _p, _i64,
                                     _p, _p, _p],
@@ -129,6 +131,11 @@ def fp4_gemm_panel(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtyp
 def fp4_gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales, stream):
     return load_library().fp4_gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes,
                                               out_scales, stream)
+
+
+def fp4_gemm_panel_gelu_f32(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales, stream):
+    return load_library().fp4_gemm_panel_gelu_f32(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes,
+                                                  out_scales, stream)
 
 
 def fp4_gemm_panel_euler(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, residual, x, x_out, ldx, t_cur, t_next,
@@ -387,9 +394,10 @@ def gemm(a, b, out_dtype="bf16", residual=None, out=None):
     return out
 
 
-def gemm_gelu(a, b, out=None):
+def gemm_gelu(a, b, out=None, exact=False):
     """MXFP4 panel QTensor of GELU(bf16(A_hat B_hat^T)) for panel-layout
-    QTensors a [m, k], b [n, k] (m, n multiples of 256)."""
+    QTensors a [m, k], b [n, k] (m, n multiples of 256); exact=True takes
+    GELU of the fp32 sums instead (fp4_gemm_panel_gelu_f32)."""
     torch = _torch()
     if a.layout != "panel" or b.layout != "panel" or a.k != b.k:
         raise ValueError("gemm_gelu takes panel-layout operands of one k")
@@ -400,9 +408,10 @@ def gemm_gelu(a, b, out=None):
                       torch.empty(sb, dtype=torch.uint8, device=a.codes.device), None, FMT_MX, n, "panel", m)
     if out.layout != "panel" or out.rows != m or out.k != n:
         raise ValueError("out was allocated for another shape")
-    st = fp4_gemm_panel_gelu(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
-                             m, n, k, out.codes.data_ptr(), out.scales.data_ptr(), _stream())
-    _check(st, "fp4_gemm_panel_gelu")
+    fn = fp4_gemm_panel_gelu_f32 if exact else fp4_gemm_panel_gelu
+    st = fn(a.fmt, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+            m, n, k, out.codes.data_ptr(), out.scales.data_ptr(), _stream())
+    _check(st, fn.__name__)
     return out
 
 

@@ -192,22 +192,40 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
   }
 }
 
+namespace {
+fp4_status gemm_panel_gelu(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, uint8_t* out_codes,
+                           uint8_t* out_scales, int exact, void* stream) {
+  if (fmt != FP4_FMT_MX && fmt != FP4_FMT_NV) return FP4_INVALID_ARGUMENT;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !out_codes || !out_scales) return FP4_INVALID_ARGUMENT;
+  if (m < 1 || n < 1 || k < 32 || k % 32 != 0) return FP4_INVALID_ARGUMENT;
+  if (m >= kMaxDim - 256 || n >= kMaxDim - 256 || k > ((int64_t)1 << 23)) return FP4_INVALID_ARGUMENT;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+      !aligned(out_codes, 16) || !aligned(out_scales, 4))
+    return FP4_INVALID_ARGUMENT;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (tiles >= kMaxDim) return FP4_INVALID_ARGUMENT;
+  if (fmt == FP4_FMT_NV || m % 256 != 0 || n % 256 != 0) return FP4_UNSUPPORTED;
+  return from_hip(fp4r::launch_gemm_mx_panel_gelu(a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales,
+                                                  exact, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
 FP4_API fp4_status fp4_gemm_panel_gelu(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
                                        int64_t k, uint8_t* out_codes, uint8_t* out_scales, void* stream) {
   try {
-    if (fmt != FP4_FMT_MX && fmt != FP4_FMT_NV) return FP4_INVALID_ARGUMENT;
-    if (!a_codes || !a_scales || !b_codes || !b_scales || !out_codes || !out_scales) return FP4_INVALID_ARGUMENT;
-    if (m < 1 || n < 1 || k < 32 || k % 32 != 0) return FP4_INVALID_ARGUMENT;
-    if (m >= kMaxDim - 256 || n >= kMaxDim - 256 || k > ((int64_t)1 << 23)) return FP4_INVALID_ARGUMENT;
-    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
-        !aligned(out_codes, 16) || !aligned(out_scales, 4))
-      return FP4_INVALID_ARGUMENT;
-    const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
-    if (tiles >= kMaxDim) return FP4_INVALID_ARGUMENT;
-    if (fmt == FP4_FMT_NV || m % 256 != 0 || n % 256 != 0) return FP4_UNSUPPORTED;
-    return from_hip(fp4r::launch_gemm_mx_panel_gelu(a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes,
-                                                    out_scales, static_cast<hipStream_t>(stream)));
+    return gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales, 0, stream);
+  } catch (...) {
+    return FP4_INTERNAL;
+  }
+}
+
+FP4_API fp4_status fp4_gemm_panel_gelu_f32(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                                           int64_t k, uint8_t* out_codes, uint8_t* out_scales, void* stream) {
+  try {
+    return gemm_panel_gelu(fmt, a_codes, a_scales, b_codes, b_scales, m, n, k, out_codes, out_scales, 1, stream);
   } catch (...) {
     return FP4_INTERNAL;
   }
@@ -422,6 +440,6 @@ FP4_API fp4_status fp4_nft_loss(const float* v_old, const float* v_theta, const 
   }
 }
 
-FP4_API int fp4_abi_version(void) { return 109; }
+FP4_API int fp4_abi_version(void) { return 110; }
 
 }  // extern "C"

@@ -36,9 +36,10 @@ hipError_t launch_gemm_mx(const uint8_t* a, int64_t lda, const uint8_t* as, int6
 hipError_t launch_gemm_mx_panel(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                                 int64_t m, int64_t n, int64_t k, void* c, int c_bf16, int64_t ldc,
                                 const float* residual, hipStream_t st);
+// exact: GELU of the fp32 sums (erfc per element) instead of their bf16 rounding (table)
 hipError_t launch_gemm_mx_panel_gelu(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                                      int64_t m, int64_t n, int64_t k, uint8_t* out_codes, uint8_t* out_scales,
-                                     hipStream_t st);
+                                     int exact, hipStream_t st);
 hipError_t launch_gemm_mx_panel_euler(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                                       int64_t m, int64_t n, int64_t k, const float* residual, const float* x,
                                       float* x_out, int64_t ldx, float dt, hipStream_t st);

@@ -534,7 +534,8 @@ __device__ __forceinline__ float acc_read(float a) {
 // epilogue, 2 code stores and 1 scale store per 32 rows.)
 template <int BF16OUT, int RESID>
 constexpr int full_tile_vmem() {
-  return RESID == 3 ? 12 : (RESID == 4 ? 16 * 12 + 5 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))));
+  return (RESID == 3 || RESID == 5) ? 12
+                                    : (RESID == 4 ? 16 * 12 + 5 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -740,6 +741,10 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // rows m0 .. m0 + 127 of the panel: codes of 32 rows are staged in LDS and
 // leave as 2 KiB contiguous (two 16-byte stores per lane), the 4 scale bytes
 // of a row as one 4-byte store.
+// EXACT: GELU of the fp32 sum itself (erfc evaluated per element, no bf16
+// rounding, no table) -- the operations of an fp32-out GEMM followed by
+// fp4_quantize(GELU prologue) on its fp32 output, so the same bits.
+template <bool EXACT>
 __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
                                                    uint8_t* stage, const float* tab) {
   int lane = threadIdx.x & 63;
@@ -753,16 +758,21 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float g[16];
+      if (EXACT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
-        const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
-        uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
-        asm("" : "+v"(u));  // one pair conversion (the compiler would convert the even element again on its own)
-        g[2 * e] = __uint_as_float(u << 16);
-        g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+        for (int e = 0; e < 16; ++e) g[e] = gelu_erfc(acc_read(acc[i][j][e]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
+          const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
+          uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
+          asm("" : "+v"(u));  // one pair conversion (the compiler would convert the even element again on its own)
+          g[2 * e] = __uint_as_float(u << 16);
+          g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
       uint32_t am = amax_bits<16>(g);
       {  // the other lane half's amax: one of each swapped pair is this lane's own
         const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
@@ -915,14 +925,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
   // full tiles' epilogue through an LDS staging area (the MXFP4 ring leaves
   // room for it; the NVFP4-style ring, with twice the scale bytes, does not);
   // the GELU + MXFP4 epilogue has its own, smaller one and the GELU table
-  constexpr bool GELU_Q = RESID == 3;
+  constexpr bool GELU_Q = RESID == 3 || RESID == 5;  // 5: GELU of the fp32 sum (no table)
+  constexpr bool GELU_TAB = RESID == 3;
   constexpr bool EPI_LDS = !NV && !GELU_Q;
   // The GELU + MXFP4 epilogue needs the registers that the next tile's first
   // fragments would hold across it: it reads them afterwards.
   constexpr bool DEFER_READ = GELU_Q;
   __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : (GELU_Q ? 4 * kQWaveBytes : 16)];
-  __shared__ float gtab[GELU_Q ? kGeluTab : 1];
-  if (GELU_Q) gelu_table_fill(gtab);  // visible to all waves after the first pipeline barrier
+  __shared__ float gtab[GELU_TAB ? kGeluTab : 1];
+  if (GELU_TAB) gelu_table_fill(gtab);  // visible to all waves after the first pipeline barrier
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
@@ -988,7 +999,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
     counted = rows16 && (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
     if (GELU_Q) {
       // every tile is full (the host launches this epilogue only for m, n multiples of 256)
-      store_tile_gelu_mx(acc, (int64_t)tm * p.qnc + 2 * tn + wn, wm * 128, p, epi_stage + wave * kQWaveBytes, gtab);
+      store_tile_gelu_mx<RESID == 5>(acc, (int64_t)tm * p.qnc + 2 * tn + wn, wm * 128, p,
+                                     epi_stage + wave * kQWaveBytes, gtab);
       counted = true;
     } else if (counted) {
       if (EPI_LDS && BF16OUT)
@@ -1201,18 +1213,21 @@ hipError_t launch_gemm_mx_panel_euler_reward_noalloc(const uint8_t* a, const uin
 
 // The first solver linear with GELU and MXFP4 quantization of its output in
 // its epilogue: codes / scales of GELU(bf16(A_hat B_hat^T)) in the panel
-// layout of an [m, n] operand. m and n must be multiples of 256 (checked by
-// the caller).
+// layout of an [m, n] operand -- or, with `exact`, of GELU of the fp32 sums
+// themselves. m and n must be multiples of 256 (checked by the caller).
 hipError_t launch_gemm_mx_panel_gelu(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                                      int64_t m, int64_t n, int64_t k, uint8_t* out_codes, uint8_t* out_scales,
-                                     hipStream_t st) {
+                                     int exact, hipStream_t st) {
   Problem p = make_problem(a, as, b, bs, m, n, k);
   p.qc = out_codes;
   p.qs = out_scales;
   p.qnc = (int)(n / 128);
   const int nst4 = (p.nkc + NBUF - 1) / NBUF * NBUF;
   const unsigned grid = (unsigned)min(p.total, cu_count());
-  gemm_fp4_kernel<0, 3, LD_PANEL><<<grid, kThreads, 0, st>>>(p, nullptr, 0, nullptr, nst4);
+  if (exact)
+    gemm_fp4_kernel<0, 5, LD_PANEL><<<grid, kThreads, 0, st>>>(p, nullptr, 0, nullptr, nst4);
+  else
+    gemm_fp4_kernel<0, 3, LD_PANEL><<<grid, kThreads, 0, st>>>(p, nullptr, 0, nullptr, nst4);
   return hipGetLastError();
 }
 

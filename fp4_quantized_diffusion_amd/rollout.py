@@ -73,11 +73,11 @@ class Fp4Rollout:
         timer: optional callable(name, fn) wrapping each launch (for timing);
         it is called with the launch's stream current.
         hidden: "bf16" (default) rounds the first linear's output to bf16
-        before GELU -- in the fused epilogue, or stored as bf16 between the
-        kernels; "f32" keeps it fp32 (GEMM with fp32 output, then the GELU
-        quantizer evaluates erfc on the fp32 values), which is the float64
-        oracle's reading of the hidden activation, at the cost of the unfused
-        path's traffic."""
+        before GELU -- in the fused epilogue (table lookup), or stored as bf16
+        between the kernels; "f32" keeps it fp32 (the fused epilogue evaluates
+        erfc on the fp32 sums, fp4_gemm_panel_gelu_f32; the unfused path
+        stores z as fp32), which is the float64 oracle's reading of the hidden
+        activation, at about three times the epilogue arithmetic."""
         if fmt != "mx":
             raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
         self.w1, self.w2, self.u = list(w1), list(w2), u
@@ -146,7 +146,7 @@ class Fp4Rollout:
         hidden = self.w1[0].shape[0]
         # the first linear quantizes GELU of its own output (fp4_gemm_panel_gelu)
         # when the shapes allow; otherwise z goes through HBM as bf16
-        fused = self.layout == "panel" and rows % 256 == 0 and hidden % 256 == 0 and self.hidden == "bf16"
+        fused = self.layout == "panel" and rows % 256 == 0 and hidden % 256 == 0
         zdt = torch.bfloat16 if self.hidden == "bf16" else torch.float32
         z = None if fused else self._buf("z", (rows, hidden), zdt, x.device)
         src = x
@@ -156,7 +156,8 @@ class Fp4Rollout:
                 src, self.fmt, prologue="rmsnorm", out=self._qbuf("a1", rows, dim, x.device)))
             if fused:
                 a2 = self._call("gemm", lambda: fb.gemm_gelu(a1, self.q1[b], out=self._qbuf("a2", rows, hidden,
-                                                                                          x.device)))
+                                                                                          x.device),
+                                                             exact=self.hidden == "f32"))
             else:
                 self._gemm(a1, self.q1[b], self.hidden, out=z)
                 a2 = self._call("quant_gelu", lambda: fb.quantize(

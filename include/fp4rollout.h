@@ -275,6 +275,21 @@ FP4_API fp4_status fp4_gemm_panel_gelu(int fmt, const uint8_t* a_codes, const ui
                                uint8_t* out_codes, uint8_t* out_scales, void* stream);
 
 /*
+ * fp4_gemm_panel_gelu_f32 -- fp4_gemm_panel_gelu with GELU evaluated on the
+ * fp32 sums themselves (no bf16 rounding of the hidden activation): the
+ * reading in which the hidden activation stays fp32 between the two linears.
+ * Bit-identical to fp4_gemm_panel(..., FP4_DT_F32) into z followed by
+ * fp4_quantize(z, FP4_LAYOUT_PANEL | FP4_PRO_GELU). GELU is z Phi(z) with the
+ * complementary error function evaluated per element (relative error about
+ * 5e-7), so the epilogue does about three times the arithmetic of
+ * fp4_gemm_panel_gelu's table lookup. Arguments as fp4_gemm_panel_gelu.
+ */
+FP4_API fp4_status fp4_gemm_panel_gelu_f32(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales,
+                                   int64_t m, int64_t n, int64_t k,
+                                   uint8_t* out_codes, uint8_t* out_scales, void* stream);
+
+/*
  * fp4_gemm_panel_euler -- the last block of the velocity network fused with
  * the Euler step that consumes it (aitrends summary, Stage-1 paragraph: a
  * 6-step FP4 ODE solve; the velocity is the residual stream plus the last

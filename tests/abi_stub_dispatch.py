@@ -38,6 +38,7 @@ CASES = [
     ("fp4_gemm", (1, P, 32, P3, 4, P, P2, 32, P3, 4, P2, 8, 8, 64, P, 1, 8, None, STREAM), "launch_gemm_nv"),
     ("fp4_gemm_panel", (0, P, P3, P2, P3, 8, 8, 64, P, 0, 8, P2, STREAM), "launch_gemm_mx_panel"),
     ("fp4_gemm_panel_gelu", (0, P, P3, P2, P3, 256, 512, 64, P, P3, STREAM), "launch_gemm_mx_panel_gelu"),
+    ("fp4_gemm_panel_gelu_f32", (0, P, P3, P2, P3, 256, 512, 64, P, P3, STREAM), "launch_gemm_mx_panel_gelu(exact)"),
     ("fp4_gemm_panel_euler", (0, P, P3, P2, P3, 8, 8, 64, P2, P3, P, 8, 1.0, 0.5, STREAM),
      "launch_gemm_mx_panel_euler"),
     ("fp4_gemm_panel_euler_reward", (0, P, P3, P2, P3, 256, 256, 64, P2, P3, P, 256, 1.0, 0.5, P2, 128, P3, P,

@@ -42,8 +42,8 @@ hipError_t launch_gemm_mx_panel(const uint8_t*, const uint8_t*, const uint8_t*, 
   return hit("launch_gemm_mx_panel");
 }
 hipError_t launch_gemm_mx_panel_gelu(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
-                                     int64_t, uint8_t*, uint8_t*, hipStream_t) {
-  return hit("launch_gemm_mx_panel_gelu");
+                                     int64_t, uint8_t*, uint8_t*, int exact, hipStream_t) {
+  return hit(exact ? "launch_gemm_mx_panel_gelu(exact)" : "launch_gemm_mx_panel_gelu");
 }
 hipError_t launch_gemm_mx_panel_euler(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t,
                                       int64_t, int64_t, const float*, const float*, float*, int64_t, float,

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(fq.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert fq.fp4_abi_version() == 109
+    assert fq.fp4_abi_version() == 110
 
 
 def test_status_strings(lib):
@@ -194,6 +194,20 @@ def test_gemm_panel_gelu_rejects(lib, kw):
 @pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=300), dict(n=128)])
 def test_gemm_panel_gelu_unsupported(lib, kw):
     assert gg(**kw) == fq.binding.UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=3), dict(a=None), dict(oc=None), dict(m=0), dict(k=48), dict(oc=P + 8)])
+def test_gemm_panel_gelu_f32_rejects(lib, kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=256, n=256, k=64, oc=P, os=P3, stream=None)
+    a.update(kw)
+    assert fq.fp4_gemm_panel_gelu_f32(*a.values()) == fq.binding.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=1), dict(m=300), dict(n=128)])
+def test_gemm_panel_gelu_f32_unsupported(lib, kw):
+    a = dict(fmt=0, a=P, a_s=P3, b=P2, b_s=P3, m=256, n=256, k=64, oc=P, os=P3, stream=None)
+    a.update(kw)
+    assert fq.fp4_gemm_panel_gelu_f32(*a.values()) == fq.binding.UNSUPPORTED
 
 
 def ql(**kw):

@@ -230,6 +230,29 @@ def test_gemm_gelu_equals_gemm_then_gelu_quantize(gpu_lib, m, n, k, wscale):
     np.testing.assert_array_equal(to_np(out.codes), to_np(ref.codes))
 
 
+@pytest.mark.parametrize("m,n,k,wscale", [(256, 256, 256, 1.0), (512, 768, 1024, 1.0), (768, 512, 3072, 1.0),
+                                          (512, 512, 416, 1.0), (256, 512, 3072, 10.0), (256, 256, 64, 0.001)])
+def test_gemm_gelu_f32_equals_f32_gemm_then_gelu_quantize(gpu_lib, m, n, k, wscale):
+    """fp4_gemm_panel_gelu_f32: GELU of the fp32 sums, bit-identical codes and
+    scales to the fp32 GEMM followed by the GELU quantizer (which evaluates
+    erfc on fp32 input), tails and tiny values included."""
+    qa = gpu_lib.quantize(dev(act(m, k, m + k)), "mx", layout="panel")
+    qb = gpu_lib.quantize(dev(wts(n, k, n + 1) * np.float32(wscale)), "mx", layout="panel")
+    z = gpu_lib.gemm(qa, qb, "f32", out=torch.empty((m, n), dtype=torch.float32, device=DEV))
+    ref = gpu_lib.quantize(z, "mx", prologue="gelu", layout="panel")
+    out = gpu_lib.gemm_gelu(qa, qb, exact=True)
+    np.testing.assert_array_equal(to_np(out.scales), to_np(ref.scales))
+    np.testing.assert_array_equal(to_np(out.codes), to_np(ref.codes))
+    # against the oracle: GELU of the exact product, codes equal except within the fp32 GEMM bound of a decision
+    # point (1e-4 S_abs through GELU's slope, at most 1.13) plus the 2e-6 evaluation band
+    ac, as_, _ = panel_to_rows(to_np(qa.codes), to_np(qa.scales), m, k)
+    bc, bs, _ = panel_to_rows(to_np(qb.codes), to_np(qb.scales), n, k)
+    c_exact, s_abs = ogemm.gemm_mx(ac, as_, bc, bs)
+    oc, osc, _ = panel_to_rows(to_np(out.codes), to_np(out.scales), m, n)
+    bad, flips = mx_codes_near_boundary_ok(orollout.gelu(c_exact), oc, osc, band=1.13 * 1e-4 * s_abs)
+    assert bad == 0, (bad, flips)
+
+
 def test_gemm_gelu_full_size_flux(gpu_lib):
     """The FLUX-class first linear (36864 x 3072 -> 12288) in the benchmark's
     launch configuration: fused and unfused outputs agree byte for byte."""
