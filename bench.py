@@ -248,6 +248,31 @@ def cpu_baseline(cfg, tokens_sample=512, w_rows_sample=1024, gemm_rows=512):
             "host": env}
 
 
+def cpu_quantizers_full(chunk_rows=4096):
+    """--cpu-full: the oracle's MXFP4 quantization of every class activation
+    in full (the rows in chunks, each chunk quantized by the oracle as it
+    stands; only the quantization is timed, not the draws)."""
+    from fp4_quantized_diffusion_amd import inputs
+    from oracle import mxfp4
+    out = {}
+    for name in ("flux", "sana", "sd35"):
+        cfg = inputs.CLASS_SHAPES[name]
+        for which in (1, 2):
+            _, k, _ = inputs.class_gemm(name, which)
+            m = cfg["m"]
+            rng = np.random.default_rng([cfg["seed"], which, 0])
+            t = 0.0
+            for r0 in range(0, m, chunk_rows):
+                a = inputs.activations(rng, min(chunk_rows, m - r0), k, cfg["act"])
+                t0 = time.perf_counter()
+                mxfp4.quantize(a)
+                t += time.perf_counter() - t0
+            key = f"mx_quantize_act_{name}_{m}x{k}"
+            out[key] = {"seconds": round(t, 2), "gb_per_s": round(m * k * 2.53125 / t / 1e9, 4)}
+            log(f"cpu oracle {key}: {t:.1f}s")
+    return out
+
+
 def time_launches(fns, reps=50, warm_ms=100.0):
     """Median / p10 / p90 (microseconds) of one launch, from a HIP event pair
     around each call on the current stream. fns: one callable per rotating
@@ -430,6 +455,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
     ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle's quantization of every class activation in full (minutes of CPU)")
     ap.add_argument("--no-stage2", action="store_true",
                     help="skip the Stage-2 block (BF16 regeneration of the selected seeds, FP4 step-count ablation)")
     ap.add_argument("--ablation", action="store_true",
@@ -568,6 +595,8 @@ def main():
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(cfg)
+        if args.cpu_full:
+            out["cpu_baseline"]["class_quantizers_full"] = cpu_quantizers_full()
         log(f"cpu baseline: {time.time() - t0:.1f}s")
     print(json.dumps(out), flush=True)
 
