@@ -38,9 +38,9 @@ PEAK_HBM = 8.0e12       # bytes/s
 # runs of this workload, averaged over a step's GEMM launches; valid only for
 # the kernel sources they were taken with (reported as null once those
 # change). See profiles/rollout_96x4096x3072_kernels.md.
-GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "ee7a2361324a772a", "gemm_common.h": "d8952e405ad1a5b1",
+GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "55d74820f7fa69cc", "gemm_common.h": "d8952e405ad1a5b1",
                             "mx_common.h": "f336665198c3bb5f"},
-                "bytes_per_launch": 20.44e9}
+                "bytes_per_launch": 19.20e9}
 
 
 def gemm_traffic():
