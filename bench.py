@@ -33,14 +33,18 @@ PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 
 # Bytes each GEMM launch moves between L2 and the memory fabric (Infinity
-# Cache or HBM), from rocprofv3 FETCH_SIZE (x2: every read request is
-# 128 bytes, which the counter's formula weighs as 64) and WRITE_SIZE (x1)
-# runs of this workload, averaged over a step's GEMM launches; valid only for
-# the kernel sources they were taken with (reported as null once those
+# Cache or HBM). By default they are measured in every run (measure_traffic:
+# two rocprofv3 counter passes over the rollout's GEMMs, in child processes,
+# before this process touches the GPU). Where that cannot run, the figure of
+# the committed profile is reported instead, from FETCH_SIZE (x2: every read
+# request is 128 bytes, which the counter's formula weighs as 64) and
+# WRITE_SIZE (x1) runs of this workload averaged over a step's GEMM launches;
+# it holds only for the kernel sources it was taken with (null once those
 # change). See profiles/rollout_96x4096x3072_kernels.md.
 GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "55d74820f7fa69cc", "gemm_common.h": "d8952e405ad1a5b1",
                             "mx_common.h": "f336665198c3bb5f"},
                 "bytes_per_launch": 19.20e9}
+COPY_BYTES = 1 << 30    # the known-size copy that calibrates the byte counters
 
 
 def gemm_traffic():
@@ -51,6 +55,136 @@ def gemm_traffic():
             if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
                 return None
     return GEMM_TRAFFIC["bytes_per_launch"]
+
+
+def gemm_variants(cfg):
+    """The rollout step's GEMM launches by epilogue: (kernel template, launches
+    per step). The first linear of every block quantizes GELU in its epilogue;
+    the second adds the residual, except in the last block, where it also takes
+    the Euler step, and in the last step also the reward partial sums."""
+    b, s = cfg["blocks"], cfg["steps"]
+    return {"gelu_mxfp4": ("gemm_fp4_kernel<0, 3, 2>", b * s), "residual": ("gemm_fp4_kernel<0, 1, 2>", (b - 1) * s),
+            "euler": ("gemm_fp4_kernel<0, 2, 2>", s - 1), "euler_reward": ("gemm_fp4_kernel<0, 4, 2>", 1)}
+
+
+def traffic_probe(cfg):
+    """The program measure_traffic runs under rocprofv3: one device copy of
+    COPY_BYTES, then one step of the benchmark's rollout (the same inputs,
+    buffers and launches as the timed steps)."""
+    import torch
+    import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
+    fq.load_library()
+    dev = "cuda:0"
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    noise, w1, w2, u = make_inputs(cfg, dev)
+    work = torch.empty_like(noise)
+    ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=cfg["n_cand"])
+    ro.run(noise, work)
+    torch.cuda.synchronize()
+    print("traffic probe: rollout step done", flush=True)
+
+
+def _under_profiler(env=None):
+    env = os.environ if env is None else env
+    return any(k.startswith(("ROCPROF", "ROCP_")) for k in env) or "rocprof" in env.get("LD_PRELOAD", "")
+
+
+def counter_kib(db, counter, variants):
+    """Per-dispatch values (KiB) of `counter` in a rocprofv3 results database,
+    grouped into the calibration copy and the GEMM variants; None when one of
+    them has no dispatch."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                           (counter,)).fetchall()
+    finally:
+        con.close()
+    kib = {"copy": []}
+    kib.update({name: [] for name in variants})
+    for kname, v in rows:
+        if "__amd_rocclr_copyBuffer" in kname:
+            kib["copy"].append(float(v))
+        for name, (tmpl, _) in variants.items():
+            if tmpl + "(" in kname or kname.endswith(tmpl):
+                kib[name].append(float(v))
+    return kib if all(kib.values()) else None
+
+
+def weighted_traffic(per, variants):
+    """Mean read + write bytes per launch over a step's GEMM launches."""
+    total = sum(n for _, n in variants.values())
+    return sum((per[k]["read_GB"] + per[k]["write_GB"]) * 1e9 * variants[k][1] for k in variants) / total
+
+
+def measure_traffic(cfg, timeout_s=420):
+    """Bytes per GEMM launch between L2 and the memory fabric, measured now:
+    two child processes run traffic_probe under `rocprofv3 --pmc FETCH_SIZE`
+    and then `--pmc WRITE_SIZE` (one counter block per run). Each counter is
+    scaled by what it reads for the COPY_BYTES copy in the same run. Returns
+    (dict, None) or (None, reason). Must run before this process initializes
+    the GPU, so the children start from a process with no GPU state."""
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None, "rocprofv3 not on PATH"
+    tmp = tempfile.mkdtemp(prefix="fp4r_traffic_")
+    env = dict(os.environ)
+    env.setdefault("TMPDIR", "/tmp")
+    variants = gemm_variants(cfg)
+    per = {name: {} for name in variants}
+    factors = {}
+    try:
+        for counter, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+            t0 = time.time()
+            out_name = counter.lower()
+            cmd = [prof, "--pmc", counter, "-d", tmp, "-o", out_name, "--", sys.executable,
+                   os.path.join(ROOT, "bench.py"), "--traffic-probe", "--tokens", str(cfg["tokens"])]
+            logf = os.path.join(tmp, out_name + ".log")
+            with open(logf, "w") as lf:
+                p = subprocess.Popen(cmd, stdout=lf, stderr=subprocess.STDOUT, cwd=tmp, env=env,
+                                     start_new_session=True)
+                try:
+                    rc = p.wait(timeout=timeout_s)
+                except subprocess.TimeoutExpired:
+                    os.killpg(p.pid, signal.SIGKILL)
+                    p.wait()
+                    return None, f"{counter} pass exceeded {timeout_s} s"
+            with open(logf, errors="replace") as lf:
+                text = lf.read()
+            db = os.path.join(tmp, out_name + "_results.db")
+            # rocprofv3 may end with a non-zero status after the program's own
+            # end; the results count when the probe finished and the file is there
+            if "traffic probe: rollout step done" not in text or not os.path.exists(db):
+                return None, f"{counter} pass failed (status {rc}): {text.strip().splitlines()[-1:] or ''}"
+            kib = counter_kib(db, counter, variants)
+            if kib is None or any(len(kib[n]) != variants[n][1] for n in variants):
+                return None, f"{counter} pass: the GEMM launches counted differ from one step's"
+            f = COPY_BYTES / (sum(kib["copy"]) * 1024.0)
+            # the copy reads and writes COPY_BYTES: FETCH_SIZE counts 128-byte reads as 64 (x2), WRITE_SIZE x1
+            if not (1.6 < f < 2.4 if key == "read" else 0.8 < f < 1.2):
+                return None, f"{counter} copy calibration factor {f:.3f} is outside its expected range"
+            factors[key] = round(f, 4)
+            for name in variants:
+                gb = [v * 1024.0 * f / 1e9 for v in kib[name]]
+                per[name][key + "_GB"] = round(sum(gb) / len(gb), 3)
+                per[name][key + "_GB_range"] = [round(min(gb), 3), round(max(gb), 3)]
+                per[name]["launches_counted"] = len(gb)
+            log(f"traffic pass {counter}: {time.time() - t0:.1f}s")
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    mean = weighted_traffic(per, variants)
+    for n in variants:
+        per[n]["launches_per_step"] = variants[n][1]
+    return {"bytes_per_launch": mean, "by_variant": per, "counter_factors": factors}, None
 
 
 def log(*a):
@@ -465,23 +599,53 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
+    ap.add_argument("--no-traffic", action="store_true",
+                    help="skip the live GEMM byte-counter passes (roofline.traffic then comes from the profile)")
+    ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.traffic_probe:
+        from fp4_quantized_diffusion_amd.inputs import ROLLOUT
+        traffic_probe(dict(ROLLOUT, tokens=args.tokens))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the rollout shards over candidates "
               "with no cross-GPU traffic besides a 384-byte reward exchange, which this build does not run.",
               file=sys.stderr)
         sys.exit(2)
 
+    from fp4_quantized_diffusion_amd.inputs import ROLLOUT
+    cfg = dict(ROLLOUT)
+    cfg["tokens"] = args.tokens
+    chunk = args.chunk or cfg["n_cand"]
+    default_workload = args.layout == "panel" and not args.overlap and args.tokens == 4096 and chunk == cfg["n_cand"]
+    # the byte counters first, while this process has no GPU state
+    traffic, traffic_src = None, None
+    if default_workload:
+        if args.no_traffic or _under_profiler():
+            why = "--no-traffic" if args.no_traffic else "this run is itself profiled"
+        else:
+            t0 = time.time()
+            measured, why = measure_traffic(cfg)
+            log(f"GEMM byte counters: {time.time() - t0:.1f}s" + (f" (not measured: {why})" if why else ""))
+            if measured is not None:
+                traffic = measured["bytes_per_launch"]
+                traffic_src = {"source": "measured in this run: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, "
+                                         "each in a child process over one step of this rollout (all its GEMM "
+                                         "launches); factors from a 1 GiB device copy in the same runs",
+                               **measured}
+                traffic_src.pop("bytes_per_launch")
+        if traffic is None:
+            traffic = gemm_traffic()
+            traffic_src = {"source": "profile (profiles/rollout_96x4096x3072_kernels.md)" if traffic is not None
+                           else "none: the GEMM sources changed since the profile's counters",
+                           "not_measured": why}
+
     import torch
     import fp4_quantized_diffusion_amd as fq
-    from fp4_quantized_diffusion_amd.inputs import ROLLOUT
     from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
 
     fq.load_library()
     dev = "cuda:0"
-    cfg = dict(ROLLOUT)
-    cfg["tokens"] = args.tokens
-    chunk = args.chunk or cfg["n_cand"]
     noise, w1, w2, u = make_inputs(cfg, dev)
     work = torch.empty_like(noise)
     timer = EventTimer()
@@ -521,8 +685,6 @@ def main():
     achieved = gemm_flop / (gemm_ms * 1e-3)
     kernels = {k: {"launches_per_step": n // args.steps, "avg_us": round(ms * 1e3, 2)} for k, (n, ms) in ks.items()}
 
-    default_workload = args.layout == "panel" and not args.overlap and args.tokens == 4096 and chunk == cfg["n_cand"]
-    traffic = gemm_traffic() if default_workload else None
     out = {
         "metric": METRIC,
         "value": round(cfg["n_cand"] / sec, 4),
@@ -547,6 +709,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4, 4),
                      "traffic": None if traffic is None else round(traffic / 1e9, 2),
                      "traffic_unit": "GB per launch (L2 <-> fabric reads + writes, rocprofv3 counters)",
+                     "traffic_detail": traffic_src,
                      "kernel": f"gemm_fp4_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate; "
                                + ("the first linear's launches quantize GELU(bf16(C)) to MXFP4 in their epilogue, "
                                   "the second's add the residual, the last block's also apply the Euler step)"
