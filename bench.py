@@ -33,9 +33,9 @@ PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 
 # Bytes each GEMM launch moves between L2 and the memory fabric (Infinity
-# Cache or HBM). By default they are measured in every run (measure_traffic:
-# two rocprofv3 counter passes over the rollout's GEMMs, in child processes,
-# before this process touches the GPU). Where that cannot run, the figure of
+# Cache or HBM). By default they are measured in every run (measure_counters:
+# rocprofv3 counter passes over one rollout step, in child processes, before
+# this process touches the GPU). Where that cannot run, the figure of
 # the committed profile is reported instead, from FETCH_SIZE (x2: every read
 # request is 128 bytes, which the counter's formula weighs as 64) and
 # WRITE_SIZE (x1) runs of this workload averaged over a step's GEMM launches;
@@ -68,7 +68,7 @@ def gemm_variants(cfg):
 
 
 def traffic_probe(cfg):
-    """The program measure_traffic runs under rocprofv3: one device copy of
+    """The program measure_counters runs under rocprofv3: one device copy of
     COPY_BYTES, then one step of the benchmark's rollout (the same inputs,
     buffers and launches as the timed steps)."""
     import torch
@@ -94,26 +94,41 @@ def _under_profiler(env=None):
     return any(k.startswith(("ROCPROF", "ROCP_")) for k in env) or "rocprof" in env.get("LD_PRELOAD", "")
 
 
-def counter_kib(db, counter, variants):
-    """Per-dispatch values (KiB) of `counter` in a rocprofv3 results database,
-    grouped into the calibration copy and the GEMM variants; None when one of
-    them has no dispatch."""
+# The counter passes, one rocprofv3 run each (each within one pass's limits per
+# counter block): bytes read and written past L2, then MFMA busy cycles and
+# GPU-active cycles (the shader clock over each dispatch's duration).
+COUNTER_PASSES = (("FETCH_SIZE",), ("WRITE_SIZE",), ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+N_XCD, N_SIMD = 8, 1024   # GRBM_GUI_ACTIVE sums the 8 XCDs; MFMA busy cycles sum 256 CUs x 4 SIMDs
+
+
+def counter_dispatches(db, counters, variants):
+    """The dispatches of a rocprofv3 results database, grouped into the
+    calibration copy ("copy") and the GEMM variants: lists of (duration ns,
+    {counter: value}). None when one group has no dispatch."""
     import sqlite3
     con = sqlite3.connect(db)
     try:
-        rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?",
-                           (counter,)).fetchall()
+        rows = con.execute("select dispatch_id, kernel_name, counter_name, value, start, end "
+                           "from counters_collection").fetchall()
     finally:
         con.close()
-    kib = {"copy": []}
-    kib.update({name: [] for name in variants})
-    for kname, v in rows:
+    disp = {}
+    for did, kname, cname, v, t0, t1 in rows:
+        if cname in counters:
+            d = disp.setdefault(did, [kname, (t1 - t0) if t0 is not None and t1 is not None else None, {}])
+            d[2][cname] = float(v)
+    groups = {"copy": []}
+    groups.update({name: [] for name in variants})
+    for did in sorted(disp):
+        kname, dur, vals = disp[did]
+        if len(vals) != len(counters):
+            continue
         if "__amd_rocclr_copyBuffer" in kname:
-            kib["copy"].append(float(v))
+            groups["copy"].append((dur, vals))
         for name, (tmpl, _) in variants.items():
             if tmpl + "(" in kname or kname.endswith(tmpl):
-                kib[name].append(float(v))
-    return kib if all(kib.values()) else None
+                groups[name].append((dur, vals))
+    return groups if all(groups.values()) else None
 
 
 def weighted_traffic(per, variants):
@@ -122,13 +137,25 @@ def weighted_traffic(per, variants):
     return sum((per[k]["read_GB"] + per[k]["write_GB"]) * 1e9 * variants[k][1] for k in variants) / total
 
 
-def measure_traffic(cfg, timeout_s=420):
-    """Bytes per GEMM launch between L2 and the memory fabric, measured now:
-    two child processes run traffic_probe under `rocprofv3 --pmc FETCH_SIZE`
-    and then `--pmc WRITE_SIZE` (one counter block per run). Each counter is
-    scaled by what it reads for the COPY_BYTES copy in the same run. Returns
-    (dict, None) or (None, reason). Must run before this process initializes
-    the GPU, so the children start from a process with no GPU state."""
+def clock_stats(disps):
+    """Shader clock (GHz) and MFMA busy fraction over dispatches of the clock
+    pass: GPU-active cycles of one XCD over the dispatches' time, and MFMA busy
+    cycles per SIMD over those cycles."""
+    cyc = sum(v["GRBM_GUI_ACTIVE"] for _, v in disps) / N_XCD
+    ns = sum(d for d, _ in disps)
+    busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for _, v in disps) / (cyc * N_SIMD)
+    return cyc / ns, busy
+
+
+def measure_counters(cfg, timeout_s=420):
+    """Counters of the rollout's GEMMs, taken now: child processes run
+    traffic_probe under `rocprofv3 --pmc <counters>`, one run per entry of
+    COUNTER_PASSES. Gives the bytes per launch between L2 and the memory
+    fabric (each byte counter scaled by what it reads for the COPY_BYTES copy
+    in the same run), and each variant's shader clock and MFMA busy fraction.
+    Returns (dict, None) or (None, reason). Must run before this process
+    initializes the GPU, so the children start from a process with no GPU
+    state."""
     import shutil
     import signal
     import subprocess
@@ -136,17 +163,19 @@ def measure_traffic(cfg, timeout_s=420):
     prof = shutil.which("rocprofv3")
     if prof is None:
         return None, "rocprofv3 not on PATH"
-    tmp = tempfile.mkdtemp(prefix="fp4r_traffic_")
+    tmp = tempfile.mkdtemp(prefix="fp4r_counters_")
     env = dict(os.environ)
     env.setdefault("TMPDIR", "/tmp")
     variants = gemm_variants(cfg)
     per = {name: {} for name in variants}
     factors = {}
+    all_disp = []
     try:
-        for counter, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        for i, counters in enumerate(COUNTER_PASSES):
             t0 = time.time()
-            out_name = counter.lower()
-            cmd = [prof, "--pmc", counter, "-d", tmp, "-o", out_name, "--", sys.executable,
+            tag = "+".join(counters)
+            out_name = f"pass{i}"
+            cmd = [prof, "--pmc", *counters, "-d", tmp, "-o", out_name, "--", sys.executable,
                    os.path.join(ROOT, "bench.py"), "--traffic-probe", "--tokens", str(cfg["tokens"])]
             logf = os.path.join(tmp, out_name + ".log")
             with open(logf, "w") as lf:
@@ -157,34 +186,45 @@ def measure_traffic(cfg, timeout_s=420):
                 except subprocess.TimeoutExpired:
                     os.killpg(p.pid, signal.SIGKILL)
                     p.wait()
-                    return None, f"{counter} pass exceeded {timeout_s} s"
+                    return None, f"{tag} pass exceeded {timeout_s} s"
             with open(logf, errors="replace") as lf:
                 text = lf.read()
             db = os.path.join(tmp, out_name + "_results.db")
             # rocprofv3 may end with a non-zero status after the program's own
             # end; the results count when the probe finished and the file is there
             if "traffic probe: rollout step done" not in text or not os.path.exists(db):
-                return None, f"{counter} pass failed (status {rc}): {text.strip().splitlines()[-1:] or ''}"
-            kib = counter_kib(db, counter, variants)
-            if kib is None or any(len(kib[n]) != variants[n][1] for n in variants):
-                return None, f"{counter} pass: the GEMM launches counted differ from one step's"
-            f = COPY_BYTES / (sum(kib["copy"]) * 1024.0)
-            # the copy reads and writes COPY_BYTES: FETCH_SIZE counts 128-byte reads as 64 (x2), WRITE_SIZE x1
-            if not (1.6 < f < 2.4 if key == "read" else 0.8 < f < 1.2):
-                return None, f"{counter} copy calibration factor {f:.3f} is outside its expected range"
-            factors[key] = round(f, 4)
-            for name in variants:
-                gb = [v * 1024.0 * f / 1e9 for v in kib[name]]
-                per[name][key + "_GB"] = round(sum(gb) / len(gb), 3)
-                per[name][key + "_GB_range"] = [round(min(gb), 3), round(max(gb), 3)]
-                per[name]["launches_counted"] = len(gb)
-            log(f"traffic pass {counter}: {time.time() - t0:.1f}s")
+                return None, f"{tag} pass failed (status {rc}): {text.strip().splitlines()[-1:]}"
+            g = counter_dispatches(db, counters, variants)
+            if g is None or any(len(g[n]) != variants[n][1] for n in variants):
+                return None, f"{tag} pass: the GEMM launches counted differ from one step's"
+            if counters[0] in ("FETCH_SIZE", "WRITE_SIZE"):
+                c = counters[0]
+                key = "read" if c == "FETCH_SIZE" else "write"
+                f = COPY_BYTES / (sum(v[c] for _, v in g["copy"]) * 1024.0)
+                # the copy reads and writes COPY_BYTES: FETCH_SIZE counts 128-byte reads as 64 (x2), WRITE_SIZE x1
+                if not (1.6 < f < 2.4 if key == "read" else 0.8 < f < 1.2):
+                    return None, f"{c} copy calibration factor {f:.3f} is outside its expected range"
+                factors[key] = round(f, 4)
+                for name in variants:
+                    gb = [v[c] * 1024.0 * f / 1e9 for _, v in g[name]]
+                    per[name][key + "_GB"] = round(sum(gb) / len(gb), 3)
+                    per[name][key + "_GB_range"] = [round(min(gb), 3), round(max(gb), 3)]
+            else:
+                if any(d is None or d <= 0 for name in variants for d, _ in g[name]):
+                    return None, "clock pass: dispatches without timestamps"
+                for name in variants:
+                    clk, busy = clock_stats(g[name])
+                    per[name]["sclk_GHz"] = round(clk, 3)
+                    per[name]["mfma_busy"] = round(busy, 4)
+                    all_disp += g[name]
+            log(f"counter pass {tag}: {time.time() - t0:.1f}s")
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    mean = weighted_traffic(per, variants)
     for n in variants:
         per[n]["launches_per_step"] = variants[n][1]
-    return {"bytes_per_launch": mean, "by_variant": per, "counter_factors": factors}, None
+    clk, busy = clock_stats(all_disp)
+    return {"bytes_per_launch": weighted_traffic(per, variants), "by_variant": per, "counter_factors": factors,
+            "sclk_GHz": round(clk, 3), "mfma_busy": round(busy, 4)}, None
 
 
 def log(*a):
@@ -618,23 +658,23 @@ def main():
     cfg["tokens"] = args.tokens
     chunk = args.chunk or cfg["n_cand"]
     default_workload = args.layout == "panel" and not args.overlap and args.tokens == 4096 and chunk == cfg["n_cand"]
-    # the byte counters first, while this process has no GPU state
-    traffic, traffic_src = None, None
+    # the counters first, while this process has no GPU state
+    traffic, counters, traffic_src = None, None, None
     if default_workload:
         if args.no_traffic or _under_profiler():
             why = "--no-traffic" if args.no_traffic else "this run is itself profiled"
         else:
             t0 = time.time()
-            measured, why = measure_traffic(cfg)
-            log(f"GEMM byte counters: {time.time() - t0:.1f}s" + (f" (not measured: {why})" if why else ""))
-            if measured is not None:
-                traffic = measured["bytes_per_launch"]
-                traffic_src = {"source": "measured in this run: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, "
-                                         "each in a child process over one step of this rollout (all its GEMM "
-                                         "launches); factors from a 1 GiB device copy in the same runs",
-                               **measured}
-                traffic_src.pop("bytes_per_launch")
-        if traffic is None:
+            counters, why = measure_counters(cfg)
+            log(f"GEMM counters: {time.time() - t0:.1f}s" + (f" (not measured: {why})" if why else ""))
+        if counters is not None:
+            traffic = counters["bytes_per_launch"]
+            traffic_src = {"source": "measured in this run: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, "
+                                     "then --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE, each in a child "
+                                     "process over one step of this rollout (all its GEMM launches); byte "
+                                     "factors from a 1 GiB device copy in the same runs",
+                           "by_variant": counters["by_variant"], "counter_factors": counters["counter_factors"]}
+        else:
             traffic = gemm_traffic()
             traffic_src = {"source": "profile (profiles/rollout_96x4096x3072_kernels.md)" if traffic is not None
                            else "none: the GEMM sources changed since the profile's counters",
@@ -719,6 +759,11 @@ def main():
         "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),
         "kernels": kernels,
     }
+    if counters is not None:
+        # the spec peak scaled to the shader clock the GEMMs ran at (counter pass of this run)
+        out["roofline"]["sclk_GHz"] = counters["sclk_GHz"]
+        out["roofline"]["mfma_busy"] = counters["mfma_busy"]
+        out["roofline"]["frac_of_clock_adjusted_peak"] = round(achieved / (PEAK_FP4 * counters["sclk_GHz"] / 2.4), 4)
     if not args.no_class_gemms:
         t0 = time.time()
         out["class_gemms"], out["memory_kernels"] = class_benchmarks(dev)

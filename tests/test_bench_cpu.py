@@ -1,6 +1,7 @@
-"""Host logic of bench.py's live byte-counter measurement: the grouping of a
-rocprofv3 results database's counter records, the copy calibration, the
-launch-weighted mean, and the refusal paths (no profiler, nested profiling)."""
+"""Host logic of bench.py's live counter measurement: the grouping of a
+rocprofv3 results database's counter records by dispatch, the
+launch-weighted mean of the byte counts, the clock and MFMA-busy arithmetic,
+and the refusal paths (no profiler, nested profiling)."""
 import importlib.util
 import os
 import sqlite3
@@ -30,9 +31,11 @@ def test_variants_cover_every_gemm_launch_of_a_step(bench):
 
 
 def _db(path, rows):
+    """rows: (dispatch_id, kernel_name, counter_name, value, start, end)"""
     con = sqlite3.connect(path)
-    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
-    con.executemany("insert into counters_collection values (?, ?, ?)", rows)
+    con.execute("create table counters_collection (dispatch_id integer, kernel_name text, counter_name text, "
+                "value real, start integer, end integer)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
     con.commit()
     con.close()
 
@@ -43,28 +46,61 @@ def _name(tmpl):
 
 def test_counter_records_are_grouped_by_kernel(bench, tmp_path):
     v = bench.gemm_variants(CFG)
-    rows = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 262144.0), ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 262144.0),
-            ("__amd_rocclr_copyBuffer", "WRITE_SIZE", 999.0),           # another counter: ignored
-            ("void quant_mx_rmsnorm_wave_kernel<0, 6, true>(float const*)", "FETCH_SIZE", 5.0)]
+    rows = [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 262144.0, 0, 10),
+            (2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 262144.0, 10, 20),
+            (2, "__amd_rocclr_copyBuffer", "SQ_WAVES", 999.0, 10, 20),            # another counter: ignored
+            (3, "void quant_mx_rmsnorm_wave_kernel<0, 6, true>(float const*)", "FETCH_SIZE", 5.0, 20, 30)]
+    did = 10
     for i, (tmpl, _) in enumerate(v.values()):
-        rows += [(_name(tmpl), "FETCH_SIZE", 1000.0 * (i + 1)), (_name(tmpl), "FETCH_SIZE", 1000.0 * (i + 1) + 2)]
+        for j in range(2):
+            rows.append((did, _name(tmpl), "FETCH_SIZE", 1000.0 * (i + 1) + 2 * j, 100 * did, 100 * did + 7 + j))
+            did += 1
     # a kernel whose template arguments extend another's must not be taken for it
-    rows.append((_name("gemm_fp4_kernel<0, 3, 2, 1>"), "FETCH_SIZE", 7.0))
+    rows.append((99, _name("gemm_fp4_kernel<0, 3, 2, 1>"), "FETCH_SIZE", 7.0, 0, 1))
     db = str(tmp_path / "f.db")
     _db(db, rows)
-    kib = bench.counter_kib(db, "FETCH_SIZE", v)
-    assert kib["copy"] == [262144.0, 262144.0]
+    g = bench.counter_dispatches(db, ("FETCH_SIZE",), v)
+    assert g["copy"] == [(10, {"FETCH_SIZE": 262144.0}), (10, {"FETCH_SIZE": 262144.0})]
     for i, name in enumerate(v):
-        assert kib[name] == [1000.0 * (i + 1), 1000.0 * (i + 1) + 2]
+        assert g[name] == [(7, {"FETCH_SIZE": 1000.0 * (i + 1)}), (8, {"FETCH_SIZE": 1000.0 * (i + 1) + 2})]
+
+
+def test_two_counters_of_one_dispatch_are_joined(bench, tmp_path):
+    v = bench.gemm_variants(CFG)
+    c = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    rows = [(1, "__amd_rocclr_copyBuffer", c[0], 1.0, 0, 5), (1, "__amd_rocclr_copyBuffer", c[1], 2.0, 0, 5)]
+    did = 2
+    for tmpl, _ in v.values():
+        rows += [(did, _name(tmpl), c[0], 3.0 * did, 0, 9), (did, _name(tmpl), c[1], 5.0 * did, 0, 9)]
+        did += 1
+    rows.append((50, _name("gemm_fp4_kernel<0, 1, 2>"), c[0], 1.0, 0, 9))   # one counter missing: dropped
+    db = str(tmp_path / "c.db")
+    _db(db, rows)
+    g = bench.counter_dispatches(db, c, v)
+    for k, name in enumerate(v):
+        d = k + 2
+        assert g[name] == [(9, {c[0]: 3.0 * d, c[1]: 5.0 * d})]
 
 
 def test_a_missing_variant_fails_the_pass(bench, tmp_path):
     v = bench.gemm_variants(CFG)
-    rows = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 1.0)]
-    rows += [(_name(t), "FETCH_SIZE", 1.0) for name, (t, _) in v.items() if name != "euler"]
+    rows = [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 1.0, 0, 1)]
+    rows += [(i + 2, _name(t), "FETCH_SIZE", 1.0, 0, 1) for i, (name, (t, _)) in enumerate(v.items())
+             if name != "euler"]
     db = str(tmp_path / "g.db")
     _db(db, rows)
-    assert bench.counter_kib(db, "FETCH_SIZE", v) is None
+    assert bench.counter_dispatches(db, ("FETCH_SIZE",), v) is None
+
+
+def test_clock_and_mfma_busy(bench):
+    # 8 XCDs of 2e9 active cycles each over 1 s: 2 GHz; MFMA busy on half the
+    # 1024 SIMDs' cycles: 0.5. A second dispatch at 1 GHz and busy 0.25 weighs by
+    # its cycles and time.
+    d1 = (1e9, {"GRBM_GUI_ACTIVE": 8 * 2e9, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 2e9 * 1024})
+    assert bench.clock_stats([d1]) == pytest.approx((2.0, 0.5))
+    d2 = (1e9, {"GRBM_GUI_ACTIVE": 8 * 1e9, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1e9 * 1024})
+    clk, busy = bench.clock_stats([d1, d2])
+    assert clk == pytest.approx(1.5) and busy == pytest.approx((0.5 * 2 + 0.25 * 1) / 3)
 
 
 def test_weighted_mean_per_launch(bench):
@@ -77,7 +113,7 @@ def test_weighted_mean_per_launch(bench):
 
 def test_no_profiler_on_path_is_reported_not_raised(bench, monkeypatch, tmp_path):
     monkeypatch.setenv("PATH", str(tmp_path))
-    res, why = bench.measure_traffic(CFG)
+    res, why = bench.measure_counters(CFG)
     assert res is None and "rocprofv3" in why
 
 
