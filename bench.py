@@ -67,12 +67,36 @@ def gemm_variants(cfg):
             "euler": ("gemm_fp4_kernel<0, 2, 2>", s - 1), "euler_reward": ("gemm_fp4_kernel<0, 4, 2>", 1)}
 
 
+CLASS_NAMES = ("flux", "sana", "sd35")
+CLASS_TMPL = "gemm_fp4_kernel<1, 0, 2>"   # bf16 C, panel operands: the class GEMMs (the rollout never uses it)
+PROBE_CLASS_LAUNCHES = 2
+
+
+def class_key(name, which, m, k, n):
+    from fp4_quantized_diffusion_amd import inputs
+    return f"{name}_{inputs.class_gemm(name, which)[0]}_{m}x{k}x{n}"
+
+
+def class_shapes():
+    """[(key, m, k, n)] of the class GEMMs, in the order the probe launches them."""
+    from fp4_quantized_diffusion_amd import inputs
+    out = []
+    for name in CLASS_NAMES:
+        for which in (1, 2):
+            _, k, n = inputs.class_gemm(name, which)
+            m = inputs.CLASS_SHAPES[name]["m"]
+            out.append((class_key(name, which, m, k, n), m, k, n))
+    return out
+
+
 def traffic_probe(cfg):
     """The program measure_counters runs under rocprofv3: one device copy of
-    COPY_BYTES, then one step of the benchmark's rollout (the same inputs,
-    buffers and launches as the timed steps)."""
+    COPY_BYTES, one step of the benchmark's rollout (the same inputs, buffers
+    and launches as the timed steps), then PROBE_CLASS_LAUNCHES launches of
+    each class GEMM (MXFP4, bf16 C) in class_shapes() order."""
     import torch
     import fp4_quantized_diffusion_amd as fq
+    from fp4_quantized_diffusion_amd import inputs
     from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
     fq.load_library()
     dev = "cuda:0"
@@ -86,7 +110,19 @@ def traffic_probe(cfg):
     ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=cfg["n_cand"])
     ro.run(noise, work)
     torch.cuda.synchronize()
-    print("traffic probe: rollout step done", flush=True)
+    print("counter probe: rollout step done", flush=True)
+    del ro, noise, work, w1, w2
+    torch.cuda.empty_cache()
+    for name in CLASS_NAMES:
+        for which in (1, 2):
+            a, w = inputs.class_linear_device(name, which, dev)
+            qa, qb = fq.quantize(a, "mx", layout="panel"), fq.quantize(w, "mx", layout="panel")
+            c = torch.empty((a.shape[0], w.shape[0]), dtype=torch.bfloat16, device=dev)
+            for _ in range(PROBE_CLASS_LAUNCHES):
+                fq.gemm(qa, qb, "bf16", out=c)
+            torch.cuda.synchronize()
+            del a, w, qa, qb, c
+    print("counter probe: done", flush=True)
 
 
 def _under_profiler(env=None):
@@ -103,8 +139,10 @@ N_XCD, N_SIMD = 8, 1024   # GRBM_GUI_ACTIVE sums the 8 XCDs; MFMA busy cycles su
 
 def counter_dispatches(db, counters, variants):
     """The dispatches of a rocprofv3 results database, grouped into the
-    calibration copy ("copy") and the GEMM variants: lists of (duration ns,
-    {counter: value}). None when one group has no dispatch."""
+    calibration copy ("copy": device copies dispatched before the rollout's
+    first GEMM), the rollout's GEMM variants and the class GEMMs ("class", in
+    dispatch order): lists of (duration ns, {counter: value}). None when the
+    copy or a variant has no dispatch."""
     import sqlite3
     con = sqlite3.connect(db)
     try:
@@ -117,18 +155,29 @@ def counter_dispatches(db, counters, variants):
         if cname in counters:
             d = disp.setdefault(did, [kname, (t1 - t0) if t0 is not None and t1 is not None else None, {}])
             d[2][cname] = float(v)
-    groups = {"copy": []}
-    groups.update({name: [] for name in variants})
+    def is_(kname, tmpl):
+        return tmpl + "(" in kname or kname.endswith(tmpl)
+    groups = {name: [] for name in variants}
+    copies, cls, first_gemm = [], [], None
     for did in sorted(disp):
         kname, dur, vals = disp[did]
         if len(vals) != len(counters):
             continue
         if "__amd_rocclr_copyBuffer" in kname:
-            groups["copy"].append((dur, vals))
+            copies.append((did, dur, vals))
         for name, (tmpl, _) in variants.items():
-            if tmpl + "(" in kname or kname.endswith(tmpl):
+            if is_(kname, tmpl):
                 groups[name].append((dur, vals))
-    return groups if all(groups.values()) else None
+                first_gemm = did if first_gemm is None else first_gemm
+        if is_(kname, CLASS_TMPL):
+            cls.append((dur, vals))
+    # the calibration copy runs before anything else copies on the device;
+    # later copies (input generation) are not it
+    groups["copy"] = [(dur, vals) for did, dur, vals in copies if first_gemm is None or did < first_gemm]
+    if not all(groups.values()):
+        return None
+    groups["class"] = cls
+    return groups
 
 
 def weighted_traffic(per, variants):
@@ -145,6 +194,14 @@ def clock_stats(disps):
     ns = sum(d for d, _ in disps)
     busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for _, v in disps) / (cyc * N_SIMD)
     return cyc / ns, busy
+
+
+def class_groups(disps, shapes, per_shape=PROBE_CLASS_LAUNCHES):
+    """Pairs (key, dispatches) of the class GEMMs from their dispatches in
+    launch order; none unless every shape has its launches."""
+    if len(disps) != per_shape * len(shapes):
+        return []
+    return [(key, disps[i * per_shape:(i + 1) * per_shape]) for i, (key, _, _, _) in enumerate(shapes)]
 
 
 def measure_counters(cfg, timeout_s=420):
@@ -167,7 +224,9 @@ def measure_counters(cfg, timeout_s=420):
     env = dict(os.environ)
     env.setdefault("TMPDIR", "/tmp")
     variants = gemm_variants(cfg)
+    shapes = class_shapes()
     per = {name: {} for name in variants}
+    per_class = {}
     factors = {}
     all_disp = []
     try:
@@ -192,7 +251,7 @@ def measure_counters(cfg, timeout_s=420):
             db = os.path.join(tmp, out_name + "_results.db")
             # rocprofv3 may end with a non-zero status after the program's own
             # end; the results count when the probe finished and the file is there
-            if "traffic probe: rollout step done" not in text or not os.path.exists(db):
+            if "counter probe: rollout step done" not in text or not os.path.exists(db):
                 return None, f"{tag} pass failed (status {rc}): {text.strip().splitlines()[-1:]}"
             g = counter_dispatches(db, counters, variants)
             if g is None or any(len(g[n]) != variants[n][1] for n in variants):
@@ -209,6 +268,9 @@ def measure_counters(cfg, timeout_s=420):
                     gb = [v[c] * 1024.0 * f / 1e9 for _, v in g[name]]
                     per[name][key + "_GB"] = round(sum(gb) / len(gb), 3)
                     per[name][key + "_GB_range"] = [round(min(gb), 3), round(max(gb), 3)]
+                for ck, ds in class_groups(g["class"], shapes):
+                    per_class.setdefault(ck, {})[key + "_GB"] = round(
+                        sum(v[c] for _, v in ds) / len(ds) * 1024.0 * f / 1e9, 3)
             else:
                 if any(d is None or d <= 0 for name in variants for d, _ in g[name]):
                     return None, "clock pass: dispatches without timestamps"
@@ -217,6 +279,10 @@ def measure_counters(cfg, timeout_s=420):
                     per[name]["sclk_GHz"] = round(clk, 3)
                     per[name]["mfma_busy"] = round(busy, 4)
                     all_disp += g[name]
+                for ck, ds in class_groups(g["class"], shapes):
+                    if all(d is not None and d > 0 for d, _ in ds):
+                        clk, busy = clock_stats(ds)
+                        per_class.setdefault(ck, {}).update(sclk_GHz=round(clk, 3), mfma_busy=round(busy, 4))
             log(f"counter pass {tag}: {time.time() - t0:.1f}s")
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
@@ -224,7 +290,7 @@ def measure_counters(cfg, timeout_s=420):
         per[n]["launches_per_step"] = variants[n][1]
     clk, busy = clock_stats(all_disp)
     return {"bytes_per_launch": weighted_traffic(per, variants), "by_variant": per, "counter_factors": factors,
-            "sclk_GHz": round(clk, 3), "mfma_busy": round(busy, 4)}, None
+            "sclk_GHz": round(clk, 3), "mfma_busy": round(busy, 4), "class_gemms": per_class}, None
 
 
 def log(*a):
@@ -490,7 +556,7 @@ def class_benchmarks(dev, n_sets=4):
         return {"tflops": round(flop / us / 1e6, 1), "frac_of_peak": round(flop / us / 1e-6 / peak, 4)}
 
     gemms, mem = {}, {}
-    for name in ("flux", "sana", "sd35"):
+    for name in CLASS_NAMES:
         for which in (1, 2):
             t0 = time.time()
             draws = [inputs.class_linear_device(name, which, dev, draw=d) for d in range(n_sets)]
@@ -500,7 +566,7 @@ def class_benchmarks(dev, n_sets=4):
             qb = [fq.quantize(w, "mx", layout="panel") for _, w in draws]
             c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             flop = 2.0 * m * n * k
-            key = f"{name}_{inputs.class_gemm(name, which)[0]}_{m}x{k}x{n}"
+            key = class_key(name, which, m, k, n)
             f_us = time_launches([lambda i=i: fq.gemm(qa[i], qb[i], "bf16", out=c) for i in range(n_sets)])
             b_us = time_launches([lambda i=i: F.linear(draws[i][0], draws[i][1]) for i in range(n_sets)])
             g = {"m": m, "k": k, "n": n,
@@ -671,8 +737,9 @@ def main():
             traffic = counters["bytes_per_launch"]
             traffic_src = {"source": "measured in this run: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, "
                                      "then --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE, each in a child "
-                                     "process over one step of this rollout (all its GEMM launches); byte "
-                                     "factors from a 1 GiB device copy in the same runs",
+                                     "process over one step of this rollout (all its GEMM launches) and two "
+                                     "launches of each class GEMM; byte factors from a 1 GiB device copy in "
+                                     "the same runs",
                            "by_variant": counters["by_variant"], "counter_factors": counters["counter_factors"]}
         else:
             traffic = gemm_traffic()
@@ -767,6 +834,18 @@ def main():
     if not args.no_class_gemms:
         t0 = time.time()
         out["class_gemms"], out["memory_kernels"] = class_benchmarks(dev)
+        if counters is not None:
+            for key, m, k, n in class_shapes():
+                g, cs = out["class_gemms"].get(key), counters["class_gemms"].get(key, {})
+                if g is None or "sclk_GHz" not in cs:
+                    continue
+                # operands' codes and scales read once, bf16 C written once
+                alg = (m + n) * k * (0.5 + 1 / 32) + 2.0 * m * n
+                g.update({"sclk_GHz": cs["sclk_GHz"], "mfma_busy": cs["mfma_busy"],
+                          "mxfp4_frac_of_clock_adjusted_peak": round(
+                              g["mxfp4_tflops"] * 1e12 / (PEAK_FP4 * cs["sclk_GHz"] / 2.4), 4),
+                          "read_GB": cs.get("read_GB"), "write_GB": cs.get("write_GB"),
+                          "algorithmic_GB": round(alg / 1e9, 3)})
         log(f"class benchmarks: {time.time() - t0:.1f}s")
     if not args.no_step_kernels:
         # after the rollout's outputs are read: the Euler timing overwrites `work`

@@ -57,6 +57,8 @@ def test_counter_records_are_grouped_by_kernel(bench, tmp_path):
             did += 1
     # a kernel whose template arguments extend another's must not be taken for it
     rows.append((99, _name("gemm_fp4_kernel<0, 3, 2, 1>"), "FETCH_SIZE", 7.0, 0, 1))
+    # a copy after the rollout's GEMMs (input generation) is not the calibration copy
+    rows.append((500, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 123.0, 0, 1))
     db = str(tmp_path / "f.db")
     _db(db, rows)
     g = bench.counter_dispatches(db, ("FETCH_SIZE",), v)
@@ -126,3 +128,26 @@ def test_nested_profiling_is_detected(bench):
 def test_profile_fallback_is_the_recorded_figure_or_none(bench):
     # reported only while the GEMM sources hash to the recorded values
     assert bench.gemm_traffic() in (None, bench.GEMM_TRAFFIC["bytes_per_launch"])
+
+
+def test_class_dispatches_are_kept_in_launch_order(bench, tmp_path):
+    v = bench.gemm_variants(CFG)
+    shapes = bench.class_shapes()
+    assert len(shapes) == 6 and len({k for k, *_ in shapes}) == 6
+    rows = [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 1.0, 0, 1)]
+    rows += [(i + 2, _name(t), "FETCH_SIZE", 1.0, 0, 1) for i, (t, _) in enumerate(v.values())]
+    n_cls = bench.PROBE_CLASS_LAUNCHES * len(shapes)
+    # dispatch ids deliberately not in insertion order
+    for j in reversed(range(n_cls)):
+        rows.append((100 + j, _name(bench.CLASS_TMPL), "FETCH_SIZE", float(j), 0, 1))
+    db = str(tmp_path / "k.db")
+    _db(db, rows)
+    g = bench.counter_dispatches(db, ("FETCH_SIZE",), v)
+    assert [val["FETCH_SIZE"] for _, val in g["class"]] == [float(j) for j in range(n_cls)]
+    pairs = bench.class_groups(g["class"], shapes)
+    assert [k for k, _ in pairs] == [k for k, *_ in shapes]
+    per = bench.PROBE_CLASS_LAUNCHES
+    for i, (_, ds) in enumerate(pairs):
+        assert [val["FETCH_SIZE"] for _, val in ds] == [float(per * i + r) for r in range(per)]
+    # a launch missing: no class figures rather than shifted ones
+    assert bench.class_groups(g["class"][1:], shapes) == []
