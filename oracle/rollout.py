@@ -13,6 +13,10 @@ shape of its MLP linears. Readings (the pages give no network):
     GELU(z) = z Phi(z) with Phi the standard normal CDF, no time conditioning;
   * every linear input is rounded to fp32 and then quantized (the quantizers
     take fp32 or bf16 input); everything else is float64;
+  * the hidden activation z = W1 RMSNorm(h) enters GELU unrounded
+    (hidden="f32", the default). hidden="bf16" is the other reading a bf16
+    network would take: z rounded to fp32 and then to bf16, both to nearest
+    even, before GELU;
   * proxy reward = <mean over tokens of x_final, u> for a fixed vector u;
   * Euler steps on the uniform grid t_i = 1 - i/6.
 """
@@ -75,17 +79,35 @@ class QuantLinear:
         return gemm.gemm_dense(x_hat, self.w_hat)[0]
 
 
-def velocity(x, w1, w2):
-    """x: [tokens_total, dim]; w1[b]: QuantLinear dim->hidden; w2[b]: hidden->dim."""
+def bf16_round(z):
+    """z rounded to fp32, then to bf16 (8 significant bits), each to nearest
+    with ties to even, as float64. The second rounding drops the 16 low bits
+    of the fp32 pattern: add half of their range, minus one unless the lowest
+    kept bit is set, then clear them (finite inputs; the carry may step into
+    the exponent, which is the correct rounding)."""
+    f = np.ascontiguousarray(np.asarray(z, dtype=np.float64).astype(np.float32))
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def velocity(x, w1, w2, hidden="f32"):
+    """x: [tokens_total, dim]; w1[b]: QuantLinear dim->hidden; w2[b]: hidden->dim.
+    hidden: "f32" (GELU of z itself) or "bf16" (GELU of bf16_round(z))."""
+    if hidden not in ("f32", "bf16"):
+        raise ValueError(hidden)
     h = np.asarray(x, dtype=np.float64)
     for l1, l2 in zip(w1, w2):
-        h = h + l2(gelu(l1(rmsnorm(h))))
+        z = l1(rmsnorm(h))
+        if hidden == "bf16":
+            z = bf16_round(z)
+        h = h + l2(gelu(z))
     return h
 
 
-def rollout(noise, w1, w2, u, n_steps=6, fmt="mx", k_top=12, k_bottom=12):
+def rollout(noise, w1, w2, u, n_steps=6, fmt="mx", k_top=12, k_bottom=12, hidden="f32"):
     """noise: [n_cand, tokens, dim]; w1/w2: lists of float weights [out, in]
-    (or of ready QuantLinear layers).
+    (or of ready QuantLinear layers); hidden: as velocity.
 
     Returns (x_final [n_cand, tokens, dim], rewards [n_cand], top, bottom)."""
     noise = np.asarray(noise, dtype=np.float32)
@@ -95,7 +117,7 @@ def rollout(noise, w1, w2, u, n_steps=6, fmt="mx", k_top=12, k_bottom=12):
     t = euler.schedule(n_steps)
     x = noise.reshape(n_cand * tokens, dim).astype(np.float64)
     for i in range(n_steps):
-        v = velocity(x, q1, q2)
+        v = velocity(x, q1, q2, hidden)
         x = euler.step(x, v, t[i], t[i + 1])
     r = reward.proxy_reward(x, tokens, u)
     top, bottom = reward.select(r, k_top, k_bottom)
