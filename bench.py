@@ -43,12 +43,14 @@ PEAK_HBM = 8.0e12       # bytes/s
 # change). See profiles/rollout_96x4096x3072_kernels.md.
 GEMM_TRAFFIC = {"sources": {"gemm_mx.hip": "55d74820f7fa69cc", "gemm_common.h": "d8952e405ad1a5b1",
                             "mx_common.h": "f336665198c3bb5f"},
-                "bytes_per_launch": 19.20e9}
+                "hidden": "bf16", "bytes_per_launch": 19.20e9}
 COPY_BYTES = 1 << 30    # the known-size copy that calibrates the byte counters
 
 
-def gemm_traffic():
+def gemm_traffic(hidden):
     import hashlib
+    if hidden != GEMM_TRAFFIC["hidden"]:
+        return None
     csrc = os.path.join(ROOT, "fp4_quantized_diffusion_amd", "csrc")
     for name, digest in GEMM_TRAFFIC["sources"].items():
         with open(os.path.join(csrc, name), "rb") as f:
@@ -59,11 +61,14 @@ def gemm_traffic():
 
 def gemm_variants(cfg):
     """The rollout step's GEMM launches by epilogue: (kernel template, launches
-    per step). The first linear of every block quantizes GELU in its epilogue;
-    the second adds the residual, except in the last block, where it also takes
-    the Euler step, and in the last step also the reward partial sums."""
+    per step). The first linear of every block quantizes GELU in its epilogue
+    (of the fp32 sums, or with cfg["hidden_act"] == "bf16" of their bf16
+    rounding); the second adds the residual, except in the last block, where
+    it also takes the Euler step, and in the last step also the reward
+    partial sums."""
     b, s = cfg["blocks"], cfg["steps"]
-    return {"gelu_mxfp4": ("gemm_fp4_kernel<0, 3, 2>", b * s), "residual": ("gemm_fp4_kernel<0, 1, 2>", (b - 1) * s),
+    gelu = "gemm_fp4_kernel<0, 3, 2>" if cfg.get("hidden_act") == "bf16" else "gemm_fp4_kernel<0, 5, 2>"
+    return {"gelu_mxfp4": (gelu, b * s), "residual": ("gemm_fp4_kernel<0, 1, 2>", (b - 1) * s),
             "euler": ("gemm_fp4_kernel<0, 2, 2>", s - 1), "euler_reward": ("gemm_fp4_kernel<0, 4, 2>", 1)}
 
 
@@ -107,7 +112,8 @@ def traffic_probe(cfg):
     del src, dst
     noise, w1, w2, u = make_inputs(cfg, dev)
     work = torch.empty_like(noise)
-    ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=cfg["n_cand"])
+    ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=cfg["n_cand"],
+                    hidden=cfg["hidden_act"])
     ro.run(noise, work)
     torch.cuda.synchronize()
     print("counter probe: rollout step done", flush=True)
@@ -235,7 +241,8 @@ def measure_counters(cfg, timeout_s=420):
             tag = "+".join(counters)
             out_name = f"pass{i}"
             cmd = [prof, "--pmc", *counters, "-d", tmp, "-o", out_name, "--", sys.executable,
-                   os.path.join(ROOT, "bench.py"), "--traffic-probe", "--tokens", str(cfg["tokens"])]
+                   os.path.join(ROOT, "bench.py"), "--traffic-probe", "--tokens", str(cfg["tokens"]),
+                   "--hidden", cfg["hidden_act"]]
             logf = os.path.join(tmp, out_name + ".log")
             with open(logf, "w") as lf:
                 p = subprocess.Popen(cmd, stdout=lf, stderr=subprocess.STDOUT, cwd=tmp, env=env,
@@ -680,6 +687,21 @@ def gelu_epilogue_variants(x, w1, cfg):
             "bf16_table_tflops": round(flop / t_tab[0] / 1e6, 1), "f32_erfc_tflops": round(flop / t_f32[0] / 1e6, 1)}
 
 
+def run_config(args):
+    """(cfg, candidates per chunk, whether this is the default workload) for
+    the parsed arguments: the rollout's sizes, with the token count and the
+    hidden activation's precision (cfg["hidden_act"]; cfg["hidden"] is the
+    hidden width) from the arguments."""
+    from fp4_quantized_diffusion_amd.inputs import ROLLOUT
+    cfg = dict(ROLLOUT)
+    cfg["tokens"] = args.tokens
+    cfg["hidden_act"] = args.hidden or ("bf16" if args.overlap else "f32")
+    chunk = args.chunk or cfg["n_cand"]
+    default = (args.layout == "panel" and not args.overlap and args.tokens == 4096 and chunk == cfg["n_cand"]
+               and cfg["hidden_act"] == "f32")
+    return cfg, chunk, default
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -694,7 +716,11 @@ def main():
                     help="skip the standalone Euler / proxy reward / selection timings at the rollout's size")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per candidate (4096 is the workload)")
     ap.add_argument("--layout", choices=("panel", "row"), default="panel", help="FP4 operand layout of the GEMMs")
-    ap.add_argument("--overlap", action="store_true", help="two-stream schedule (GEMMs beside quantizers)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="two-stream schedule (GEMMs beside quantizers; stores the hidden activation as bf16)")
+    ap.add_argument("--hidden", choices=("f32", "bf16"), default=None,
+                    help="the first linear's output into GELU: f32 (default; the oracle's arithmetic) or bf16 "
+                         "(rounded first: a faster epilogue, but a different network)")
     ap.add_argument("--cpu-full", action="store_true",
                     help="also time the oracle's quantization of every class activation in full (minutes of CPU)")
     ap.add_argument("--no-stage2", action="store_true",
@@ -711,7 +737,7 @@ def main():
     args = ap.parse_args()
     if args.traffic_probe:
         from fp4_quantized_diffusion_amd.inputs import ROLLOUT
-        traffic_probe(dict(ROLLOUT, tokens=args.tokens))
+        traffic_probe(dict(ROLLOUT, tokens=args.tokens, hidden_act=args.hidden or "f32"))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the rollout shards over candidates "
@@ -719,11 +745,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    from fp4_quantized_diffusion_amd.inputs import ROLLOUT
-    cfg = dict(ROLLOUT)
-    cfg["tokens"] = args.tokens
-    chunk = args.chunk or cfg["n_cand"]
-    default_workload = args.layout == "panel" and not args.overlap and args.tokens == 4096 and chunk == cfg["n_cand"]
+    cfg, chunk, default_workload = run_config(args)
     # the counters first, while this process has no GPU state
     traffic, counters, traffic_src = None, None, None
     if default_workload:
@@ -742,9 +764,10 @@ def main():
                                      "the same runs",
                            "by_variant": counters["by_variant"], "counter_factors": counters["counter_factors"]}
         else:
-            traffic = gemm_traffic()
+            traffic = gemm_traffic(cfg["hidden_act"])
             traffic_src = {"source": "profile (profiles/rollout_96x4096x3072_kernels.md)" if traffic is not None
-                           else "none: the GEMM sources changed since the profile's counters",
+                           else "none: the profile's counters were taken with other GEMM sources or "
+                                "another hidden activation",
                            "not_measured": why}
 
     import torch
@@ -757,7 +780,7 @@ def main():
     work = torch.empty_like(noise)
     timer = EventTimer()
     ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
-                    timer=timer, layout=args.layout, overlap=args.overlap)
+                    timer=timer, layout=args.layout, overlap=args.overlap, hidden=cfg["hidden_act"])
 
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
@@ -810,6 +833,7 @@ def main():
                    "n_cand": cfg["n_cand"], "tokens": cfg["tokens"], "dim": cfg["dim"], "hidden": cfg["hidden"],
                    "blocks": cfg["blocks"], "euler_steps": cfg["steps"], "chunk_candidates": chunk,
                    "operand_layout": args.layout, "two_stream_overlap": args.overlap,
+                   "hidden_activation": cfg["hidden_act"],
                    "gemm_shapes": [[m_rows, cfg["dim"], cfg["hidden"]], [m_rows, cfg["hidden"], cfg["dim"]]]},
         # the recorded traffic is that of the default workload (panel layout, one stream, all candidates)
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_FP4 / 1e12,
@@ -818,8 +842,9 @@ def main():
                      "traffic_unit": "GB per launch (L2 <-> fabric reads + writes, rocprofv3 counters)",
                      "traffic_detail": traffic_src,
                      "kernel": f"gemm_fp4_kernel, {args.layout} layout (MXFP4 x MXFP4, fp32 accumulate; "
-                               + ("the first linear's launches quantize GELU(bf16(C)) to MXFP4 in their epilogue, "
-                                  "the second's add the residual, the last block's also apply the Euler step)"
+                               + (f"the first linear's launches quantize "
+                                  f"{'GELU(C)' if cfg['hidden_act'] == 'f32' else 'GELU(bf16(C))'} to MXFP4 in their "
+                                  "epilogue, the second's add the residual, the last block's also apply the Euler step)"
                                   if args.layout == "panel" else "the second linear's launches add the residual)"),
                      "flop_per_launch": gemm_flop, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "gemm_tflops": round(achieved / 1e12, 2),

@@ -3,11 +3,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common_host.h"
 
 namespace fp4r {
 
 // ---- device helpers ----
+// f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile time
+// (the index is a constant in every copy, whatever the body holds).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

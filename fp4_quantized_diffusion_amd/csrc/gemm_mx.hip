@@ -538,8 +538,6 @@ constexpr int full_tile_vmem() {
                                     : (RESID == 4 ? 16 * 12 + 5 : 16 * (BF16OUT ? 2 : (RESID == 2 ? 12 : (RESID ? 8 : 4))));
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // MFMA tiles are stored in the order t = 4 j + i (j: m block, i: n block),
 // so the two tiles i = 2k, 2k + 1 that share a 128-byte line of a bf16 row
 // are written back to back.
@@ -741,27 +739,73 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // rows m0 .. m0 + 127 of the panel: codes of 32 rows are staged in LDS and
 // leave as 2 KiB contiguous (two 16-byte stores per lane), the 4 scale bytes
 // of a row as one 4-byte store.
-// EXACT: GELU of the fp32 sum itself (erfc evaluated per element, no bf16
-// rounding, no table) -- the operations of an fp32-out GEMM followed by
-// fp4_quantize(GELU prologue) on its fp32 output, so the same bits.
+// EXACT: GELU of the fp32 sum itself (no bf16 rounding: the table's entry
+// near it and a Taylor expansion, gelu_f32_tab_n) -- the operations of an
+// fp32-out GEMM followed by fp4_quantize(GELU prologue) on its fp32 output,
+// so the same bits.
+// Quantize the 16 GELU values g of MFMA tile (i, j) (this lane's half of
+// a 32-block) and stage the wave's codes; returns the block's scale byte.
+__device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* stage, int r32, int h) {
+  uint32_t am = amax_bits<16>(g);
+  {  // the other lane half's amax: one of each swapped pair is this lane's own
+    const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+    am = max(sw[0], sw[1]);
+  }
+  const uint32_t S = mx_scale(am);
+  // x: block bytes 2h, 2h+1, 4+2h, 5+2h (q = 0, 1); y: the same for q = 2, 3.
+  // After the swap lane half 0 holds x of both halves, half 1 y of both.
+  const auto xy = __builtin_amdgcn_permlane32_swap(mx_pack8(g, S), mx_pack8(g + 8, S), false, false);
+  const uint32_t w0 = __builtin_amdgcn_perm(xy[1], xy[0], 0x05040100u);
+  const uint32_t w1 = __builtin_amdgcn_perm(xy[1], xy[0], 0x07060302u);
+  *reinterpret_cast<uint2*>(stage + r32 * kQPitch + 16 * i + 8 * h) = make_uint2(w0, w1);
+  return S;
+}
+
+// Write the staged codes of 32 rows (2 KiB contiguous, two 16-byte stores per
+// lane) and their 4 scale bytes per row.
+__device__ __forceinline__ void gelu_rows_out(uint8_t* qc, uint8_t* qs, int m0, int j, uint32_t sreg,
+                                              const uint8_t* stage, int lane, int r32, int h) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 16 * half + (lane >> 2), col = lane & 3;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kQPitch + col * 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(qc + (int64_t)(m0 + 32 * j + row) * 64 + col * 16));
+  }
+  if (h == 0) __builtin_nontemporal_store(sreg, reinterpret_cast<uint32_t*>(qs + (int64_t)(m0 + 32 * j + r32) * 4));
+  __builtin_amdgcn_sched_barrier(0);  // the next rows' staging writes stay behind these reads
+}
+
 template <bool EXACT>
 __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
-                                                   uint8_t* stage, const float* tab) {
+                                                   uint8_t* stage, const float* tab, const float2* tab2) {
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
   const int r32 = lane & 31, h = lane >> 5;
   uint8_t* qc = p.qc + blk * 16384;
   uint8_t* qs = p.qs + blk * 1024;
+  if constexpr (EXACT) {
+    // compile-time tile indices: gelu_f32_tab_n holds a loop, and an (i, j)
+    // loop around it would stay rolled, indexing the accumulators at run time
+    static_for<0, 4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      uint32_t sreg = 0;
+      static_for<0, 4>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        float z[16], g[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t sreg = 0;
+        for (int e = 0; e < 16; ++e) z[e] = acc_read(acc[i][j][e]);
+        gelu_f32_tab_n<16>(g, z, tab2);
+        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
+      });
+      gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+    });
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float g[16];
-      if (EXACT) {
+    for (int j = 0; j < 4; ++j) {
+      uint32_t sreg = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) g[e] = gelu_erfc(acc_read(acc[i][j][e]));
-      } else {
+      for (int i = 0; i < 4; ++i) {
+        float g[16];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
           const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
@@ -772,29 +816,10 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
+        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
       }
-      uint32_t am = amax_bits<16>(g);
-      {  // the other lane half's amax: one of each swapped pair is this lane's own
-        const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
-        am = max(sw[0], sw[1]);
-      }
-      const uint32_t S = mx_scale(am);
-      // x: block bytes 2h, 2h+1, 4+2h, 5+2h (q = 0, 1); y: the same for q = 2, 3.
-      // After the swap lane half 0 holds x of both halves, half 1 y of both.
-      const auto xy = __builtin_amdgcn_permlane32_swap(mx_pack8(g, S), mx_pack8(g + 8, S), false, false);
-      const uint32_t w0 = __builtin_amdgcn_perm(xy[1], xy[0], 0x05040100u);
-      const uint32_t w1 = __builtin_amdgcn_perm(xy[1], xy[0], 0x07060302u);
-      *reinterpret_cast<uint2*>(stage + r32 * kQPitch + 16 * i + 8 * h) = make_uint2(w0, w1);
-      sreg |= S << (8 * i);
+      gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
     }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = 16 * half + (lane >> 2), col = lane & 3;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kQPitch + col * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(qc + (int64_t)(m0 + 32 * j + row) * 64 + col * 16));
-    }
-    if (h == 0) __builtin_nontemporal_store(sreg, reinterpret_cast<uint32_t*>(qs + (int64_t)(m0 + 32 * j + r32) * 4));
-    __builtin_amdgcn_sched_barrier(0);  // the next rows' staging writes stay behind these reads
   }
 }
 
@@ -925,15 +950,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
   // full tiles' epilogue through an LDS staging area (the MXFP4 ring leaves
   // room for it; the NVFP4-style ring, with twice the scale bytes, does not);
   // the GELU + MXFP4 epilogue has its own, smaller one and the GELU table
-  constexpr bool GELU_Q = RESID == 3 || RESID == 5;  // 5: GELU of the fp32 sum (no table)
-  constexpr bool GELU_TAB = RESID == 3;
+  constexpr bool GELU_Q = RESID == 3 || RESID == 5;  // 5: GELU of the fp32 sum, 3: of its bf16 rounding
   constexpr bool EPI_LDS = !NV && !GELU_Q;
   // The GELU + MXFP4 epilogue needs the registers that the next tile's first
   // fragments would hold across it: it reads them afterwards.
   constexpr bool DEFER_READ = GELU_Q;
   __shared__ __attribute__((aligned(16))) uint8_t epi_stage[EPI_LDS ? 4 * kEpiWaveBytes : (GELU_Q ? 4 * kQWaveBytes : 16)];
-  __shared__ float gtab[GELU_TAB ? kGeluTab : 1];
-  if (GELU_TAB) gelu_table_fill(gtab);  // visible to all waves after the first pipeline barrier
+  // GELU tables, visible to all waves after the first pipeline barrier
+  __shared__ float gtab[RESID == 3 ? kGeluTab : 1];     // bf16 sums: Q at every bf16 magnitude from 2^-22
+  __shared__ float2 gtab2[RESID == 5 ? kGeluTTab : 1];  // fp32 sums: (Q, phi) from 2^-10, Taylor in between
+  if (RESID == 3) gelu_table_fill(gtab);
+  if (RESID == 5) gelu_table_fill(gtab2);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // the wave's 128 x 128 sub-tile
@@ -1000,7 +1027,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(Problem p, void* 
     if (GELU_Q) {
       // every tile is full (the host launches this epilogue only for m, n multiples of 256)
       store_tile_gelu_mx<RESID == 5>(acc, (int64_t)tm * p.qnc + 2 * tn + wn, wm * 128, p,
-                                     epi_stage + wave * kQWaveBytes, gtab);
+                                     epi_stage + wave * kQWaveBytes, gtab, gtab2);
       counted = true;
     } else if (counted) {
       if (EPI_LDS && BF16OUT)

@@ -9,6 +9,8 @@
 
 namespace fp4r {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // GELU(z) = z Phi(z), Phi the standard normal CDF, through the complementary
 // error function: with Q = erfc(|z| / sqrt 2) / 2, Phi(z) = Q for z < 0 and
 // 1 - Q otherwise, so the negative side never forms 1 + erf (which cancels
@@ -68,6 +70,24 @@ __device__ __forceinline__ float gelu_erfc(float z) {
   return gelu_q(z, phi_tail(fabsf(z)));
 }
 
+// The standard normal density phi(a) = exp(-a^2 / 2) / sqrt(2 pi), with the
+// exponent split exactly as in phi_tail (relative error a few fp32 ulps).
+__device__ __forceinline__ float gauss_pdf(float a) {
+#pragma clang fp contract(off)
+  constexpr float kHalfLog2eHi = -0.7213475f;
+  constexpr float kHalfLog2eLo = -9.629815e-09f;
+  constexpr float kLn2 = 0.693147180559945309f;
+  constexpr float kInvSqrt2Pi = 0.398942280401432678f;
+  const float s = a * a, s_lo = fmaf(a, a, -s);
+  const float y = s * kHalfLog2eHi;
+  float e = fmaf(s, kHalfLog2eHi, -y);
+  e = fmaf(s_lo, kHalfLog2eHi, e);
+  e = fmaf(s, kHalfLog2eLo, e);
+  float es = __builtin_amdgcn_exp2f(y);
+  es = fmaf(es * e, kLn2, es);
+  return es * kInvSqrt2Pi;
+}
+
 // GELU of a bf16 input through a table of Q(|z|). A bf16 value has 8
 // significant bits, so the magnitudes 2^-22 .. 16 are 26 binades of 128
 // values plus 16 itself: 3329 entries (13 KiB in LDS), holding phi_tail of
@@ -89,6 +109,81 @@ __device__ __forceinline__ void gelu_table_fill(float* tab) {
 __device__ __forceinline__ float gelu_bf16(float z, const float* tab) {
   const uint32_t m = min(max((__float_as_uint(z) >> 16) & 0x7FFFu, kGeluLo), kGeluHi);  // z is a bf16 value
   return gelu_q(z, tab[m - kGeluLo]);
+}
+
+// GELU of an fp32 input through a table of (Q(a), phi(a)) at the bf16
+// magnitudes a from 2^-10 to 16: 14 binades of 128 values plus 16 itself,
+// 1793 entries (14 KiB in LDS), Q = phi_tail(a). With a_c the bf16 rounding
+// of |z| clamped to [2^-10, 16] and d = |z| - a_c (|d| <= 2^-9 a_c above
+// 2^-10, |d| <= 2^-10 below; exact by Sterbenz where |z| >= a_c / 2), the
+// fourth-order Taylor expansion
+//     Q(a_c + d) = Q - phi d [1 - a_c d / 2 + (a_c^2 - 1) d^2 / 6
+//                             + a_c (3 - a_c^2) d^3 / 24]
+// follows from Q^(1) = -phi, Q^(2) = a phi, Q^(3) = (1 - a^2) phi,
+// Q^(4) = (a^3 - 3 a) phi. The next term, phi (a^4 - 6 a^2 + 3) d^5 / 120, is
+// below 1.5e-8 of Q for |z| <= 6 (Q / phi >= a / (a^2 + 1)); the rounding of
+// the expansion adds a few fp32 ulps of phi d, so the result carries
+// phi_tail's error (about 5e-7 relative). At the table's points (d = 0) the
+// result is phi_tail's, bit for bit. Beyond |z| = kGeluTaylorMax the callers
+// take gelu_erfc instead, element by element, so the value depends on z
+// alone.
+constexpr uint32_t kGeluTLo = (127u - 10u) << 7;  // bf16 magnitude bits of 2^-10
+constexpr int kGeluTTab = (int)(kGeluHi - kGeluTLo + 1);
+constexpr float kGeluTaylorMax = 6.0f;
+
+__device__ __forceinline__ void gelu_table_fill(float2* tab) {
+  for (int e = threadIdx.x; e < kGeluTTab; e += blockDim.x) {
+    const float a = __uint_as_float((kGeluTLo + (uint32_t)e) << 16);
+    tab[e] = make_float2(phi_tail(a), gauss_pdf(a));
+  }
+}
+
+// mag16: the magnitude bits of the bf16 rounding (nearest even) of z. Valid
+// for |z| <= kGeluTaylorMax (see above).
+__device__ __forceinline__ float gelu_f32_tab(float z, uint32_t mag16, const float2* tab) {
+#pragma clang fp contract(off)
+  const uint32_t m = min(max(mag16, kGeluTLo), kGeluHi);  // any pattern, NaN included, stays in the table
+  const float2 t = tab[m - kGeluTLo];
+  const float ac = __uint_as_float(m << 16);
+  const float d = fabsf(z) - ac;
+  const float s = ac * ac;
+  float b = fmaf(ac * fmaf(s, -1.0f / 24.0f, 0.125f), d, fmaf(s, 1.0f / 6.0f, -1.0f / 6.0f));
+  b = fmaf(b, d, -0.5f * ac);
+  b = fmaf(b, d, 1.0f);
+  return gelu_q(z, fmaf(-t.y, b * d, t.x));
+}
+
+// GELU of N (even) fp32 values through the table: the expansion where
+// |z| <= kGeluTaylorMax, the evaluated erfc elsewhere (a branch that lanes
+// skip unless one of their N values is that large). The bf16 roundings come
+// from the hardware's nearest-even pair conversion.
+template <int N>
+__device__ __forceinline__ void gelu_f32_tab_n(float* g, const float* z, const float2* tab) {
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < N; e += 2) {
+    uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)z[e], (__bf16)z[e + 1]});
+    asm("" : "+v"(u));  // one pair conversion
+    g[e] = gelu_f32_tab(z[e], u & 0x7FFFu, tab);
+    g[e + 1] = gelu_f32_tab(z[e + 1], (u >> 16) & 0x7FFFu, tab);
+    m = fmaxf(m, fmaxf(fabsf(z[e]), fabsf(z[e + 1])));
+  }
+  if (!(m <= kGeluTaylorMax)) {  // NaN goes this way too
+    // One evaluation per trip of a loop that stays rolled, so the code stays
+    // small wherever this is inlined; the value is picked out and put back
+    // by selects on compile-time positions (no register array is indexed
+    // by a run-time value, which would move it to scratch memory).
+#pragma unroll 1
+    for (int e = 0; e < N; ++e) {
+      float ze = z[0];
+#pragma unroll
+      for (int k = 1; k < N; ++k) ze = k == e ? z[k] : ze;
+      const float r = gelu_erfc(ze);
+      const bool tail = !(fabsf(ze) <= kGeluTaylorMax);
+#pragma unroll
+      for (int k = 0; k < N; ++k) g[k] = (k == e && tail) ? r : g[k];
+    }
+  }
 }
 
 // Bits of max |v_j| by the IEEE maximum (v_maximum3_f32, absolute values as

@@ -36,24 +36,41 @@ __device__ __forceinline__ void st_out(T* p, T v) {
 
 enum { PRO_NONE = 0, PRO_RMSNORM = 1, PRO_GELU = 2 };
 
-// Elementwise prologue of one loaded octet (tab: the GELU table, bf16 input).
+// Elementwise prologue of one loaded octet (tab: the GELU table -- of Q at
+// every bf16 magnitude for bf16 input, of (Q, phi) for fp32 input).
 template <int BF16, int PRO>
-__device__ __forceinline__ void prologue8(float v[8], const float* tab) {
+__device__ __forceinline__ void prologue8(float v[8], const void* tab) {
   if (PRO == PRO_GELU) {
+    if (BF16) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = BF16 ? gelu_bf16(v[j], tab) : gelu_erfc(v[j]);
+      for (int j = 0; j < 8; ++j) v[j] = gelu_bf16(v[j], static_cast<const float*>(tab));
+    } else {
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z[j] = v[j];
+      gelu_f32_tab_n<8>(v, z, static_cast<const float2*>(tab));
+    }
   }
 }
 
-// LDS for the GELU table when the kernel needs it (bf16 input, GELU).
+// LDS for the GELU table when the kernel needs it (GELU prologue).
 template <int BF16, int PRO>
 struct GeluLds {
-  __device__ __forceinline__ float* get() { return nullptr; }
+  __device__ __forceinline__ const void* get() { return nullptr; }
 };
 template <>
 struct GeluLds<1, PRO_GELU> {
-  __device__ __forceinline__ float* get() {
+  __device__ __forceinline__ const void* get() {
     __shared__ float tab[kGeluTab];
+    gelu_table_fill(tab);
+    __syncthreads();
+    return tab;
+  }
+};
+template <>
+struct GeluLds<0, PRO_GELU> {
+  __device__ __forceinline__ const void* get() {
+    __shared__ float2 tab[kGeluTTab];
     gelu_table_fill(tab);
     __syncthreads();
     return tab;
@@ -107,7 +124,7 @@ template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(
     const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, int64_t opr, UDiv segs, int64_t steps) {
-  const float* tab = GeluLds<BF16, PRO>().get();
+  const void* tab = GeluLds<BF16, PRO>().get();
   const int64_t G = gridDim.x;
   for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
     float v[kUnroll][8];
@@ -145,7 +162,7 @@ template <int BF16, int PRO>
 __global__ __launch_bounds__(kThreads) void quant_mx_panel_kernel(
     const void* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, UDiv nc, int64_t steps) {
-  const float* tab = GeluLds<BF16, PRO>().get();
+  const void* tab = GeluLds<BF16, PRO>().get();
   const int64_t G = gridDim.x;
   for (int64_t st0 = blockIdx.x; st0 < steps; st0 += kUnroll * G) {
     float v[kUnroll][8];
@@ -549,7 +566,7 @@ hipError_t launch_quant_mx(const void* x, int x_bf16, int64_t rows, int64_t k, i
       x, ldx, codes, ld_codes, scales, ld_scales, opr, make_udiv(segs), steps)
   if (prologue == PRO_GELU) {
     if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
-    else FP4R_LAUNCH(0, PRO_GELU, false);
+    else FP4R_LAUNCH(0, PRO_GELU, true);
   } else {
     if (x_bf16) FP4R_LAUNCH(1, PRO_NONE, false);
     else FP4R_LAUNCH(0, PRO_NONE, false);
@@ -577,7 +594,7 @@ hipError_t launch_quant_mx_panel(const void* x, int x_bf16, int64_t rows, int64_
       x, rows, k, ldx, codes, scales, make_udiv(nc), steps)
   if (prologue == PRO_GELU) {
     if (x_bf16) FP4R_LAUNCH(1, PRO_GELU, true);
-    else FP4R_LAUNCH(0, PRO_GELU, false);
+    else FP4R_LAUNCH(0, PRO_GELU, true);
   } else {
     if (x_bf16) FP4R_LAUNCH(1, PRO_NONE, false);
     else FP4R_LAUNCH(0, PRO_NONE, false);

@@ -11,20 +11,24 @@ shape of their MLP linears: 4 residual blocks
 (dim -> hidden -> dim, no time conditioning), then Euler steps on the
 uniform grid t_i = 1 - i/steps. Per block the device work is:
     fp4_quantize(h, RMSNORM prologue)     -> A1 (MXFP4)
-    fp4_gemm(A1, W1q) -> z (bf16)
+    fp4_gemm(A1, W1q) -> z (fp32)
     fp4_quantize(z, GELU prologue)        -> A2 (MXFP4)
     fp4_gemm(A2, W2q, residual = h) -> h  (fp32, in place)
 and per step euler_step(x, v = h). With the panel layout (the default) and
 row counts that are multiples of 256, the first two lines are one call,
-fp4_gemm_panel_gelu(A1, W1q) -> A2, which applies the bf16 rounding, the GELU
-and the MXFP4 quantization in the GEMM's epilogue (bit-identical to the pair,
-without writing z); and the last block's second GEMM and the Euler step are
-one call,
+fp4_gemm_panel_gelu_f32(A1, W1q) -> A2, which applies the GELU to the fp32
+sums and the MXFP4 quantization in the GEMM's epilogue (bit-identical to the
+pair, without writing z); and the last block's second GEMM and the Euler
+step are one call,
 fp4_gemm_panel_euler(A2, W2q, residual = h, x) -> x_next, which applies
 x + dt (h + A2 W2q^T) in the GEMM's epilogue -- bit-identical to the GEMM into
 v followed by euler_step, without writing v or reading it back. The hidden
-activation z is stored as bf16 between the two kernels (the float64 oracle
-keeps it unrounded). The FP4 operands use the panel layout by default
+activation z stays fp32, as in the float64 oracle's reading; hidden="bf16"
+rounds it to bf16 first (fp4_gemm_panel_gelu, a GELU table in LDS, faster,
+but not the oracle's arithmetic: at 96 x 4096 x 3072 the final state then
+differs from the oracle's by about a quarter, because the rounding moves
+about one hidden value in a hundred across an FP4 decision point and the
+next blocks' quantizers amplify that). The FP4 operands use the panel layout by default
 (fp4_quantize with FP4_LAYOUT_PANEL, fp4_gemm_panel): the same codes and
 scales, stored so that every GEMM stage load is contiguous; layout="row" runs
 the row-major entry points (and a separate euler_step) instead.
@@ -36,14 +40,15 @@ quantizer of one half runs while a GEMM of the other half does:
     GEMM stream:       G1(A) G1(B) G2(A) G2(B) G1'(A) ...
     quantizer stream:  R(A) R(B) Q(A) Q(B) R'(A) R'(B) ...
 (R: RMSNorm quantize, Q: GELU quantize; every edge is a device-side event
-wait, no host synchronization). The quantizers are VALU-bound and fit
+wait, no host synchronization). It stores the hidden activation as bf16, so
+it needs hidden="bf16". The quantizers are VALU-bound and fit
 beside the GEMM's one workgroup per CU (its waves leave VGPRs for one more
 wave per SIMD), so they overlap it. Every kernel computes rows independently
 of how the rows are chunked, so the result is bit-identical to the
 one-stream schedule. Both streams run at the default priority. On MI355X
 this schedule measured slower than the one-stream schedule of the same
 (unfused) kernels for the 96 x 4096 x 3072 rollout (534 vs 523 ms per step;
-the fused default path takes 370-381 ms): the GEMM runs at the card's power
+the fused path with a bf16 hidden activation took 370-381 ms): the GEMM runs at the card's power
 limit, and the overlapped quantizers lower the clock and slow the GEMM by
 more than they hide; it is kept as an option.
 
@@ -56,7 +61,7 @@ from . import binding as fb
 
 class Fp4Rollout:
     def __init__(self, w1, w2, u, steps=6, k_top=12, k_bottom=12, fmt="mx", chunk=None, timer=None,
-                 layout="panel", overlap=False, lora=None, fuse_reward=True, hidden="bf16"):
+                 layout="panel", overlap=False, lora=None, fuse_reward=True, hidden="f32"):
         """w1[b]: bf16 or fp32 CUDA [hidden, dim]; w2[b]: [dim, hidden]; u: fp32 [dim].
         lora: optional (lora1, lora2), one entry per block each, None or a
         LoRA adapter (B, A, scale) of that weight; the per-iteration
@@ -72,12 +77,15 @@ class Fp4Rollout:
         at least 2 candidates).
         timer: optional callable(name, fn) wrapping each launch (for timing);
         it is called with the launch's stream current.
-        hidden: "bf16" (default) rounds the first linear's output to bf16
-        before GELU -- in the fused epilogue (table lookup), or stored as bf16
-        between the kernels; "f32" keeps it fp32 (the fused epilogue evaluates
-        erfc on the fp32 sums, fp4_gemm_panel_gelu_f32; the unfused path
-        stores z as fp32), which is the float64 oracle's reading of the hidden
-        activation, at about three times the epilogue arithmetic."""
+        hidden: "f32" (default) keeps the first linear's output fp32 into
+        GELU, the float64 oracle's reading of the hidden activation (the
+        fused epilogue evaluates erfc on the fp32 sums,
+        fp4_gemm_panel_gelu_f32; the unfused path stores z as fp32). "bf16"
+        rounds it to bf16 before GELU (the fused epilogue reads a table in
+        LDS, fp4_gemm_panel_gelu; the unfused path stores z as bf16): about
+        a third of the epilogue arithmetic, but a different network -- the
+        rounding moves hidden values across FP4 decision points, which the
+        following quantizers amplify."""
         if fmt != "mx":
             raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
         self.w1, self.w2, self.u = list(w1), list(w2), u
@@ -90,7 +98,7 @@ class Fp4Rollout:
         if hidden not in ("bf16", "f32"):
             raise ValueError(f"unknown hidden dtype {hidden!r}")
         if hidden == "f32" and overlap:
-            raise ValueError("the two-stream schedule stores the hidden activation as bf16")
+            raise ValueError("the two-stream schedule stores the hidden activation as bf16: pass hidden='bf16'")
         self.hidden = hidden
         self._side = None
         self.timer = timer

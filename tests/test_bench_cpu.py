@@ -23,6 +23,8 @@ CFG = {"n_cand": 96, "tokens": 4096, "dim": 3072, "hidden": 12288, "blocks": 4, 
 
 
 def test_variants_cover_every_gemm_launch_of_a_step(bench):
+    assert bench.gemm_variants(CFG)["gelu_mxfp4"][0] == "gemm_fp4_kernel<0, 5, 2>"       # fp32 hidden (default)
+    assert bench.gemm_variants(dict(CFG, hidden_act="bf16"))["gelu_mxfp4"][0] == "gemm_fp4_kernel<0, 3, 2>"
     v = bench.gemm_variants(CFG)
     assert {k: n for k, (_, n) in v.items()} == {"gelu_mxfp4": 24, "residual": 18, "euler": 5, "euler_reward": 1}
     # two linears per block and Euler step
@@ -126,8 +128,11 @@ def test_nested_profiling_is_detected(bench):
 
 
 def test_profile_fallback_is_the_recorded_figure_or_none(bench):
-    # reported only while the GEMM sources hash to the recorded values
-    assert bench.gemm_traffic() in (None, bench.GEMM_TRAFFIC["bytes_per_launch"])
+    # reported only while the GEMM sources hash to the recorded values, and for
+    # the hidden activation the profile was taken with
+    h = bench.GEMM_TRAFFIC["hidden"]
+    assert bench.gemm_traffic(h) in (None, bench.GEMM_TRAFFIC["bytes_per_launch"])
+    assert bench.gemm_traffic("f32" if h == "bf16" else "bf16") is None
 
 
 def test_class_dispatches_are_kept_in_launch_order(bench, tmp_path):
@@ -151,3 +156,17 @@ def test_class_dispatches_are_kept_in_launch_order(bench, tmp_path):
         assert [val["FETCH_SIZE"] for _, val in ds] == [float(per * i + r) for r in range(per)]
     # a launch missing: no class figures rather than shifted ones
     assert bench.class_groups(g["class"][1:], shapes) == []
+
+
+def test_run_config_keeps_sizes_apart_from_options(bench):
+    import argparse
+    ns = argparse.Namespace(tokens=4096, hidden=None, overlap=False, chunk=0, layout="panel")
+    cfg, chunk, default = bench.run_config(ns)
+    assert (cfg["hidden"], cfg["dim"], cfg["n_cand"], chunk) == (12288, 3072, 96, 96)
+    assert cfg["hidden_act"] == "f32" and default
+    cfg, _, default = bench.run_config(argparse.Namespace(tokens=4096, hidden=None, overlap=True, chunk=0,
+                                                          layout="panel"))
+    assert cfg["hidden_act"] == "bf16" and cfg["hidden"] == 12288 and not default
+    cfg, _, default = bench.run_config(argparse.Namespace(tokens=4096, hidden="bf16", overlap=False, chunk=0,
+                                                          layout="panel"))
+    assert not default and bench.gemm_variants(cfg)["gelu_mxfp4"][0] == "gemm_fp4_kernel<0, 3, 2>"

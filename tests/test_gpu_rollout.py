@@ -1,5 +1,6 @@
 """GPU rollout (all steps through the C ABI) against the float64 oracle's
-rollout on a reduced problem. The composite is not bit-comparable (fp32 vs
+rollout on a reduced problem (the full-size rollout is checked on sampled
+rows in test_gpu_rollout_full.py). The composite is not bit-comparable (fp32 vs
 float64 intermediates re-quantized every block), so this is statistical:
 parity unpinned beyond the per-call tests -- final-latent relative error,
 reward rank correlation and selection overlap."""
@@ -20,18 +21,21 @@ def ranks(v):
     return np.argsort(np.argsort(v))
 
 
-# (layout, tokens, chunk, n_cand): 64-token candidates in chunks of 3 give
-# 192-row launches, which take the unfused kernels (bf16 hidden activation
-# through HBM, separate Euler step and reward); 256-token candidates in chunks
-# of 4 give 1024-row launches, which take the fused kernels the benchmark
-# times (GELU + MXFP4 in the first GEMM's epilogue, the Euler step and the
-# proxy reward in the last GEMM's).
+# The bf16 hidden activation (hidden="bf16", the faster option; fp32 is the
+# default, tested below) against the oracle's bf16 reading of the hidden
+# activation. (layout, tokens, chunk, n_cand): 64-token candidates in chunks
+# of 3 give 192-row launches, which take the unfused kernels (z stored as
+# bf16, separate Euler step and reward); 256-token candidates in chunks of 4
+# give 1024-row launches, which take the fused kernels (GELU + MXFP4 in the
+# first GEMM's epilogue, the Euler step and the proxy reward in the last
+# GEMM's).
 ROLLOUT_CASES = [("panel", 64, 3, 8), ("row", 64, 3, 8), ("panel", 256, 4, 16)]
-# Observed on MI355X: final-latent relative L2 4.20e-2 (all three cases),
-# Spearman rho 1.000 / 1.000 / 0.988, top-2 and bottom-2 overlap 4 of 4. The
-# distance is dominated by the bf16 rounding of the hidden activation before
-# GELU (the oracle keeps it exact), which moves values across quantization
-# decision points; the gates sit above the observed values.
+# Observed on MI355X against the oracle's bf16 reading: relative L2 5.8e-8
+# (both 192-row cases) and 1.0e-3 (the fused case, where a quantization
+# decision within fp32 rounding of its point flips and the next blocks carry
+# it on), largest reward error 7.9e-4 of the largest reward, Spearman rho
+# 1.000, top-2/bottom-2 overlap 4 of 4; against the fp32 reading 4.2e-2. The
+# gates leave about twice the largest observed distance.
 
 
 @pytest.mark.parametrize("layout,tokens,chunk,n_cand", ROLLOUT_CASES)
@@ -42,24 +46,29 @@ def test_reduced_rollout_against_oracle(gpu_lib, layout, tokens, chunk, n_cand):
     w1 = [w[0] for w in ws]
     w2 = [w[1] for w in ws]
     u = inputs.reward_vector(seed, dim)
-    x_or, r_or, t_or, b_or = orollout.rollout(noise, w1, w2, u, fmt="mx", k_top=2, k_bottom=2)
+    q1 = [orollout.QuantLinear(w, "mx") for w in w1]
+    q2 = [orollout.QuantLinear(w, "mx") for w in w2]
+    x_or, r_or, t_or, b_or = orollout.rollout(noise, q1, q2, u, fmt="mx", k_top=2, k_bottom=2, hidden="bf16")
+    x_f32 = orollout.rollout(noise, q1, q2, u, fmt="mx", k_top=2, k_bottom=2)[0]
 
     ro = Fp4Rollout([torch.from_numpy(w).to(DEV).bfloat16() for w in w1],
                     [torch.from_numpy(w).to(DEV).bfloat16() for w in w2],
-                    torch.from_numpy(u).to(DEV), k_top=2, k_bottom=2, chunk=chunk, layout=layout)
+                    torch.from_numpy(u).to(DEV), k_top=2, k_bottom=2, chunk=chunk, layout=layout, hidden="bf16")
     xd = torch.from_numpy(noise).to(DEV)
     r, top, bottom, rn = ro.run(xd)
     torch.cuda.synchronize()
     x_gpu = to_np(xd).astype(np.float64)
     rel = np.linalg.norm(x_gpu - x_or) / np.linalg.norm(x_or)
+    across = np.linalg.norm(x_gpu - x_f32) / np.linalg.norm(x_f32)
     rho = np.corrcoef(ranks(to_np(r)), ranks(r_or))[0, 1]
     rrel = np.abs(to_np(r) - r_or).max() / np.abs(r_or).max()
     ov = len(set(to_np(top)) & set(t_or)) + len(set(to_np(bottom)) & set(b_or))
-    print(f"rollout {layout} tokens={tokens} chunk={chunk}: rel L2 {rel:.3e}  reward rel {rrel:.3e}  "
-          f"spearman {rho:.4f}  top/bottom overlap {ov}/4")
-    assert rel < 0.05
-    assert rho > 0.95
-    assert ov >= 3
+    print(f"rollout bf16 hidden {layout} tokens={tokens} chunk={chunk}: rel L2 {rel:.3e} (against the fp32 "
+          f"reading {across:.3e})  reward rel {rrel:.3e}  spearman {rho:.4f}  top/bottom overlap {ov}/4")
+    assert rel < 2e-3
+    assert rrel < 2e-3
+    assert rho > 0.99
+    assert ov == 4
     # the GPU's selection is the exact selection of its own rewards
     from oracle import reward as oreward
     gt, gb = oreward.select(to_np(r), 2, 2)
@@ -67,7 +76,8 @@ def test_reduced_rollout_against_oracle(gpu_lib, layout, tokens, chunk, n_cand):
     np.testing.assert_array_equal(to_np(bottom), gb)
 
 
-def test_panel_and_row_layouts_agree_bitwise(gpu_lib):
+@pytest.mark.parametrize("hid", ["f32", "bf16"])
+def test_panel_and_row_layouts_agree_bitwise(gpu_lib, hid):
     """The two operand layouts store the same codes and run the same K order,
     so whole rollouts (ragged chunk, 300-token candidates: a ragged last
     panel) agree bit for bit."""
@@ -79,7 +89,7 @@ def test_panel_and_row_layouts_agree_bitwise(gpu_lib):
     w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
     outs = []
     for layout in ("panel", "row"):
-        ro = Fp4Rollout(w1, w2, u, k_top=2, k_bottom=1, chunk=2, layout=layout)
+        ro = Fp4Rollout(w1, w2, u, k_top=2, k_bottom=1, chunk=2, layout=layout, hidden=hid)
         xd = torch.from_numpy(noise).to(DEV)
         r, top, bottom, rn = ro.run(xd)
         torch.cuda.synchronize()
@@ -93,7 +103,8 @@ def test_two_stream_schedule_matches_one_stream(gpu_lib, n_cand):
     """The two-stream schedule (GEMMs and quantizers of the two halves
     overlapped through device-side events) reproduces the one-stream
     schedule bit for bit: every kernel's rows are independent of chunking.
-    Odd candidate counts give unequal halves; 300 tokens give ragged panels."""
+    Odd candidate counts give unequal halves; 300 tokens give ragged panels.
+    The two-stream schedule stores the hidden activation as bf16."""
     seed, tokens, dim, hidden = 6, 300, 256, 1024
     noise = np.stack([inputs.rollout_noise(seed, c, tokens, dim) for c in range(n_cand)])
     ws = [inputs.rollout_weights(seed, b, dim, hidden) for b in range(4)]
@@ -102,7 +113,7 @@ def test_two_stream_schedule_matches_one_stream(gpu_lib, n_cand):
     w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
     outs = []
     for overlap in (True, False):
-        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, overlap=overlap)
+        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, overlap=overlap, hidden="bf16")
         nd = torch.from_numpy(noise).to(DEV)
         work = torch.empty_like(nd)
         for _ in range(2):  # a second run reuses every buffer
@@ -114,7 +125,8 @@ def test_two_stream_schedule_matches_one_stream(gpu_lib, n_cand):
     np.testing.assert_array_equal(outs[0][5], noise)  # noise left intact
 
 
-def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
+@pytest.mark.parametrize("hid", ["f32", "bf16"])
+def test_fused_gelu_rollout_matches_row_layout(gpu_lib, hid):
     """Row counts that are multiples of 256 (2 candidates x 256 tokens per
     chunk) take the fused first linear (GEMM + GELU + MXFP4 in one call) and
     the fused Euler step on the panel layout; the row-major path runs every
@@ -129,7 +141,7 @@ def test_fused_gelu_rollout_matches_row_layout(gpu_lib):
     w2 = [torch.from_numpy(w[1]).to(DEV).bfloat16() for w in ws]
     outs = []
     for layout in ("panel", "row"):
-        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, chunk=2, layout=layout, fuse_reward=False)
+        ro = Fp4Rollout(w1, w2, u, k_top=1, k_bottom=1, chunk=2, layout=layout, fuse_reward=False, hidden=hid)
         xd = torch.from_numpy(noise).to(DEV)
         r, top, bottom, rn = ro.run(xd)
         torch.cuda.synchronize()
