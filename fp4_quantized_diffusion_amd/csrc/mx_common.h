@@ -114,14 +114,16 @@ __device__ __forceinline__ float gelu_bf16(float z, const float* tab) {
 // GELU of an fp32 input through a table of (Q(a), phi(a)) at the bf16
 // magnitudes a from 2^-10 to 16: 14 binades of 128 values plus 16 itself,
 // 1793 entries (14 KiB in LDS), Q = phi_tail(a). With a_c the bf16 rounding
-// of |z| clamped to [2^-10, 16] and d = |z| - a_c (|d| <= 2^-9 a_c above
-// 2^-10, |d| <= 2^-10 below; exact by Sterbenz where |z| >= a_c / 2), the
-// fourth-order Taylor expansion
+// of |z| clamped to [2^-10, 16] and d = |z| - a_c (half a bf16 ulp above
+// 2^-10, |d| <= 2^-8 a_c; |d| <= 2^-10 below; exact by Sterbenz where
+// |z| >= a_c / 2), the fourth-order Taylor expansion
 //     Q(a_c + d) = Q - phi d [1 - a_c d / 2 + (a_c^2 - 1) d^2 / 6
 //                             + a_c (3 - a_c^2) d^3 / 24]
 // follows from Q^(1) = -phi, Q^(2) = a phi, Q^(3) = (1 - a^2) phi,
-// Q^(4) = (a^3 - 3 a) phi. The next term, phi (a^4 - 6 a^2 + 3) d^5 / 120, is
-// below 1.5e-8 of Q for |z| <= 6 (Q / phi >= a / (a^2 + 1)); the rounding of
+// Q^(4) = (a^3 - 3 a) phi. What it leaves out, about
+// phi (a^4 - 6 a^2 + 3) d^5 / 120, is below 6e-8 of Q for |z| <= 6 (largest
+// just below 6; below 2e-10 for |z| <= 4; a float64 evaluation of the
+// expansion at 4 million points against erfc gives 5.5e-8); the rounding of
 // the expansion adds a few fp32 ulps of phi d, so the result carries
 // phi_tail's error (about 5e-7 relative). At the table's points (d = 0) the
 // result is phi_tail's, bit for bit. Beyond |z| = kGeluTaylorMax the callers
