@@ -672,9 +672,10 @@ def rollout_step_kernels(x, v, u, cfg):
 
 def gelu_epilogue_variants(x, w1, cfg):
     """The first linear's fused GELU + MXFP4 epilogue at the rollout's size,
-    two ways: GELU of bf16(C) from the LDS table (the default) and GELU of the
-    fp32 sums (fp4_gemm_panel_gelu_f32, the oracle's reading), each timed
-    alone. x: fp32 [rows, dim]; w1: the first block's bf16 weight."""
+    two ways: GELU of the fp32 sums (fp4_gemm_panel_gelu_f32, the default and
+    the oracle's reading) and GELU of bf16(C) from the LDS table
+    (fp4_gemm_panel_gelu), each timed alone. x: fp32 [rows, dim]; w1: the
+    first block's bf16 weight."""
     import fp4_quantized_diffusion_amd as fq
     a1 = fq.quantize(x, "mx", prologue="rmsnorm", layout="panel")
     wq = fq.quantize(w1, "mx", layout="panel")
@@ -683,8 +684,27 @@ def gelu_epilogue_variants(x, w1, cfg):
     t_f32 = time_launches([lambda: fq.gemm_gelu(a1, wq, out=out, exact=True)], reps=10)
     flop = 2.0 * x.shape[0] * cfg["dim"] * cfg["hidden"]
     return {"shape": [x.shape[0], cfg["dim"], cfg["hidden"]],
-            "bf16_table_us": [round(a, 1) for a in t_tab], "f32_erfc_us": [round(a, 1) for a in t_f32],
-            "bf16_table_tflops": round(flop / t_tab[0] / 1e6, 1), "f32_erfc_tflops": round(flop / t_f32[0] / 1e6, 1)}
+            "f32_us": [round(a, 1) for a in t_f32], "bf16_table_us": [round(a, 1) for a in t_tab],
+            "f32_tflops": round(flop / t_f32[0] / 1e6, 1), "bf16_table_tflops": round(flop / t_tab[0] / 1e6, 1)}
+
+
+def other_hidden_rollout(noise, work, w1, w2, u, cfg, chunk, layout, steps=3):
+    """The same rollout with the other reading of the hidden activation
+    (bf16 when the run's is fp32), timed the same way, outside the main timed
+    region: its rate, and how its rewards rank against the main run's."""
+    import torch
+    from fp4_quantized_diffusion_amd.rollout import Fp4Rollout
+    other = "bf16" if cfg["hidden_act"] == "f32" else "f32"
+    ro = Fp4Rollout(w1, w2, u, steps=cfg["steps"], k_top=cfg["k_top"], k_bottom=cfg["k_bottom"], chunk=chunk,
+                    layout=layout, hidden=other)
+    ro.run(noise, work)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r, top, bottom, _ = ro.run(noise, work)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    return other, sec, r
 
 
 def run_config(args):
@@ -731,6 +751,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warmup, run one device copy of MIB MiB (a known-size kernel for scaling "
                          "profiler byte counters); not part of any step")
+    ap.add_argument("--no-other-hidden", action="store_true",
+                    help="skip the comparison rollout with the other reading of the hidden activation")
     ap.add_argument("--no-traffic", action="store_true",
                     help="skip the live GEMM byte-counter passes (roofline.traffic then comes from the profile)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
@@ -879,6 +901,17 @@ def main():
                                                            u, cfg)
         out["rollout_step_kernels"]["gelu_epilogue"] = gelu_epilogue_variants(noise.view(-1, cfg["dim"]), w1[0], cfg)
         log(f"standalone step kernels: {time.time() - t0:.1f}s")
+    if not args.no_other_hidden and not args.overlap:
+        # the other reading of the hidden activation, for comparison (not the headline: a different network)
+        from fp4_quantized_diffusion_amd import stage2
+        t0 = time.time()
+        other, osec, r_other = other_hidden_rollout(noise, work, w1, w2, u, cfg, chunk, args.layout)
+        out["other_hidden_rollout"] = {
+            "hidden_activation": other, "ms_per_step": round(osec * 1e3, 3),
+            "candidates_per_s": round(cfg["n_cand"] / osec, 4),
+            "rank_agreement_with_headline": stage2.rank_stats(r_other.cpu().numpy(), rewards.cpu().numpy(),
+                                                             cfg["k_top"])}
+        log(f"rollout with the {other} hidden activation: {osec * 1e3:.1f} ms/step [{time.time() - t0:.1f}s]")
     if not args.no_rank_agreement:
         from fp4_quantized_diffusion_amd import stage2
         try:
