@@ -284,6 +284,45 @@ def test_mx_gelu_negative_tail(gpu_lib, layout):
 
 
 @pytest.mark.parametrize("layout", ["row", "panel"])
+def test_mx_gelu_fp32_table_ranges(gpu_lib, layout):
+    """Fused GELU on fp32 input, whose value comes from a (Q, phi) table at
+    bf16 points from 2^-10 to 16 and a fourth-order expansion, or from the
+    evaluated erfc beyond |z| = 6. Each 32-block is drawn from one narrow band,
+    so its scale and codes are set by GELU's relative accuracy there: every
+    binade from 2^-14 (below the table's first point, where the expansion
+    runs from 2^-10) to 4, both signs; [4, 6); a band straddling 6, where the
+    elements of one block take both paths; [6, 12); and blocks mixing signed
+    zeros and subnormals with normal values. Same 2e-6 decision band as the
+    other fused-prologue tests; zeros keep their sign (code 0x0 or 0x8)."""
+    rng = np.random.default_rng(23)
+    bands = [(2.0 ** e, 2.0 ** (e + 1)) for e in range(-14, 2)] + [(4.0, 6.0), (5.9, 6.1), (6.0, 12.0)]
+    rows_per = 8
+    blocks = []
+    for lo, hi in bands:
+        for sign in (1.0, -1.0):
+            blocks.append(sign * rng.uniform(lo, hi, size=(rows_per, 128)))
+    special = rng.standard_normal((rows_per, 128))
+    special[:, 0::4] = 0.0
+    special[:, 1::4] = -0.0
+    special[:, 2::8] = 1e-40                        # fp32 subnormal
+    special[:, 6::8] = -3e-39
+    blocks.append(special)
+    x = np.concatenate(blocks).astype(np.float32)
+    rows, k = x.shape
+    q = gpu_lib.quantize(torch.from_numpy(x).to(DEV), "mx", prologue="gelu", layout=layout)
+    if layout == "panel":
+        gc, gs, _ = panel_to_rows(to_np(q.codes), to_np(q.scales), rows, k)
+    else:
+        gc, gs = to_np(q.codes)[:, : k // 2], to_np(q.scales)[:, : k // 32]
+    bad, flips = mx_codes_near_boundary_ok(orollout.gelu(x.astype(np.float64)), gc, gs)
+    assert bad == 0, (bad, flips)
+    nib = np.empty((rows, k), np.uint8)
+    nib[:, 0::2], nib[:, 1::2] = gc & 0xF, gc >> 4
+    z = x == 0
+    assert (nib[z & ~np.signbit(x)] == 0x0).all() and (nib[z & np.signbit(x)] == 0x8).all()
+
+
+@pytest.mark.parametrize("layout", ["row", "panel"])
 def test_mx_gelu_every_bf16_value(gpu_lib, layout):
     """Fused GELU on bf16 input over every finite bf16 value: 32-blocks of
     consecutive bit patterns (one binade and sign per block) cover both
