@@ -300,6 +300,50 @@ def measure_counters(cfg, timeout_s=420):
             "sclk_GHz": round(clk, 3), "mfma_busy": round(busy, 4), "class_gemms": per_class}, None
 
 
+class PowerSampler:
+    """Socket power during a region, sampled by `amd-smi metric -p` in a
+    background thread (a child process per sample, 2 s timeout each); empty
+    where amd-smi is missing or reports nothing."""
+
+    def __init__(self, period_s=0.1):
+        import shutil
+        self.cmd = shutil.which("amd-smi")
+        self.period = period_s
+        self.samples = []
+
+    def _loop(self):
+        import re
+        import subprocess
+        while not self.stop.is_set():
+            try:
+                r = subprocess.run([self.cmd, "metric", "-p", "--json"], capture_output=True, text=True, timeout=2)
+                m = re.search(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', r.stdout)
+                if m:
+                    self.samples.append(float(m.group(1)))
+            except (subprocess.SubprocessError, OSError):
+                return
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._loop, daemon=True) if self.cmd else None
+        if self.thread:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread:
+            self.thread.join(timeout=5)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"socket_W_mean": round(sum(self.samples) / len(self.samples), 1), "socket_W_max": max(self.samples),
+                "samples": len(self.samples), "source": "amd-smi metric -p, every 0.1 s over the timed steps"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -818,11 +862,12 @@ def main():
         log(f"warmup step {i + 1}/{args.warmup} done")
     timer.enabled = True
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        rewards, top, bottom, rn = ro.run(noise, work)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with PowerSampler() as power:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            rewards, top, bottom, rn = ro.run(noise, work)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     sec = (t1 - t0) / args.steps
     top_l, bottom_l = top.tolist(), bottom.tolist()
     log(f"timed {args.steps} steps: {sec * 1e3:.1f} ms/step; top {top_l[:4]}... bottom {bottom_l[:4]}...")
@@ -872,6 +917,7 @@ def main():
         "gemm_tflops": round(achieved / 1e12, 2),
         "gemm_frac_of_mxfp4_peak": round(achieved / PEAK_FP4, 4),
         "kernels": kernels,
+        "power": power.summary(),
     }
     if counters is not None:
         # the spec peak scaled to the shader clock the GEMMs ran at (counter pass of this run)

@@ -170,3 +170,10 @@ def test_run_config_keeps_sizes_apart_from_options(bench):
     cfg, _, default = bench.run_config(argparse.Namespace(tokens=4096, hidden="bf16", overlap=False, chunk=0,
                                                           layout="panel"))
     assert not default and bench.gemm_variants(cfg)["gelu_mxfp4"][0] == "gemm_fp4_kernel<0, 3, 2>"
+
+
+def test_power_sampler_without_amd_smi(bench, monkeypatch, tmp_path):
+    monkeypatch.setenv("PATH", str(tmp_path))
+    with bench.PowerSampler() as p:
+        pass
+    assert p.summary() is None
