@@ -56,7 +56,11 @@ typedef int32_t fp4_status;
 
 /* fp4_quantize flags */
 #define FP4_PRO_RMSNORM        0x1   /* quantize x * (mean_k(x^2) + 1e-6)^(-1/2) (row-wise, unit gain) */
-#define FP4_PRO_GELU           0x2   /* quantize 0.5 x (1 + erf(x / sqrt 2)) */
+#define FP4_PRO_GELU           0x2   /* quantize x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)). bf16 x: Phi(-|x|)
+                                        from a table at every bf16 magnitude in [2^-22, 16]. fp32 x:
+                                        the table entry at the bf16 rounding of |x| in [2^-10, 16]
+                                        carried to |x| by a 4th-order expansion; erfc evaluated
+                                        where |x| > 6. Relative error about 5e-7 either way */
 #define FP4_TENSOR_SCALE_GIVEN 0x100 /* NV: read s_g from *tensor_scale instead of computing it */
 #define FP4_LAYOUT_PANEL       0x200 /* MX: write codes and scales in the panel layout (below) */
 
@@ -256,14 +260,15 @@ FP4_API fp4_status fp4_gemm_panel(int fmt, const uint8_t* a_codes, const uint8_t
 
 /*
  * fp4_gemm_panel_gelu -- the first solver linear of a velocity block with the
- * GELU and the MXFP4 quantization of its output in its epilogue: the codes
- * and scales of GELU(bf16(A_hat B_hat^T)) in the panel layout of an [m, n]
- * operand, ready for the block's second linear (project page, "Two-Stage
- * Pipeline": every solver linear runs FP4 x FP4; the synthetic velocity block
- * is h + W2 GELU(W1 RMSNorm(h))). The hidden activation is rounded to bf16
- * before the GELU, as the unfused path stores it, so the output is
- * bit-identical to fp4_gemm_panel(..., FP4_DT_BF16) into z followed by
+ * GELU and the MXFP4 quantization of its output in its epilogue, for the
+ * reading in which the hidden activation is stored as bf16 between the two
+ * linears: the codes and scales of GELU(bf16(A_hat B_hat^T)) in the panel
+ * layout of an [m, n] operand, ready for the block's second linear (project
+ * page, "Two-Stage Pipeline": every solver linear runs FP4 x FP4; the
+ * synthetic velocity block is h + W2 GELU(W1 RMSNorm(h))). Bit-identical to
+ * fp4_gemm_panel(..., FP4_DT_BF16) into z followed by
  * fp4_quantize(z, FP4_LAYOUT_PANEL | FP4_PRO_GELU) -- without writing z.
+ * The rollout's default is fp4_gemm_panel_gelu_f32; this is its option.
  *   fmt, a_*, b_*, m, n, k  as in fp4_gemm_panel; m and n multiples of 256
  *                           (otherwise FP4_UNSUPPORTED: use the unfused pair).
  *   out_codes, out_scales   the panel layout of [m, n] (fp4_panel_bytes(m, n)
@@ -277,12 +282,16 @@ FP4_API fp4_status fp4_gemm_panel_gelu(int fmt, const uint8_t* a_codes, const ui
 /*
  * fp4_gemm_panel_gelu_f32 -- fp4_gemm_panel_gelu with GELU evaluated on the
  * fp32 sums themselves (no bf16 rounding of the hidden activation): the
- * reading in which the hidden activation stays fp32 between the two linears.
- * Bit-identical to fp4_gemm_panel(..., FP4_DT_F32) into z followed by
- * fp4_quantize(z, FP4_LAYOUT_PANEL | FP4_PRO_GELU). GELU is z Phi(z) with the
- * complementary error function evaluated per element (relative error about
- * 5e-7), so the epilogue does about three times the arithmetic of
- * fp4_gemm_panel_gelu's table lookup. Arguments as fp4_gemm_panel_gelu.
+ * reading in which the hidden activation stays fp32 between the two linears,
+ * and the first linear of the rollout by default. Bit-identical to
+ * fp4_gemm_panel(..., FP4_DT_F32) into z followed by
+ * fp4_quantize(z, FP4_LAYOUT_PANEL | FP4_PRO_GELU). GELU is z Phi(z): Phi(-|z|)
+ * from the workgroup's LDS table of (Phi(-a), phi(a)) at the bf16 magnitudes
+ * a in [2^-10, 16], taken at a_c = the bf16 rounding of |z| and carried to |z|
+ * by the fourth-order Taylor expansion in d = |z| - a_c (truncation below
+ * 6e-8 relative); where |z| > 6 (or z is NaN) the complementary error
+ * function is evaluated for that element instead. Relative error about 5e-7
+ * overall; the value depends on z alone. Arguments as fp4_gemm_panel_gelu.
  */
 FP4_API fp4_status fp4_gemm_panel_gelu_f32(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales,
