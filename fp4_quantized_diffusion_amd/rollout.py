@@ -23,9 +23,11 @@ step are one call,
 fp4_gemm_panel_euler(A2, W2q, residual = h, x) -> x_next, which applies
 x + dt (h + A2 W2q^T) in the GEMM's epilogue -- bit-identical to the GEMM into
 v followed by euler_step, without writing v or reading it back. The hidden
-activation z stays fp32, as in the float64 oracle's reading; hidden="bf16"
-rounds it to bf16 first (fp4_gemm_panel_gelu, a GELU table in LDS, faster,
-but not the oracle's arithmetic: at 96 x 4096 x 3072 the final state then
+activation z stays fp32, as in the float64 oracle's reading (GELU from an
+LDS table of (Q, phi) at bf16 points carried to z by a fourth-order
+expansion, erfc evaluated beyond |z| = 6); hidden="bf16" rounds it to bf16
+first (fp4_gemm_panel_gelu, one table read per value, faster -- 370-400 ms
+per rollout step against about 460 -- but not the oracle's arithmetic: at 96 x 4096 x 3072 the final state then
 differs from the oracle's by about a quarter, because the rounding moves
 about one hidden value in a hundred across an FP4 decision point and the
 next blocks' quantizers amplify that). The FP4 operands use the panel layout by default
@@ -47,9 +49,9 @@ wave per SIMD), so they overlap it. Every kernel computes rows independently
 of how the rows are chunked, so the result is bit-identical to the
 one-stream schedule. Both streams run at the default priority. On MI355X
 this schedule measured slower than the one-stream schedule of the same
-(unfused) kernels for the 96 x 4096 x 3072 rollout (534 vs 523 ms per step;
-the fused path with a bf16 hidden activation took 370-381 ms): the GEMM runs at the card's power
-limit, and the overlapped quantizers lower the clock and slow the GEMM by
+(unfused) kernels for the 96 x 4096 x 3072 rollout (534 vs 523 ms per step,
+where the fused one-stream path takes 370-400 ms with the same bf16 hidden
+activation): the GEMM runs at the card's power limit, and the overlapped quantizers lower the clock and slow the GEMM by
 more than they hide; it is kept as an option.
 
 Every call enqueues on the current stream (and the second stream, which the
@@ -79,13 +81,13 @@ class Fp4Rollout:
         it is called with the launch's stream current.
         hidden: "f32" (default) keeps the first linear's output fp32 into
         GELU, the float64 oracle's reading of the hidden activation (the
-        fused epilogue evaluates erfc on the fp32 sums,
-        fp4_gemm_panel_gelu_f32; the unfused path stores z as fp32). "bf16"
-        rounds it to bf16 before GELU (the fused epilogue reads a table in
-        LDS, fp4_gemm_panel_gelu; the unfused path stores z as bf16): about
-        a third of the epilogue arithmetic, but a different network -- the
-        rounding moves hidden values across FP4 decision points, which the
-        following quantizers amplify."""
+        fused epilogue, fp4_gemm_panel_gelu_f32, takes GELU of the fp32 sums
+        from a (Q, phi) table and a fourth-order expansion; the unfused path
+        stores z as fp32). "bf16" rounds it to bf16 before GELU (the fused
+        epilogue, fp4_gemm_panel_gelu, reads one table entry per value; the
+        unfused path stores z as bf16): about half the epilogue arithmetic,
+        but a different network -- the rounding moves hidden values across
+        FP4 decision points, which the following quantizers amplify."""
         if fmt != "mx":
             raise ValueError("the rollout's fused quantize prologues are implemented for MXFP4")
         self.w1, self.w2, self.u = list(w1), list(w2), u
