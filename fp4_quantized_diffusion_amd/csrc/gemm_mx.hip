@@ -740,9 +740,9 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // leave as 2 KiB contiguous (two 16-byte stores per lane), the 4 scale bytes
 // of a row as one 4-byte store.
 // EXACT: GELU of the fp32 sum itself (no bf16 rounding: the table's entry
-// near it and a Taylor expansion, gelu_f32_tab_n) -- the operations of an
-// fp32-out GEMM followed by fp4_quantize(GELU prologue) on its fp32 output,
-// so the same bits.
+// near it and a Taylor expansion, gelu_f32_fetch / gelu_f32_finish, as in
+// gelu_f32_tab_n) -- the operations of an fp32-out GEMM followed by
+// fp4_quantize(GELU prologue) on its fp32 output, so the same bits.
 // Quantize the 16 GELU values g of MFMA tile (i, j) (this lane's half of
 // a 32-block) and stage the wave's codes; returns the block's scale byte.
 __device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* stage, int r32, int h) {
@@ -784,20 +784,36 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
   uint8_t* qc = p.qc + blk * 16384;
   uint8_t* qs = p.qs + blk * 1024;
   if constexpr (EXACT) {
-    // compile-time tile indices: gelu_f32_tab_n holds a loop, and an (i, j)
-    // loop around it would stay rolled, indexing the accumulators at run time
-    static_for<0, 4>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      uint32_t sreg = 0;
-      static_for<0, 4>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        float z[16], g[16];
+    // compile-time tile indices (an (i, j) loop would stay rolled around the
+    // fallback loop, indexing the accumulators at run time); the table reads
+    // of the next 16 values are in flight while the current ones are
+    // evaluated and quantized
+    GeluBatch<16> cur;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = acc_read(acc[i][j][e]);
-        gelu_f32_tab_n<16>(g, z, tab2);
+    for (int e = 0; e < 16; ++e) cur.z[e] = acc_read(acc[0][0][e]);
+    gelu_f32_fetch(cur, tab2);
+    uint32_t sreg = 0;
+    static_for<0, 16>([&](auto gc) {
+      constexpr int G = decltype(gc)::value, j = G / 4, i = G % 4;
+      auto finish = [&](const GeluBatch<16>& b) {
+        float g[16];
+        gelu_f32_finish(g, b);
         sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
-      });
-      gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+        if constexpr (i == 3) {
+          gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+          sreg = 0;
+        }
+      };
+      if constexpr (G + 1 < 16) {
+        GeluBatch<16> nxt;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) nxt.z[e] = acc_read(acc[(G + 1) % 4][(G + 1) / 4][e]);
+        gelu_f32_fetch(nxt, tab2);
+        finish(cur);
+        cur = nxt;
+      } else {
+        finish(cur);
+      }
     });
   } else {
 #pragma unroll

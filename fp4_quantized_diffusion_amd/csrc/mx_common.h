@@ -140,52 +140,89 @@ __device__ __forceinline__ void gelu_table_fill(float2* tab) {
   }
 }
 
-// mag16: the magnitude bits of the bf16 rounding (nearest even) of z. Valid
-// for |z| <= kGeluTaylorMax (see above).
-__device__ __forceinline__ float gelu_f32_tab(float z, uint32_t mag16, const float2* tab) {
+// pat: the bit pattern of the bf16 rounding (nearest even) of |z| in the
+// upper half of the word, the lower half zero, so that it reads as that
+// value in fp32; clamped, it is a_c itself and, shifted, the table index.
+// The bracket of the expansion above is evaluated in x = a_c d,
+//     1 - x/2 + x^2/6 - x^3/24 + d^2 (x/8 - 1/6),
+// the same polynomial term by term (a_c d^2 = x d, a_c^2 d^2 = x^2,
+// a_c^3 d^3 = x^3). gelu_f32_from is valid for |z| <= kGeluTaylorMax.
+__device__ __forceinline__ uint32_t gelu_tab_clamp(uint32_t pat) {
+  return min(max(pat, kGeluTLo << 16), kGeluHi << 16);  // any pattern, NaN included, stays in the table
+}
+__device__ __forceinline__ float2 gelu_tab_entry(uint32_t pat, const float2* tab) {
+  return tab[(gelu_tab_clamp(pat) >> 16) - kGeluTLo];
+}
+__device__ __forceinline__ float gelu_f32_from(float z, uint32_t pat, float2 t) {
 #pragma clang fp contract(off)
-  const uint32_t m = min(max(mag16, kGeluTLo), kGeluHi);  // any pattern, NaN included, stays in the table
-  const float2 t = tab[m - kGeluTLo];
-  const float ac = __uint_as_float(m << 16);
+  const float ac = __uint_as_float(gelu_tab_clamp(pat));
   const float d = fabsf(z) - ac;
-  const float s = ac * ac;
-  float b = fmaf(ac * fmaf(s, -1.0f / 24.0f, 0.125f), d, fmaf(s, 1.0f / 6.0f, -1.0f / 6.0f));
-  b = fmaf(b, d, -0.5f * ac);
-  b = fmaf(b, d, 1.0f);
+  const float x = ac * d;
+  float b = fmaf(fmaf(fmaf(x, -1.0f / 24.0f, 1.0f / 6.0f), x, -0.5f), x, 1.0f);
+  b = fmaf(d * d, fmaf(x, 0.125f, -1.0f / 6.0f), b);
   return gelu_q(z, fmaf(-t.y, b * d, t.x));
 }
 
-// GELU of N (even) fp32 values through the table: the expansion where
-// |z| <= kGeluTaylorMax, the evaluated erfc elsewhere (a branch that lanes
-// skip unless one of their N values is that large). The bf16 roundings come
-// from the hardware's nearest-even pair conversion.
+// GELU of N (even) fp32 values through the table, in two parts so that a
+// caller can issue the table reads of one batch before it evaluates the
+// previous one: gelu_f32_fetch forms the indices and issues the reads,
+// gelu_f32_finish evaluates the expansion where |z| <= kGeluTaylorMax and
+// the evaluated erfc elsewhere (a branch that lanes skip unless one of their
+// N values is that large or NaN: the IEEE maximum propagates NaN). The bf16
+// roundings come from the hardware's nearest-even pair conversion.
 template <int N>
-__device__ __forceinline__ void gelu_f32_tab_n(float* g, const float* z, const float2* tab) {
-  float m = 0.0f;
+struct GeluBatch {
+  float z[N];
+  uint32_t p[N];
+  float2 t[N];
+  float m;
+};
+
+template <int N>
+__device__ __forceinline__ void gelu_f32_fetch(GeluBatch<N>& b, const float2* tab) {
+  b.m = 0.0f;
 #pragma unroll
   for (int e = 0; e < N; e += 2) {
-    uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)z[e], (__bf16)z[e + 1]});
+    uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)b.z[e], (__bf16)b.z[e + 1]});
     asm("" : "+v"(u));  // one pair conversion
-    g[e] = gelu_f32_tab(z[e], u & 0x7FFFu, tab);
-    g[e + 1] = gelu_f32_tab(z[e + 1], (u >> 16) & 0x7FFFu, tab);
-    m = fmaxf(m, fmaxf(fabsf(z[e]), fabsf(z[e + 1])));
+    u &= 0x7FFF7FFFu;   // the magnitudes (nearest-even rounding is symmetric)
+    b.p[e] = u << 16;
+    b.p[e + 1] = u & 0xFFFF0000u;
+    b.m = __builtin_elementwise_maximum(b.m, __builtin_elementwise_maximum(fabsf(b.z[e]), fabsf(b.z[e + 1])));
   }
-  if (!(m <= kGeluTaylorMax)) {  // NaN goes this way too
+#pragma unroll
+  for (int e = 0; e < N; ++e) b.t[e] = gelu_tab_entry(b.p[e], tab);
+}
+
+template <int N>
+__device__ __forceinline__ void gelu_f32_finish(float* g, const GeluBatch<N>& b) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) g[e] = gelu_f32_from(b.z[e], b.p[e], b.t[e]);
+  if (!(b.m <= kGeluTaylorMax)) {
     // One evaluation per trip of a loop that stays rolled, so the code stays
     // small wherever this is inlined; the value is picked out and put back
     // by selects on compile-time positions (no register array is indexed
     // by a run-time value, which would move it to scratch memory).
 #pragma unroll 1
     for (int e = 0; e < N; ++e) {
-      float ze = z[0];
+      float ze = b.z[0];
 #pragma unroll
-      for (int k = 1; k < N; ++k) ze = k == e ? z[k] : ze;
+      for (int k = 1; k < N; ++k) ze = k == e ? b.z[k] : ze;
       const float r = gelu_erfc(ze);
       const bool tail = !(fabsf(ze) <= kGeluTaylorMax);
 #pragma unroll
       for (int k = 0; k < N; ++k) g[k] = (k == e && tail) ? r : g[k];
     }
   }
+}
+
+template <int N>
+__device__ __forceinline__ void gelu_f32_tab_n(float* g, const float* z, const float2* tab) {
+  GeluBatch<N> b;
+#pragma unroll
+  for (int e = 0; e < N; ++e) b.z[e] = z[e];
+  gelu_f32_fetch(b, tab);
+  gelu_f32_finish(g, b);
 }
 
 // Bits of max |v_j| by the IEEE maximum (v_maximum3_f32, absolute values as
