@@ -303,11 +303,23 @@ def measure_counters(cfg, timeout_s=420):
 class PowerSampler:
     """Socket power during a region, sampled by `amd-smi metric -p` in a
     background thread (a child process per sample, 2 s timeout each); empty
-    where amd-smi is missing or reports nothing."""
+    where amd-smi is missing or reports nothing.
+
+    amd-smi is a Python script: it is started with this interpreter directly,
+    so no launcher process replaces itself with another program. Under a
+    profiler nothing is sampled: the profiler's preloaded library would
+    initialise the GPU in every child process."""
 
     def __init__(self, period_s=0.1):
+        import os
         import shutil
-        self.cmd = shutil.which("amd-smi")
+        path = shutil.which("amd-smi")
+        self.cmd = None
+        if path and not _under_profiler():
+            path = os.path.realpath(path)
+            with open(path, "rb") as f:
+                first = f.readline()
+            self.cmd = [sys.executable, path] if first.startswith(b"#!") and b"python" in first else [path]
         self.period = period_s
         self.samples = []
 
@@ -316,7 +328,7 @@ class PowerSampler:
         import subprocess
         while not self.stop.is_set():
             try:
-                r = subprocess.run([self.cmd, "metric", "-p", "--json"], capture_output=True, text=True, timeout=2)
+                r = subprocess.run([*self.cmd, "metric", "-p", "--json"], capture_output=True, text=True, timeout=2)
                 m = re.search(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', r.stdout)
                 if m:
                     self.samples.append(float(m.group(1)))

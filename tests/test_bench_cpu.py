@@ -177,3 +177,19 @@ def test_power_sampler_without_amd_smi(bench, monkeypatch, tmp_path):
     with bench.PowerSampler() as p:
         pass
     assert p.summary() is None
+
+
+def test_power_sampler_is_off_under_a_profiler(bench, monkeypatch):
+    # the profiler's preloaded library would initialise the GPU in each amd-smi child
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/librocprofiler-sdk-tool.so")
+    assert bench.PowerSampler().cmd is None
+
+
+def test_power_sampler_starts_a_python_script_with_this_interpreter(bench, monkeypatch, tmp_path):
+    import sys
+    script = tmp_path / "amd-smi"
+    script.write_text("#!/usr/bin/env python3\nprint('{}')\n")
+    script.chmod(0o755)
+    monkeypatch.setenv("PATH", str(tmp_path))
+    monkeypatch.delenv("LD_PRELOAD", raising=False)
+    assert bench.PowerSampler().cmd == [sys.executable, str(script)]
