@@ -745,7 +745,13 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // fp4_quantize(GELU prologue) on its fp32 output, so the same bits.
 // Quantize the 16 GELU values g of MFMA tile (i, j) (this lane's half of
 // a 32-block) and stage the wave's codes; returns the block's scale byte.
-__device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* stage, int r32, int h) {
+// HW: the hardware converter only, with `rare` set where the block's scale
+// byte S is below 103 (amax below 2^-22, which includes the ALU path's
+// blocks, S <= 2) or above 252 (an infinite or NaN value): the caller
+// redoes those with the exact treatment of every value and block.
+template <bool HW = false>
+__device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* stage, int r32, int h,
+                                                  bool* rare = nullptr) {
   uint32_t am = amax_bits<16>(g);
   {  // the other lane half's amax: one of each swapped pair is this lane's own
     const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
@@ -754,7 +760,16 @@ __device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* s
   const uint32_t S = mx_scale(am);
   // x: block bytes 2h, 2h+1, 4+2h, 5+2h (q = 0, 1); y: the same for q = 2, 3.
   // After the swap lane half 0 holds x of both halves, half 1 y of both.
-  const auto xy = __builtin_amdgcn_permlane32_swap(mx_pack8(g, S), mx_pack8(g + 8, S), false, false);
+  uint32_t x, y;
+  if constexpr (HW) {
+    *rare |= S - 103u > 149u;
+    x = mx_pack8_hw(g, S);
+    y = mx_pack8_hw(g + 8, S);
+  } else {
+    x = mx_pack8(g, S);
+    y = mx_pack8(g + 8, S);
+  }
+  const auto xy = __builtin_amdgcn_permlane32_swap(x, y, false, false);
   const uint32_t w0 = __builtin_amdgcn_perm(xy[1], xy[0], 0x05040100u);
   const uint32_t w1 = __builtin_amdgcn_perm(xy[1], xy[0], 0x07060302u);
   *reinterpret_cast<uint2*>(stage + r32 * kQPitch + 16 * i + 8 * h) = make_uint2(w0, w1);
@@ -775,6 +790,54 @@ __device__ __forceinline__ void gelu_rows_out(uint8_t* qc, uint8_t* qs, int m0, 
   __builtin_amdgcn_sched_barrier(0);  // the next rows' staging writes stay behind these reads
 }
 
+// The wave's 16 MFMA tiles as one compile-time sequence (compile-time tile
+// indices keep the accumulators in registers; an (i, j) loop around the
+// erfc fallback's loop stayed rolled, indexing them at run time), with the
+// table reads of the next 16 values in flight while the current ones are
+// evaluated and quantized. FAST: no branches, `rare` as described where this
+// is called; otherwise the exact treatment of every value and block.
+template <bool FAST>
+__device__ __forceinline__ void gelu_tile_f32(v16f acc[4][4], uint8_t* qc, uint8_t* qs, int m0, uint8_t* stage,
+                                              const float2* tab2, bool* rare) {
+  // each pass forms its own lane-dependent addresses, so that none is held
+  // from the first pass through the second
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int r32 = lane & 31, h = lane >> 5;
+  GeluBatch<16> cur;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cur.z[e] = acc_read(acc[0][0][e]);
+  gelu_f32_fetch<16, !FAST>(cur, tab2);
+  uint32_t sreg = 0;
+  static_for<0, 16>([&](auto gc) {
+    constexpr int G = decltype(gc)::value, j = G / 4, i = G % 4;
+    auto finish = [&](const GeluBatch<16>& b) {
+      float g[16];
+      if constexpr (FAST) {
+        gelu_f32_expand(g, b);
+        sreg |= gelu_block_mx<true>(g, i, stage, r32, h, rare) << (8 * i);
+      } else {
+        gelu_f32_finish(g, b);
+        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
+      }
+      if constexpr (i == 3) {
+        gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+        sreg = 0;
+      }
+    };
+    if constexpr (G + 1 < 16) {
+      GeluBatch<16> nxt;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) nxt.z[e] = acc_read(acc[(G + 1) % 4][(G + 1) / 4][e]);
+      gelu_f32_fetch<16, !FAST>(nxt, tab2);
+      finish(cur);
+      cur = nxt;
+    } else {
+      finish(cur);
+    }
+  });
+}
+
 template <bool EXACT>
 __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
                                                    uint8_t* stage, const float* tab, const float2* tab2) {
@@ -784,37 +847,30 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
   uint8_t* qc = p.qc + blk * 16384;
   uint8_t* qs = p.qs + blk * 1024;
   if constexpr (EXACT) {
-    // compile-time tile indices (an (i, j) loop would stay rolled around the
-    // fallback loop, indexing the accumulators at run time); the table reads
-    // of the next 16 values are in flight while the current ones are
-    // evaluated and quantized
-    GeluBatch<16> cur;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) cur.z[e] = acc_read(acc[0][0][e]);
-    gelu_f32_fetch(cur, tab2);
-    uint32_t sreg = 0;
-    static_for<0, 16>([&](auto gc) {
-      constexpr int G = decltype(gc)::value, j = G / 4, i = G % 4;
-      auto finish = [&](const GeluBatch<16>& b) {
-        float g[16];
-        gelu_f32_finish(g, b);
-        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
-        if constexpr (i == 3) {
-          gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
-          sreg = 0;
-        }
-      };
-      if constexpr (G + 1 < 16) {
-        GeluBatch<16> nxt;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) nxt.z[e] = acc_read(acc[(G + 1) % 4][(G + 1) / 4][e]);
-        gelu_f32_fetch(nxt, tab2);
-        finish(cur);
-        cur = nxt;
-      } else {
-        finish(cur);
-      }
-    });
+    // First a pass with no branch in it: the expansion for every value (no
+    // erfc beyond |z| = 6) and the hardware converter for every block. Its
+    // codes and scales are the exact ones unless some block's scale byte S
+    // is below 103 or above 252:
+    //   * for z > 6 both treatments give z, so those values agree;
+    //   * for z < -6 both give a negative value below 6e-9 or -0, and where
+    //     S >= 103 the block's amax is at least 2^-22 (set by a value that
+    //     both treatments share) and its scale at least 2^-24, so both
+    //     round to the negative zero code;
+    //   * NaN, infinite and overflowing values make the block's S 253.
+    // Such blocks do not occur in practice; where one does, somewhere in the
+    // wave's tile, the wave writes the whole tile again with the exact
+    // treatment (the same addresses from the same lanes, in program order,
+    // so the second writes are the ones that stay). A branch inside the
+    // pass would end the scheduler's region at every 16 values; without
+    // them the pass runs about 20% faster.
+    bool rare = false;
+    gelu_tile_f32<true>(acc, qc, qs, m0, stage, tab2, &rare);
+    if (__any(rare)) {
+      // a compiler memory barrier: nothing the first pass loaded is kept for
+      // the second, which would hold the whole tile's table entries at once
+      asm volatile("" ::: "memory");
+      gelu_tile_f32<false>(acc, qc, qs, m0, stage, tab2, nullptr);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

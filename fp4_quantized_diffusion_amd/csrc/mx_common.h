@@ -133,10 +133,13 @@ constexpr uint32_t kGeluTLo = (127u - 10u) << 7;  // bf16 magnitude bits of 2^-1
 constexpr int kGeluTTab = (int)(kGeluHi - kGeluTLo + 1);
 constexpr float kGeluTaylorMax = 6.0f;
 
+// Entries above kGeluTaylorMax are (0, 0): the exact treatment never reads
+// them (it evaluates erfc there), and with them the expansion gives exactly
+// z for z > 6 and -0 for z < -6 (see gelu_f32_expand).
 __device__ __forceinline__ void gelu_table_fill(float2* tab) {
   for (int e = threadIdx.x; e < kGeluTTab; e += blockDim.x) {
     const float a = __uint_as_float((kGeluTLo + (uint32_t)e) << 16);
-    tab[e] = make_float2(phi_tail(a), gauss_pdf(a));
+    tab[e] = a <= kGeluTaylorMax ? make_float2(phi_tail(a), gauss_pdf(a)) : make_float2(0.0f, 0.0f);
   }
 }
 
@@ -163,13 +166,16 @@ __device__ __forceinline__ float gelu_f32_from(float z, uint32_t pat, float2 t) 
   return gelu_q(z, fmaf(-t.y, b * d, t.x));
 }
 
-// GELU of N (even) fp32 values through the table, in two parts so that a
+// GELU of N (even) fp32 values through the table, in parts so that a
 // caller can issue the table reads of one batch before it evaluates the
-// previous one: gelu_f32_fetch forms the indices and issues the reads,
+// previous one: gelu_f32_fetch forms the indices and issues the reads;
 // gelu_f32_finish evaluates the expansion where |z| <= kGeluTaylorMax and
 // the evaluated erfc elsewhere (a branch that lanes skip unless one of their
-// N values is that large or NaN: the IEEE maximum propagates NaN). The bf16
-// roundings come from the hardware's nearest-even pair conversion.
+// N values is that large or NaN: the IEEE maximum propagates NaN). A caller
+// that keeps that branch out of its main sequence takes gelu_f32_expand
+// instead and redoes with gelu_f32_finish wherever the difference can show
+// (see gelu_f32_expand). The bf16 roundings come from the hardware's
+// nearest-even pair conversion.
 template <int N>
 struct GeluBatch {
   float z[N];
@@ -178,7 +184,9 @@ struct GeluBatch {
   float m;
 };
 
-template <int N>
+// MAX: also form b.m, the batch's largest |z| (NaN if any z is), which
+// gelu_f32_tail and gelu_f32_finish read.
+template <int N, bool MAX = true>
 __device__ __forceinline__ void gelu_f32_fetch(GeluBatch<N>& b, const float2* tab) {
   b.m = 0.0f;
 #pragma unroll
@@ -188,17 +196,35 @@ __device__ __forceinline__ void gelu_f32_fetch(GeluBatch<N>& b, const float2* ta
     u &= 0x7FFF7FFFu;   // the magnitudes (nearest-even rounding is symmetric)
     b.p[e] = u << 16;
     b.p[e + 1] = u & 0xFFFF0000u;
-    b.m = __builtin_elementwise_maximum(b.m, __builtin_elementwise_maximum(fabsf(b.z[e]), fabsf(b.z[e + 1])));
+    if (MAX) b.m = __builtin_elementwise_maximum(b.m, __builtin_elementwise_maximum(fabsf(b.z[e]), fabsf(b.z[e + 1])));
   }
 #pragma unroll
   for (int e = 0; e < N; ++e) b.t[e] = gelu_tab_entry(b.p[e], tab);
 }
 
+// The expansion for every value, whatever its size: the exact treatment
+// where gelu_f32_tail(b) is false. Beyond |z| = kGeluTaylorMax it gives, in
+// fp32: z itself for z > 6, as the evaluated erfc does (z Q(z) is below
+// half an ulp of z); for z < -6 a negative value of magnitude below 6e-9
+// (|z| < 6.016, which takes the entry of 6) or -0 (the entries above 6 are
+// zero), where the evaluated erfc gives a negative value below 6e-9 or -0;
+// and NaN for NaN or infinite z and once the expansion overflows (|z|
+// beyond about 1e9).
 template <int N>
-__device__ __forceinline__ void gelu_f32_finish(float* g, const GeluBatch<N>& b) {
+__device__ __forceinline__ void gelu_f32_expand(float* g, const GeluBatch<N>& b) {
 #pragma unroll
   for (int e = 0; e < N; ++e) g[e] = gelu_f32_from(b.z[e], b.p[e], b.t[e]);
-  if (!(b.m <= kGeluTaylorMax)) {
+}
+
+template <int N>
+__device__ __forceinline__ bool gelu_f32_tail(const GeluBatch<N>& b) {
+  return !(b.m <= kGeluTaylorMax);  // NaN too
+}
+
+template <int N>
+__device__ __forceinline__ void gelu_f32_finish(float* g, const GeluBatch<N>& b) {
+  gelu_f32_expand(g, b);
+  if (gelu_f32_tail(b)) {
     // One evaluation per trip of a loop that stays rolled, so the code stays
     // small wherever this is inlined; the value is picked out and put back
     // by selects on compile-time positions (no register array is indexed
@@ -270,8 +296,9 @@ __device__ __forceinline__ uint32_t mx_pack8_alu(const float v[8], uint32_t S) {
 // codes (|x| in (2^(S - 129), 2^-126)), which the ALU path's exact
 // power-of-two product handles by construction. Such blocks (amax below
 // 2^-122) do not occur in practice, so the branch costs one compare.
-__device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
-  if (S <= 2) return mx_pack8_alu(v, S);
+// mx_pack8_hw is the converter alone, for callers that have set such blocks
+// aside (S > 2).
+__device__ __forceinline__ uint32_t mx_pack8_hw(const float v[8], uint32_t S) {
   const float sc = __uint_as_float(S << 23);  // 2^(S - 127)
   uint32_t w = 0;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], sc, 0);
@@ -279,6 +306,10 @@ __device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
   return w;
+}
+
+__device__ __forceinline__ uint32_t mx_pack8(const float v[8], uint32_t S) {
+  return S <= 2 ? mx_pack8_alu(v, S) : mx_pack8_hw(v, S);
 }
 
 }  // namespace fp4r
