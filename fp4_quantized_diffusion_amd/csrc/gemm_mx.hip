@@ -746,10 +746,10 @@ constexpr int kQWaveBytes = 32 * kQPitch;
 // Quantize the 16 GELU values g of MFMA tile (i, j) (this lane's half of
 // a 32-block) and stage the wave's codes; returns the block's scale byte.
 // HW: the hardware converter only, with `rare` set where the block's scale
-// byte S is below 103 (amax below 2^-22, which includes the ALU path's
-// blocks, S <= 2) or above 252 (an infinite or NaN value): the caller
-// redoes those with the exact treatment of every value and block.
-template <bool HW = false>
+// byte S is below LO (LO >= 3 includes the ALU path's blocks, S <= 2) or
+// above 252 (an infinite or NaN value): the caller redoes those with the
+// exact treatment of every value and block.
+template <bool HW = false, uint32_t LO = 3>
 __device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* stage, int r32, int h,
                                                   bool* rare = nullptr) {
   uint32_t am = amax_bits<16>(g);
@@ -762,7 +762,7 @@ __device__ __forceinline__ uint32_t gelu_block_mx(float g[16], int i, uint8_t* s
   // After the swap lane half 0 holds x of both halves, half 1 y of both.
   uint32_t x, y;
   if constexpr (HW) {
-    *rare |= S - 103u > 149u;
+    *rare |= S - LO > 252u - LO;
     x = mx_pack8_hw(g, S);
     y = mx_pack8_hw(g + 8, S);
   } else {
@@ -815,7 +815,7 @@ __device__ __forceinline__ void gelu_tile_f32(v16f acc[4][4], uint8_t* qc, uint8
       float g[16];
       if constexpr (FAST) {
         gelu_f32_expand(g, b);
-        sreg |= gelu_block_mx<true>(g, i, stage, r32, h, rare) << (8 * i);
+        sreg |= gelu_block_mx<true, 103>(g, i, stage, r32, h, rare) << (8 * i);
       } else {
         gelu_f32_finish(g, b);
         sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
@@ -838,12 +838,46 @@ __device__ __forceinline__ void gelu_tile_f32(v16f acc[4][4], uint8_t* qc, uint8
   });
 }
 
+// The bf16 reading: GELU of bf16(sum) from the LDS table of Q, exact for
+// every value, so only the converter differs between the passes. FAST: the
+// hardware converter for every block, `rare` set where a block's scale byte
+// is 2 or less (or above 252, which changes nothing but is cheap to test).
+template <bool FAST>
+__device__ __forceinline__ void gelu_tile_bf16(v16f acc[4][4], uint8_t* qc, uint8_t* qs, int m0, uint8_t* stage,
+                                               const float* tab, bool* rare) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t sreg = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float g[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
+        const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
+        uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
+        asm("" : "+v"(u));  // one pair conversion (the compiler would convert the even element again on its own)
+        g[2 * e] = __uint_as_float(u << 16);
+        g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
+      if constexpr (FAST)
+        sreg |= gelu_block_mx<true, 3>(g, i, stage, r32, h, rare) << (8 * i);
+      else
+        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
+    }
+    gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+  }
+}
+
 template <bool EXACT>
 __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, int m0, const Problem& p,
                                                    uint8_t* stage, const float* tab, const float2* tab2) {
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // keep the lane-dependent address math in the epilogue, out of the K loop
-  const int r32 = lane & 31, h = lane >> 5;
+  // (each pass forms its lane-dependent addresses itself, behind an asm
+  // barrier that keeps that arithmetic out of the K loop)
   uint8_t* qc = p.qc + blk * 16384;
   uint8_t* qs = p.qs + blk * 1024;
   if constexpr (EXACT) {
@@ -872,25 +906,13 @@ __device__ __forceinline__ void store_tile_gelu_mx(v16f acc[4][4], int64_t blk, 
       gelu_tile_f32<false>(acc, qc, qs, m0, stage, tab2, nullptr);
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t sreg = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float g[16];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {  // hardware round-to-nearest-even bf16 of n-adjacent pairs, back to fp32 exactly
-          const float a0 = acc_read(acc[i][j][2 * e]), a1 = acc_read(acc[i][j][2 * e + 1]);
-          uint32_t u = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
-          asm("" : "+v"(u));  // one pair conversion (the compiler would convert the even element again on its own)
-          g[2 * e] = __uint_as_float(u << 16);
-          g[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) g[e] = gelu_bf16(g[e], tab);
-        sreg |= gelu_block_mx(g, i, stage, r32, h) << (8 * i);
-      }
-      gelu_rows_out(qc, qs, m0, j, sreg, stage, lane, r32, h);
+    // the same two passes for the bf16 reading (only the converter's
+    // branch is at stake there)
+    bool rare = false;
+    gelu_tile_bf16<true>(acc, qc, qs, m0, stage, tab, &rare);
+    if (__any(rare)) {
+      asm volatile("" ::: "memory");
+      gelu_tile_bf16<false>(acc, qc, qs, m0, stage, tab, nullptr);
     }
   }
 }

@@ -1,5 +1,6 @@
-"""The first linear's fused fp32 GELU + MXFP4 epilogue (fp4_gemm_panel_gelu_f32)
-on hidden values built to reach every case of its two passes.
+"""The first linear's fused GELU + MXFP4 epilogues (fp4_gemm_panel_gelu_f32,
+and fp4_gemm_panel_gelu for the bf16 reading) on hidden values built to
+reach every case of their two passes.
 
 The epilogue first runs a pass without branches: the table expansion for
 every value (no evaluated erfc beyond |z| = 6) and the hardware converter
@@ -145,3 +146,28 @@ def test_fused_fp32_gelu_redo_leaves_other_tiles_alone(gpu_lib):
     for out in (out1, out2):
         np.testing.assert_array_equal(to_np(out.scales), to_np(ref.scales))
         np.testing.assert_array_equal(to_np(out.codes), to_np(ref.codes))
+
+
+@pytest.mark.parametrize("which", ["extremes", "zero_row"])
+def test_fused_bf16_gelu_two_pass_cases(gpu_lib, which):
+    """fp4_gemm_panel_gelu (GELU of bf16(sum)) on the same operands: the
+    first pass uses the hardware converter for every block, and a tile with
+    a block whose scale byte is 2 or less (the zero blocks here) is written
+    again with the ALU converter. Byte for byte the bf16 GEMM followed by the
+    GELU quantizer."""
+    if which == "extremes":
+        a, b = operands()
+    else:
+        rng = np.random.default_rng(5)
+        a = (rng.choice(GRID, (M, K)) * rng.choice([-1.0, 1.0], (M, K)) * 0.25).astype(np.float32)
+        b = (rng.choice(GRID, (N, K)) * rng.choice([-1.0, 1.0], (N, K)) * 0.125).astype(np.float32)
+        a[300] = 0.0
+    qa = gpu_lib.quantize(torch.from_numpy(a).to(DEV), "mx", layout="panel")
+    qb = gpu_lib.quantize(torch.from_numpy(b).to(DEV), "mx", layout="panel")
+    z = gpu_lib.gemm(qa, qb, "bf16", out=torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
+    ref = gpu_lib.quantize(z, "mx", prologue="gelu", layout="panel")
+    out = gpu_lib.gemm_gelu(qa, qb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(out.scales), to_np(ref.scales))
+    np.testing.assert_array_equal(to_np(out.codes), to_np(ref.codes))
+    assert (to_np(ref.scales) <= 2).any()      # the second pass was needed somewhere
