@@ -26,11 +26,12 @@ v followed by euler_step, without writing v or reading it back. The hidden
 activation z stays fp32, as in the float64 oracle's reading (GELU from an
 LDS table of (Q, phi) at bf16 points carried to z by a fourth-order
 expansion, erfc evaluated beyond |z| = 6); hidden="bf16" rounds it to bf16
-first (fp4_gemm_panel_gelu, one table read per value, faster -- 370-400 ms
-per rollout step against about 460 -- but not the oracle's arithmetic: at 96 x 4096 x 3072 the final state then
-differs from the oracle's by about a quarter, because the rounding moves
-about one hidden value in a hundred across an FP4 decision point and the
-next blocks' quantizers amplify that). The FP4 operands use the panel layout by default
+first (fp4_gemm_panel_gelu, one table read per value, faster -- about 363
+ms per rollout step against 388 -- but not the oracle's arithmetic: at
+96 x 4096 x 3072 the final state then differs from the oracle's by about a
+quarter, because the rounding moves about one hidden value in a hundred
+across an FP4 decision point and the next blocks' quantizers amplify that).
+The FP4 operands use the panel layout by default
 (fp4_quantize with FP4_LAYOUT_PANEL, fp4_gemm_panel): the same codes and
 scales, stored so that every GEMM stage load is contiguous; layout="row" runs
 the row-major entry points (and a separate euler_step) instead.
@@ -50,9 +51,10 @@ of how the rows are chunked, so the result is bit-identical to the
 one-stream schedule. Both streams run at the default priority. On MI355X
 this schedule measured slower than the one-stream schedule of the same
 (unfused) kernels for the 96 x 4096 x 3072 rollout (534 vs 523 ms per step,
-where the fused one-stream path takes 370-400 ms with the same bf16 hidden
-activation): the GEMM runs at the card's power limit, and the overlapped quantizers lower the clock and slow the GEMM by
-more than they hide; it is kept as an option.
+where the fused one-stream path takes about 363 ms with the same bf16 hidden
+activation): the GEMM runs at the card's power limit, and the overlapped
+quantizers lower the clock and slow the GEMM by more than they hide; it is
+kept as an option.
 
 Every call enqueues on the current stream (and the second stream, which the
 current stream waits for before returning); the only host synchronization is
