@@ -44,7 +44,12 @@ Parity status per function:
   nft.noise / loss_terms ...... pinned (exact rationals, beta = 0 and equal-
                                 velocity identities, r = 0 / 1 branch
                                 selection, noising end points and slope)
-  rollout (composite) ......... parity unpinned beyond the pinned pieces it
-                                composes (statistical comparison only)
+  rollout (composite) ......... pinned (one token through one and two
+                                velocity blocks, an Euler step and the
+                                reward, in exact rationals, with plausible
+                                mis-compositions shown to miss; the bf16
+                                reading of the hidden activation by a block
+                                where the two readings differ, and its
+                                rounding against torch's casts)
 """
 from . import e2m1, mxfp4, nvfp4, gemm, euler, reward, rollout, lora, nft  # noqa: F401
