@@ -1,9 +1,11 @@
 """GPU rollout (all steps through the C ABI) against the float64 oracle's
 rollout on a reduced problem (the full-size rollout is checked on sampled
 rows in test_gpu_rollout_full.py). The composite is not bit-comparable (fp32 vs
-float64 intermediates re-quantized every block), so this is statistical:
-parity unpinned beyond the per-call tests -- final-latent relative error,
-reward rank correlation and selection overlap."""
+float64 intermediates re-quantized every block: a quantization decision within
+fp32 rounding of its point can flip and the next blocks carry it on), so the
+gates are statistical -- final-latent relative error, reward rank correlation
+and selection overlap -- set from the observed values. The oracle's composite
+itself is pinned by hand-worked exact cases (tests/test_oracle_velocity_hand.py)."""
 import numpy as np
 import pytest
 import torch

@@ -126,8 +126,9 @@ def test_rollout_zero_weights_closed_form():
 
 
 def test_rollout_small_is_deterministic_and_ranks_agree():
-    """parity unpinned beyond its parts: the FP4 rollout's ranking should
-    mostly agree with the unquantized one on a tiny problem."""
+    """Determinism, and a sanity property of the composite (its exact
+    pins are in test_oracle_velocity_hand.py): the FP4 rollout's ranking
+    should mostly agree with the unquantized one on a tiny problem."""
     rng = np.random.default_rng(19)
     noise = rng.standard_normal((8, 16, 64)).astype(np.float32)
     w1 = [(rng.standard_normal((128, 64)) * 0.02).astype(np.float32) for _ in range(2)]
