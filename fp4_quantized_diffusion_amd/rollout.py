@@ -209,6 +209,32 @@ class Fp4Rollout:
             return self._run_two_streams(noise, work)
         return self._run_one_stream(noise, work)
 
+    def graph(self, noise, work=None):
+        """Capture one run(noise, work) -- the weight re-quantization, every
+        Euler step, the reward and the selection -- in a HIP graph (through
+        torch.cuda.CUDAGraph) for callers that repeat the rollout on the same
+        buffers as one graph launch (a serving loop that replays captured
+        work). It is not faster: from 4 x 256 x 256 up, the kernels' own time
+        covers the launches, and replays ran as fast as eager rollouts.
+        Returns (replay, outputs): replay() runs the whole rollout
+        again as one graph launch on the current stream; outputs =
+        (rewards, top, bottom, r_norm) are refreshed in place by every replay.
+        noise and work stay at their addresses: write new noise into `noise`
+        (and new weights into the bf16 weights given to the constructor)
+        between replays. Every launch of the library is a kernel node (it
+        allocates and clears no device memory itself). The rollout runs once
+        eagerly first, to set up its buffers."""
+        import torch
+        if self.timer is not None:
+            raise ValueError("a timed rollout cannot be captured: build it without timer")
+        self.run(noise, work)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = self.run(noise, work)
+        self._graph = g  # the graph's memory pool lives as long as the graph
+        return g.replay, out
+
     def _run_two_streams(self, noise, work):
         import torch
         n_cand, tokens, dim = noise.shape
